@@ -1,0 +1,280 @@
+// Projections of the refreshed rows: C = A W^T with fused epilogues.
+//
+// WAM-Cache (paperpeel 2610.11401) §3: Q, K and V are linear projections of
+// the module input and the module applies an MLP, each sub-layer with a
+// residual.  Only the k_eff refreshed rows go through these GEMMs, which is
+// where the refresh saves its FLOPs (§5.2: prefill cost scales with the
+// recompute ratio).
+//
+// Epilogues (applied to acc + bias, all in f32):
+//   EPI_QKV   : Q -> q_out (act), K/V -> written straight into this layer's
+//               cache at the row's token index (the scatter is fused here);
+//   EPI_RESID : out = in + gate * v        (gated residual, f32 stream);
+//   EPI_GELU  : g = act(GELU_erf(v)).
+//
+// bf16 path: 128x128x64 tiles, 4 waves in a 2x2 layout, each wave 64x64 as
+// 2x2 v_mfma_f32_32x32x16_bf16 blocks; A and W tiles double-buffered in LDS
+// (rows padded by 16 bytes so the 32 lanes of a fragment read hit distinct
+// banks), one barrier per k-tile, global loads for tile k+1 in flight while
+// tile k is multiplied.  The tile order is XCD-aware: consecutive workgroup
+// ids go round-robin over the 8 XCDs, so ids are remapped to give each XCD a
+// contiguous range of tiles, then grouped 8 row-tiles at a time so tiles that
+// share weight columns run close together in the same L2.
+// fp32 path: 64x64x16 LDS tiles on VALU FMAs (correctness path for the small
+// fp32 workloads).
+#include "common.h"
+#include "launch.h"
+
+namespace wamc {
+
+// ---------------------------------------------------------------------------
+// shared epilogue
+// ---------------------------------------------------------------------------
+
+struct RowInfo {
+  bool valid;
+  int b, r;
+};
+
+__device__ __forceinline__ RowInfo row_info(const GemmArgs& g, int m) {
+  RowInfo ri;
+  ri.b = m / g.rows_cap;
+  ri.r = m - ri.b * g.rows_cap;
+  ri.valid = m < g.M && ri.r < rows_of(g.k_eff, ri.b, g.rows_cap);
+  return ri;
+}
+
+template <int EPI, typename T>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, const RowInfo& ri, int m, int n, float acc) {
+  if (!ri.valid || n >= g.Nout) return;
+  const float v = acc + Elem<T>::load(static_cast<const T*>(g.bias), n);
+  if constexpr (EPI == EPI_QKV) {
+    const int d = g.d_model;
+    const int which = n / d, c = n - which * d;
+    if (which == 0) {
+      Elem<T>::store(static_cast<T*>(g.q_out), static_cast<size_t>(m) * d + c, v);
+    } else {
+      const int tok = g.idx ? g.idx[static_cast<size_t>(ri.b) * g.n_tokens + ri.r] : ri.r;
+      if (tok < 0 || tok >= g.n_tokens) return;
+      T* cache = static_cast<T*>(which == 1 ? g.k_cache : g.v_cache);
+      Elem<T>::store(cache, (static_cast<size_t>(ri.b) * g.n_tokens + tok) * d + c, v);
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    const size_t o = static_cast<size_t>(m) * g.Nout + n;
+    g.resid_out[o] = g.resid_in[o] + Elem<T>::load(static_cast<const T*>(g.gate), n) * v;
+  } else {
+    Elem<T>::store(static_cast<T*>(g.g_out), static_cast<size_t>(m) * g.Nout + n, gelu_erf(v));
+  }
+}
+
+// true when no row of [m0, m0 + rows) is valid (the whole tile can exit)
+__device__ __forceinline__ bool tile_empty(const GemmArgs& g, int m0, int rows) {
+  if (m0 >= g.M) return true;
+  if (!g.k_eff) return false;
+  const int m1 = min(g.M, m0 + rows) - 1;
+  const int b0 = m0 / g.rows_cap, b1 = m1 / g.rows_cap;
+  for (int b = b0; b <= b1; ++b) {
+    const int lo = b == b0 ? m0 - b * g.rows_cap : 0;
+    if (lo < rows_of(g.k_eff, b, g.rows_cap)) return false;
+  }
+  return true;
+}
+
+// XCD-aware remap of a linear workgroup id, then grouped (GM row-tiles)
+// ordering over a tiles_m x tiles_n grid.
+__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int kXcd = 8, GM = 8;
+  const int T = tiles_m * tiles_n;
+  const int per = (T + kXcd - 1) / kXcd;
+  int tall = T % kXcd;
+  if (tall == 0) tall = kXcd;
+  const int xcd = pid % kXcd, local = pid / kXcd;
+  const int id = xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+  const int group = id / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in_group = id - group * GM * tiles_n;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA GEMM
+// ---------------------------------------------------------------------------
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kLdsK = kBK + 8;   // padded LDS row (bf16 elements)
+constexpr int kGemmThreads = 256;
+
+__device__ __forceinline__ bf16x8_t frag(const bf16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) {
+  const int tiles_m = (g.M + kBM - 1) / kBM, tiles_n = (g.Nout + kBN - 1) / kBN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  if (tile_empty(g, m0, kBM)) return;
+
+  __shared__ bf16_t As[2][kBM * kLdsK];
+  __shared__ bf16_t Ws[2][kBN * kLdsK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int half = lane >> 5, col = lane & 31;
+  const bf16_t* A = static_cast<const bf16_t*>(g.a);
+  const bf16_t* W = static_cast<const bf16_t*>(g.w);
+  const int K = g.K;
+
+  // each thread moves 4 16-byte chunks of A and 4 of W per k-tile
+  uint4 ra[4], rw[4];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int chunk = tid + i * kGemmThreads;
+      const int row = chunk >> 3, kc = (chunk & 7) * 8;
+      const int gk = k0 + kc;
+      const int am = m0 + row, wn_ = n0 + row;
+      ra[i] = (am < g.M && gk < K) ? *reinterpret_cast<const uint4*>(A + static_cast<size_t>(am) * K + gk)
+                                   : make_uint4(0, 0, 0, 0);
+      rw[i] = (wn_ < g.Nout && gk < K) ? *reinterpret_cast<const uint4*>(W + static_cast<size_t>(wn_) * K + gk)
+                                      : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int chunk = tid + i * kGemmThreads;
+      const int row = chunk >> 3, kc = (chunk & 7) * 8;
+      *reinterpret_cast<uint4*>(&As[buf][row * kLdsK + kc]) = ra[i];
+      *reinterpret_cast<uint4*>(&Ws[buf][row * kLdsK + kc]) = rw[i];
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+
+  const int nk = (K + kBK - 1) / kBK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_tile((kt + 1) * kBK);
+    const bf16_t* as = &As[cur][(wm * 64 + col) * kLdsK + half * 8];
+    const bf16_t* ws = &Ws[cur][(wn * 64 + col) * kLdsK + half * 8];
+#pragma unroll
+    for (int s = 0; s < kBK / 16; ++s) {
+      const bf16x8_t a0 = frag(as + s * 16), a1 = frag(as + 32 * kLdsK + s * 16);
+      const bf16x8_t b0 = frag(ws + s * 16), b1 = frag(ws + 32 * kLdsK + s * 16);
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // C layout of a 32x32 block: lane (half, col), element v ->
+  // row (v/4)*8 + half*4 + v%4, column col.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + wm * 64 + i * 32 + (v / 4) * 8 + half * 4 + (v % 4);
+      const RowInfo ri = row_info(g, m);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * 64 + j * 32 + col;
+        epilogue<EPI, bf16_t>(g, ri, m, n, acc[i][j][v]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 GEMM (VALU)
+// ---------------------------------------------------------------------------
+
+constexpr int kFBM = 64, kFBN = 64, kFBK = 16;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
+  const int tiles_m = (g.M + kFBM - 1) / kFBM, tiles_n = (g.Nout + kFBN - 1) / kFBN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * kFBM, n0 = tn * kFBN;
+  if (tile_empty(g, m0, kFBM)) return;
+  __shared__ float As[kFBK][kFBM + 4];
+  __shared__ float Ws[kFBK][kFBN + 4];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const float* A = static_cast<const float*>(g.a);
+  const float* W = static_cast<const float*>(g.w);
+  const int K = g.K;
+  float acc[4][4] = {};
+  const int lr = tid >> 2, lk = (tid & 3) * 4;
+  for (int k0 = 0; k0 < K; k0 += kFBK) {
+    const int gk = k0 + lk;
+    float4 va = make_float4(0, 0, 0, 0), vw = make_float4(0, 0, 0, 0);
+    if (m0 + lr < g.M && gk < K) va = *reinterpret_cast<const float4*>(A + static_cast<size_t>(m0 + lr) * K + gk);
+    if (n0 + lr < g.Nout && gk < K) vw = *reinterpret_cast<const float4*>(W + static_cast<size_t>(n0 + lr) * K + gk);
+    As[lk + 0][lr] = va.x; As[lk + 1][lr] = va.y; As[lk + 2][lr] = va.z; As[lk + 3][lr] = va.w;
+    Ws[lk + 0][lr] = vw.x; Ws[lk + 1][lr] = vw.y; Ws[lk + 2][lr] = vw.z; Ws[lk + 3][lr] = vw.w;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kFBK; ++kk) {
+      float a[4], w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = As[kk][ty * 4 + i]; w[i] = Ws[kk][tx * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], w[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    const RowInfo ri = row_info(g, m);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) epilogue<EPI, float>(g, ri, m, n0 + tx * 4 + j, acc[i][j]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+static const char* gemm_name(const GemmArgs& g, GemmEpi e) {
+  if (e == EPI_QKV) return "gemm_qkv";
+  if (e == EPI_GELU) return "gemm_up_gelu";
+  return g.K == g.d_model ? "gemm_out_resid" : "gemm_down_resid";
+}
+
+hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer) {
+  if (g.M <= 0 || g.Nout <= 0) return hipSuccess;
+  TimedLaunch t(timer, gemm_name(g, epi), s);
+  if (bf16) {
+    const unsigned grid = static_cast<unsigned>(((g.M + kBM - 1) / kBM) * ((g.Nout + kBN - 1) / kBN));
+    switch (epi) {
+      case EPI_QKV: gemm_bf16_kernel<EPI_QKV><<<grid, kGemmThreads, 0, s>>>(g); break;
+      case EPI_RESID: gemm_bf16_kernel<EPI_RESID><<<grid, kGemmThreads, 0, s>>>(g); break;
+      case EPI_GELU: gemm_bf16_kernel<EPI_GELU><<<grid, kGemmThreads, 0, s>>>(g); break;
+    }
+  } else {
+    const unsigned grid = static_cast<unsigned>(((g.M + kFBM - 1) / kFBM) * ((g.Nout + kFBN - 1) / kFBN));
+    switch (epi) {
+      case EPI_QKV: gemm_f32_kernel<EPI_QKV><<<grid, 256, 0, s>>>(g); break;
+      case EPI_RESID: gemm_f32_kernel<EPI_RESID><<<grid, 256, 0, s>>>(g); break;
+      case EPI_GELU: gemm_f32_kernel<EPI_GELU><<<grid, 256, 0, s>>>(g); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace wamc

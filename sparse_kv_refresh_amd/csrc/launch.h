@@ -1,0 +1,97 @@
+// Host-side launchers of the libwamc kernels and the optional kernel timer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wamc {
+
+// Records a pair of HIP events around each timed launch on the launch stream
+// (only while timing is enabled).  Implemented in api.cpp.
+class KernelTimer {
+ public:
+  virtual ~KernelTimer() = default;
+  virtual void begin(const char* kind, hipStream_t s) = 0;
+  virtual void end(hipStream_t s) = 0;
+};
+
+struct TimedLaunch {
+  KernelTimer* t;
+  hipStream_t s;
+  TimedLaunch(KernelTimer* timer, const char* kind, hipStream_t stream) : t(timer), s(stream) {
+    if (t) t->begin(kind, s);
+  }
+  ~TimedLaunch() {
+    if (t) t->end(s);
+  }
+};
+
+// ----- selection (select.hip) -----
+hipError_t launch_select(const float* score, int32_t* age, int B, int N, int k, int G, int rows_cap,
+                         int32_t* idx, int32_t* k_eff, int32_t* n_forced, hipStream_t s);
+hipError_t launch_ages_from_set(const int32_t* idx_in, const int32_t* k_in, int B, int N, int rows_cap,
+                                int32_t* idx_out, int32_t* k_out, int32_t* age, hipStream_t s);
+
+// ----- scoring (score.hip) -----
+struct ScorePlan {
+  int chunk_keys, nchunks, comb_blocks;
+  size_t ms_bytes, part_bytes, tok_bytes, usum_bytes;
+};
+ScorePlan plan_score(int B, int L, int H, int N, int A, bool bf16);
+hipError_t launch_score_mass(bool bf16, const void* qa, const void* kc, int B, int L, int H, int N,
+                             int A, int d, const ScorePlan& p, float2* ms, float* part,
+                             hipStream_t s, KernelTimer* timer);
+hipError_t launch_score_combine(bool bf16, const float* part, int LH, const float* mass_in,
+                                const void* z, const void* zref, int B, int N, int d, float w_attn_norm,
+                                float w_surprise, const ScorePlan& p, float* mass_tmp, float* surprise_tmp,
+                                float* usum, float* score, float* mass_out, float* surprise_out,
+                                hipStream_t s, KernelTimer* timer);
+
+// ----- row kernels (rows.hip) -----
+// x[b*rows_cap + r] = float(z[b, idx[b,r]]), zref[b, idx] = z[b, idx]
+// (idx == nullptr: identity, rows = all N tokens; age (nullable) <- 0).
+hipError_t launch_gather(bool bf16, const void* z, void* zref, const int32_t* idx, const int32_t* k_eff,
+                         int B, int N, int d, int rows_cap, float* x, int32_t* age_zero, hipStream_t s,
+                         KernelTimer* timer);
+// h[m] = act(LN(x_in[m]) * (1 + scale) + shift) for valid rows.
+hipError_t launch_ln_mod(bool bf16, const float* x, const void* shift, const void* scale, int B,
+                         int rows_cap, const int32_t* k_eff, int d, float eps, void* h, hipStream_t s,
+                         KernelTimer* timer);
+
+// ----- GEMM (gemm.hip) -----
+enum GemmEpi { EPI_QKV = 0, EPI_RESID = 1, EPI_GELU = 2 };
+struct GemmArgs {
+  const void* a;        // [M, K] act, row-major
+  const void* w;        // [Nout, K] act, row-major (linear-layer layout)
+  const void* bias;     // [Nout] act
+  int M, Nout, K;       // M = B * rows_cap
+  int rows_cap;         // rows per episode
+  const int32_t* k_eff; // nullable: valid rows per episode
+  // EPI_QKV: out cols [0,d) -> q_out[m, c]; [d,2d) -> k cache row; [2d,3d) -> v cache row
+  void* q_out;
+  void* k_cache;        // [B, N, d] act (this layer)
+  void* v_cache;
+  const int32_t* idx;   // nullable: [B, N] token of each row (identity when null)
+  int n_tokens, d_model;
+  // EPI_RESID: out[m, c] = in[m, c] + gate[c] * (acc + bias[c])   (f32)
+  const float* resid_in;
+  float* resid_out;
+  const void* gate;     // [Nout] act
+  // EPI_GELU: g[m, c] = act(gelu(acc + bias[c]))
+  void* g_out;
+};
+hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer);
+
+// ----- attention (attention.hip) -----
+struct AttnArgs {
+  const void* q;        // [B*rows_cap, d] act
+  const void* k_cache;  // [B, N, d] act
+  const void* v_cache;
+  void* o;              // [B*rows_cap, d] act
+  int B, N, H, dh, d, rows_cap;
+  const int32_t* k_eff;
+};
+hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s, KernelTimer* timer);
+
+}  // namespace wamc

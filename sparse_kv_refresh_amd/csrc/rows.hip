@@ -1,0 +1,124 @@
+// Row kernels: gather of the refreshed rows (with the reference-embedding
+// update) and the modulated LayerNorm that feeds each projection.
+//
+// WAM-Cache (paperpeel 2610.11401) §4.1: the reference embedding of a token is
+// its input embedding at the most recent refresh, so zref is overwritten for
+// exactly the refreshed tokens; §3: each DiT sub-layer starts from a
+// (modulated) normalisation of its input.
+//
+// Both kernels give one wavefront per row and move 16-byte vectors so a row
+// of d elements is read and written with fully coalesced accesses.
+#include "common.h"
+#include "launch.h"
+
+namespace wamc {
+
+constexpr int kRowThreads = 256;   // 4 rows per block
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void gather_kernel(
+    const T* __restrict__ z, T* __restrict__ zref, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ k_eff, int N, int d, int rows_cap, float* __restrict__ x,
+    int32_t* __restrict__ age_zero) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int r = blockIdx.x * (kRowThreads / kWave) + wid;
+  if (r >= rows_of(k_eff, b, rows_cap)) return;
+  const int t = idx ? idx[static_cast<size_t>(b) * N + r] : r;
+  if (t < 0 || t >= N) return;
+  const size_t src = (static_cast<size_t>(b) * N + t) * d;
+  float* xr = x + (static_cast<size_t>(b) * rows_cap + r) * d;
+  for (int c = lane * 8; c < d; c += kWave * 8) {
+    if constexpr (sizeof(T) == 2) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(z + src + c);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      float4 lo, hi;
+      lo.x = __uint_as_float(w[0] << 16); lo.y = __uint_as_float(w[0] & 0xffff0000u);
+      lo.z = __uint_as_float(w[1] << 16); lo.w = __uint_as_float(w[1] & 0xffff0000u);
+      hi.x = __uint_as_float(w[2] << 16); hi.y = __uint_as_float(w[2] & 0xffff0000u);
+      hi.z = __uint_as_float(w[3] << 16); hi.w = __uint_as_float(w[3] & 0xffff0000u);
+      *reinterpret_cast<float4*>(xr + c) = lo;
+      *reinterpret_cast<float4*>(xr + c + 4) = hi;
+      if (zref) *reinterpret_cast<uint4*>(zref + src + c) = raw;
+    } else {
+      const float4 lo = *reinterpret_cast<const float4*>(z + src + c);
+      const float4 hi = *reinterpret_cast<const float4*>(z + src + c + 4);
+      *reinterpret_cast<float4*>(xr + c) = lo;
+      *reinterpret_cast<float4*>(xr + c + 4) = hi;
+      if (zref) {
+        *reinterpret_cast<float4*>(zref + src + c) = lo;
+        *reinterpret_cast<float4*>(zref + src + c + 4) = hi;
+      }
+    }
+  }
+  if (age_zero && lane == 0) age_zero[static_cast<size_t>(b) * N + t] = 0;
+}
+
+hipError_t launch_gather(bool bf16, const void* z, void* zref, const int32_t* idx, const int32_t* k_eff,
+                         int B, int N, int d, int rows_cap, float* x, int32_t* age_zero, hipStream_t s,
+                         KernelTimer* timer) {
+  TimedLaunch t(timer, "gather", s);
+  const dim3 grid((rows_cap + 3) / 4, B);
+  if (bf16)
+    gather_kernel<bf16_t><<<grid, kRowThreads, 0, s>>>(static_cast<const bf16_t*>(z),
+        static_cast<bf16_t*>(zref), idx, k_eff, N, d, rows_cap, x, age_zero);
+  else
+    gather_kernel<float><<<grid, kRowThreads, 0, s>>>(static_cast<const float*>(z),
+        static_cast<float*>(zref), idx, k_eff, N, d, rows_cap, x, age_zero);
+  return hipGetLastError();
+}
+
+// LayerNorm without affine (biased variance), then *(1 + scale) + shift,
+// rounded to the activation type.
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void ln_mod_kernel(
+    const float* __restrict__ x, const T* __restrict__ shift, const T* __restrict__ scale,
+    int rows_cap, const int32_t* __restrict__ k_eff, int d, float eps, T* __restrict__ h) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int r = blockIdx.x * (kRowThreads / kWave) + wid;
+  if (r >= rows_of(k_eff, b, rows_cap)) return;
+  const size_t row = static_cast<size_t>(b) * rows_cap + r;
+  const float* xr = x + row * d;
+  T* hr = h + row * d;
+  float s = 0.f;
+  for (int c = lane * 4; c < d; c += kWave * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + c);
+    s += (v.x + v.y) + (v.z + v.w);
+  }
+  const float mean = wave_sum(s) / static_cast<float>(d);
+  float q = 0.f;
+  for (int c = lane * 4; c < d; c += kWave * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + c);
+    const float a = v.x - mean, bb = v.y - mean, cc = v.z - mean, dd = v.w - mean;
+    q += (a * a + bb * bb) + (cc * cc + dd * dd);
+  }
+  const float var = wave_sum(q) / static_cast<float>(d);
+  const float rstd = 1.0f / sqrtf(var + eps);
+  for (int c = lane * 4; c < d; c += kWave * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + c);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float n = (vv[i] - mean) * rstd;
+      const float y = n * (1.0f + Elem<T>::load(scale, c + i)) + Elem<T>::load(shift, c + i);
+      Elem<T>::store(hr, c + i, y);
+    }
+  }
+}
+
+hipError_t launch_ln_mod(bool bf16, const float* x, const void* shift, const void* scale, int B,
+                         int rows_cap, const int32_t* k_eff, int d, float eps, void* h, hipStream_t s,
+                         KernelTimer* timer) {
+  TimedLaunch t(timer, "ln_mod", s);
+  const dim3 grid((rows_cap + 3) / 4, B);
+  if (bf16)
+    ln_mod_kernel<bf16_t><<<grid, kRowThreads, 0, s>>>(x, static_cast<const bf16_t*>(shift),
+        static_cast<const bf16_t*>(scale), rows_cap, k_eff, d, eps, static_cast<bf16_t*>(h));
+  else
+    ln_mod_kernel<float><<<grid, kRowThreads, 0, s>>>(x, static_cast<const float*>(shift),
+        static_cast<const float*>(scale), rows_cap, k_eff, d, eps, static_cast<float*>(h));
+  return hipGetLastError();
+}
+
+}  // namespace wamc

@@ -1,0 +1,417 @@
+// Token scores: action attention mass + latent surprise.
+//
+// WAM-Cache (paperpeel 2610.11401) §1, §4.2, §4.3 name the two signals:
+// the attention the action expert paid to each visual token in the preceding
+// chunk, and how far a token's input embedding moved since its last refresh.
+// Computed here as
+//   P_i = sum_{l,h,a} softmax_j(q_{l,a,h} . K_{l,j,h} / sqrt(dh))[i]
+//   U_i = sum_c (z_i,c - zref_i,c)^2
+//   score_i = w_a P_i / (L H A) + w_s U_i / sum_j U_j.
+//
+// P needs the per-query softmax normaliser before any per-key probability
+// can be summed, so it is a two-pass computation over the key cache:
+//   pass 1 (per (episode, layer*head, key chunk)): each query's running
+//           (max, sum of exp) over the chunk's keys -> workspace;
+//   pass 2 (same grid): merge the per-chunk (max, sum) of each query,
+//           recompute the logits and sum every key's probabilities over the
+//           queries -> a [B, L*H, N] partial in workspace;
+//   combine 1 (per token block): P_i = fixed-order sum over L*H; U_i by a
+//           wavefront reduction over d; per-block partial sums of U;
+//   combine 2 (per token block): sum_j U_j from the block partials in fixed
+//           order, then the score.
+// No float atomics anywhere: results are bitwise reproducible.
+//
+// bf16 logits run on MFMA (v_mfma_f32_32x32x16_bf16): with A action queries
+// the logit work is ~A FLOP per cache byte, far above what VALU fp32 can
+// sustain at HBM speed.  Pass 1 uses S^T = K Q^T so each lane owns one query
+// and reduces its keys in registers; pass 2 uses S = Q K^T so each lane owns
+// one key and reduces its queries in registers.  K fragments are loaded
+// straight from HBM into registers (each lane walks a contiguous 128-byte
+// half row); the action queries of one (layer, head) sit in LDS.
+#include "common.h"
+#include "launch.h"
+
+namespace wamc {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ void merge_ms(float& m, float& z, float m2, float z2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) { m = m2; z = z2; return; }
+  const float mn = fmaxf(m, m2);
+  z = z * exp2f(m - mn) + z2 * exp2f(m2 - mn);
+  m = mn;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA passes
+// ---------------------------------------------------------------------------
+
+constexpr int kScoreThreads = 256;        // 4 waves
+constexpr int kScoreDh = 128;             // head dim of the MFMA path
+constexpr int kQaStride = kScoreDh + 8;   // LDS row stride (bf16), breaks bank aliasing
+constexpr int kMaxQB = 4;                 // A <= 128
+
+// Fragment slot convention (shared by both MFMA operands, so any fixed
+// bijection is valid): lane half h, k-step s, slot j <-> dh = h*64 + s*8 + j.
+__device__ __forceinline__ void load_k_frags(const bf16_t* __restrict__ krow, bool valid, int h,
+                                             uint4 (&f)[8]) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    f[s] = valid ? *reinterpret_cast<const uint4*>(krow + h * 64 + s * 8) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Stage Qa[l, b, :, h*dh:(h+1)*dh] (A x 128 bf16) into LDS, zero-padding
+// rows A..QB*32.
+__device__ __forceinline__ void stage_queries(const bf16_t* __restrict__ qa, int A, int QB, int d,
+                                              bf16_t* sq) {
+  const int chunks = QB * 32 * (kScoreDh / 8);
+  for (int c = threadIdx.x; c < chunks; c += kScoreThreads) {
+    const int row = c / (kScoreDh / 8), col = (c % (kScoreDh / 8)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < A) v = *reinterpret_cast<const uint4*>(qa + static_cast<size_t>(row) * d + col);
+    *reinterpret_cast<uint4*>(sq + row * kQaStride + col) = v;
+  }
+}
+
+__global__ __launch_bounds__(kScoreThreads) void score_pass1_bf16(
+    const bf16_t* __restrict__ qa, const bf16_t* __restrict__ kc, int B, int H, int N, int A, int d,
+    int chunk_keys, int nchunks, float scale2, float2* __restrict__ ms_out) {
+  const int c = blockIdx.x, lh = blockIdx.y, b = blockIdx.z;
+  const int l = lh / H, h = lh % H;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, half = lane >> 5, col = lane & 31;
+  const int QB = (A + 31) / 32;
+  __shared__ bf16_t sq[kMaxQB * 32 * kQaStride];
+  __shared__ float2 sms[4][kMaxQB * 32];
+
+  stage_queries(qa + (static_cast<size_t>(l) * B + b) * A * d + h * kScoreDh, A, QB, d, sq);
+  __syncthreads();
+
+  const bf16_t* kbase = kc + (static_cast<size_t>(l) * B + b) * N * d + h * kScoreDh;
+  const int k0 = c * chunk_keys, k1 = min(N, k0 + chunk_keys);
+  float m[kMaxQB], z[kMaxQB];
+#pragma unroll
+  for (int q = 0; q < kMaxQB; ++q) { m[q] = -INFINITY; z[q] = 0.f; }
+
+  for (int kb = k0 + wid * 32; kb < k1; kb += 4 * 32) {
+    const int key = kb + col;
+    uint4 kf[8];
+    load_k_frags(kbase + static_cast<size_t>(key) * d, key < k1, half, kf);
+#pragma unroll
+    for (int q = 0; q < kMaxQB; ++q) {
+      if (q >= QB) break;
+      f32x16_t acc = {};
+      const bf16_t* qrow = sq + (q * 32 + col) * kQaStride + half * 64;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint4 qf = *reinterpret_cast<const uint4*>(qrow + s * 8);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s]), as_bf16x8(qf), acc, 0, 0, 0);
+      }
+      // acc[v]: key kb + (v/4)*8 + half*4 + v%4, query q*32 + col
+      float tmax = -INFINITY;
+      float sv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kk = kb + (v / 4) * 8 + half * 4 + (v % 4);
+        sv[v] = kk < k1 ? acc[v] * scale2 : -INFINITY;
+        tmax = fmaxf(tmax, sv[v]);
+      }
+      if (tmax != -INFINITY) {
+        const float mn = fmaxf(m[q], tmax);
+        float zz = m[q] == -INFINITY ? 0.f : z[q] * exp2f(m[q] - mn);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) zz += exp2f(sv[v] - mn);
+        m[q] = mn;
+        z[q] = zz;
+      }
+    }
+  }
+  // merge the two lane halves (same query, different keys), then the waves
+#pragma unroll
+  for (int q = 0; q < kMaxQB; ++q) {
+    const float m2 = __shfl_xor(m[q], 32, kWave), z2 = __shfl_xor(z[q], 32, kWave);
+    merge_ms(m[q], z[q], m2, z2);
+    if (half == 0 && q < QB) sms[wid][q * 32 + col] = make_float2(m[q], z[q]);
+  }
+  __syncthreads();
+  for (int a = threadIdx.x; a < A; a += kScoreThreads) {
+    float mm = -INFINITY, zz = 0.f;
+    for (int w = 0; w < 4; ++w) merge_ms(mm, zz, sms[w][a].x, sms[w][a].y);
+    ms_out[((static_cast<size_t>(b) * gridDim.y + lh) * nchunks + c) * A + a] = make_float2(mm, zz);
+  }
+}
+
+__global__ __launch_bounds__(kScoreThreads) void score_pass2_bf16(
+    const bf16_t* __restrict__ qa, const bf16_t* __restrict__ kc, int B, int H, int N, int A, int d,
+    int chunk_keys, int nchunks, float scale2, const float2* __restrict__ ms_in,
+    float* __restrict__ part) {
+  const int c = blockIdx.x, lh = blockIdx.y, b = blockIdx.z;
+  const int LH = gridDim.y;
+  const int l = lh / H, h = lh % H;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, half = lane >> 5, col = lane & 31;
+  const int QB = (A + 31) / 32;
+  __shared__ bf16_t sq[kMaxQB * 32 * kQaStride];
+  __shared__ float smax[kMaxQB * 32], sinv[kMaxQB * 32];
+
+  stage_queries(qa + (static_cast<size_t>(l) * B + b) * A * d + h * kScoreDh, A, QB, d, sq);
+  for (int a = threadIdx.x; a < QB * 32; a += kScoreThreads) {
+    float mm = -INFINITY, zz = 0.f;
+    if (a < A) {
+      const float2* p = ms_in + (static_cast<size_t>(b) * LH + lh) * nchunks * A + a;
+      for (int cc = 0; cc < nchunks; ++cc) merge_ms(mm, zz, p[static_cast<size_t>(cc) * A].x,
+                                                    p[static_cast<size_t>(cc) * A].y);
+    }
+    smax[a] = a < A ? mm : INFINITY;   // padded queries contribute exp2(-inf) = 0
+    sinv[a] = a < A ? 1.f / zz : 0.f;
+  }
+  __syncthreads();
+
+  const bf16_t* kbase = kc + (static_cast<size_t>(l) * B + b) * N * d + h * kScoreDh;
+  float* prow = part + (static_cast<size_t>(b) * LH + lh) * N;
+  const int k0 = c * chunk_keys, k1 = min(N, k0 + chunk_keys);
+  for (int kb = k0 + wid * 32; kb < k1; kb += 4 * 32) {
+    const int key = kb + col;
+    uint4 kf[8];
+    load_k_frags(kbase + static_cast<size_t>(key) * d, key < k1, half, kf);
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < kMaxQB; ++q) {
+      if (q >= QB) break;
+      f32x16_t acc = {};
+      const bf16_t* qrow = sq + (q * 32 + col) * kQaStride + half * 64;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint4 qf = *reinterpret_cast<const uint4*>(qrow + s * 8);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qf), as_bf16x8(kf[s]), acc, 0, 0, 0);
+      }
+      // acc[v]: query q*32 + (v/4)*8 + half*4 + v%4, key kb + col
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int qq = q * 32 + (v / 4) * 8 + half * 4 + (v % 4);
+        sum += exp2f(acc[v] * scale2 - smax[qq]) * sinv[qq];
+      }
+    }
+    sum += __shfl_xor(sum, 32, kWave);
+    if (half == 0 && key < k1) prow[key] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 passes (plain VALU; the small fp32 workloads only)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void score_pass1_f32(
+    const float* __restrict__ qa, const float* __restrict__ kc, int B, int H, int N, int A, int d,
+    int dh, int chunk_keys, int nchunks, float scale2, float2* __restrict__ ms_out) {
+  const int c = blockIdx.x, lh = blockIdx.y, b = blockIdx.z;
+  const int l = lh / H, h = lh % H;
+  const float* kbase = kc + (static_cast<size_t>(l) * B + b) * N * d + h * dh;
+  const int k0 = c * chunk_keys, k1 = min(N, k0 + chunk_keys);
+  for (int a = threadIdx.x; a < A; a += blockDim.x) {
+    const float* q = qa + ((static_cast<size_t>(l) * B + b) * A + a) * d + h * dh;
+    float m = -INFINITY, z = 0.f;
+    for (int j = k0; j < k1; ++j) {
+      const float* kr = kbase + static_cast<size_t>(j) * d;
+      float s = 0.f;
+      for (int t = 0; t < dh; ++t) s = fmaf(q[t], kr[t], s);
+      merge_ms(m, z, s * scale2, 1.f);
+    }
+    ms_out[((static_cast<size_t>(b) * gridDim.y + lh) * nchunks + c) * A + a] = make_float2(m, z);
+  }
+}
+
+__global__ __launch_bounds__(256) void score_pass2_f32(
+    const float* __restrict__ qa, const float* __restrict__ kc, int B, int H, int N, int A, int d,
+    int dh, int chunk_keys, int nchunks, float scale2, const float2* __restrict__ ms_in,
+    float* __restrict__ part) {
+  const int c = blockIdx.x, lh = blockIdx.y, b = blockIdx.z;
+  const int LH = gridDim.y;
+  const int l = lh / H, h = lh % H;
+  extern __shared__ float smi[];   // [2 * A]: max, 1/sum
+  for (int a = threadIdx.x; a < A; a += blockDim.x) {
+    float mm = -INFINITY, zz = 0.f;
+    const float2* p = ms_in + (static_cast<size_t>(b) * LH + lh) * nchunks * A + a;
+    for (int cc = 0; cc < nchunks; ++cc) merge_ms(mm, zz, p[static_cast<size_t>(cc) * A].x,
+                                                  p[static_cast<size_t>(cc) * A].y);
+    smi[a] = mm;
+    smi[A + a] = 1.f / zz;
+  }
+  __syncthreads();
+  const float* kbase = kc + (static_cast<size_t>(l) * B + b) * N * d + h * dh;
+  const int k0 = c * chunk_keys, k1 = min(N, k0 + chunk_keys);
+  for (int j = k0 + threadIdx.x; j < k1; j += blockDim.x) {
+    const float* kr = kbase + static_cast<size_t>(j) * d;
+    float sum = 0.f;
+    for (int a = 0; a < A; ++a) {
+      const float* q = qa + ((static_cast<size_t>(l) * B + b) * A + a) * d + h * dh;
+      float s = 0.f;
+      for (int t = 0; t < dh; ++t) s = fmaf(q[t], kr[t], s);
+      sum += exp2f(s * scale2 - smi[a]) * smi[A + a];
+    }
+    part[(static_cast<size_t>(b) * LH + lh) * N + j] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine
+// ---------------------------------------------------------------------------
+
+constexpr int kCombTokens = 64;     // tokens per combine-1 block
+constexpr int kCombThreads = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kCombThreads) void score_combine1(
+    const float* __restrict__ part, int LH, const float* __restrict__ mass_in,
+    const T* __restrict__ z, const T* __restrict__ zref, int N, int d,
+    float* __restrict__ mass, float* __restrict__ surprise, float* __restrict__ usum_blocks) {
+  const int b = blockIdx.y;
+  const int t0 = blockIdx.x * kCombTokens;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ float sp[4][kCombTokens];
+  __shared__ float su[kCombTokens];
+
+  // P: 4 interleaved groups of L*H rows, combined in fixed order
+  {
+    const int tok = t0 + lane;
+    float acc = 0.f;
+    if (tok < N) {
+      if (mass_in) {
+        if (wid == 0) acc = mass_in[static_cast<size_t>(b) * N + tok];
+      } else {
+        for (int r = wid; r < LH; r += 4) acc += part[(static_cast<size_t>(b) * LH + r) * N + tok];
+      }
+    }
+    sp[wid][lane] = acc;
+  }
+  // U: one wavefront per token, lanes over channels
+  for (int i = wid; i < kCombTokens; i += 4) {
+    const int tok = t0 + i;
+    float acc = 0.f;
+    if (tok < N) {
+      const T* zr = z + (static_cast<size_t>(b) * N + tok) * d;
+      const T* rr = zref + (static_cast<size_t>(b) * N + tok) * d;
+      for (int cc = lane; cc < d; cc += kWave) {
+        const float df = Elem<T>::load(zr, cc) - Elem<T>::load(rr, cc);
+        acc = fmaf(df, df, acc);
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) su[i] = acc;
+  }
+  __syncthreads();
+  if (wid == 0) {
+    const int tok = t0 + lane;
+    const float p = ((sp[0][lane] + sp[1][lane]) + sp[2][lane]) + sp[3][lane];
+    const float u = su[lane];
+    if (tok < N) {
+      mass[static_cast<size_t>(b) * N + tok] = p;
+      surprise[static_cast<size_t>(b) * N + tok] = u;
+    }
+    const float bs = wave_sum(tok < N ? u : 0.f);
+    if (lane == 0) usum_blocks[static_cast<size_t>(b) * gridDim.x + blockIdx.x] = bs;
+  }
+}
+
+__global__ __launch_bounds__(256) void score_combine2(
+    const float* __restrict__ mass, const float* __restrict__ surprise,
+    const float* __restrict__ usum_blocks, int nblocks, int N, float w_attn_norm, float w_surprise,
+    float* __restrict__ score, float* __restrict__ mass_out, float* __restrict__ surprise_out) {
+  const int b = blockIdx.y;
+  __shared__ float red[4];
+  float acc = 0.f;
+  for (int i = threadIdx.x; i < nblocks; i += blockDim.x) acc += usum_blocks[static_cast<size_t>(b) * nblocks + i];
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  const float total = ((red[0] + red[1]) + red[2]) + red[3];
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N) return;
+  const size_t o = static_cast<size_t>(b) * N + i;
+  const float p = mass[o], u = surprise[o];
+  float s = w_attn_norm * p;
+  if (total > 0.f) s += w_surprise * (u / total);
+  score[o] = s;
+  if (mass_out) mass_out[o] = p;
+  if (surprise_out) surprise_out[o] = u;
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+
+ScorePlan plan_score(int B, int L, int H, int N, int A, bool bf16) {
+  ScorePlan p;
+  const long long keys = static_cast<long long>(N) * L * H * B;
+  int ck;
+  if (bf16) {
+    // aim for ~2048 workgroups; chunks are whole 128-key wave rounds
+    long long want = (keys + 2047) / 2048;
+    ck = static_cast<int>(((want + 127) / 128) * 128);
+    if (ck < 128) ck = 128;
+    if (ck > 2048) ck = 2048;
+  } else {
+    ck = 256;
+  }
+  p.chunk_keys = ck;
+  p.nchunks = (N + ck - 1) / ck;
+  p.comb_blocks = (N + kCombTokens - 1) / kCombTokens;
+  p.ms_bytes = static_cast<size_t>(B) * L * H * p.nchunks * A * sizeof(float2);
+  p.part_bytes = static_cast<size_t>(B) * L * H * N * sizeof(float);
+  p.tok_bytes = static_cast<size_t>(B) * N * sizeof(float);
+  p.usum_bytes = static_cast<size_t>(B) * p.comb_blocks * sizeof(float);
+  return p;
+}
+
+hipError_t launch_score_mass(bool bf16, const void* qa, const void* kc, int B, int L, int H, int N,
+                             int A, int d, const ScorePlan& p, float2* ms, float* part,
+                             hipStream_t s, KernelTimer* timer) {
+  const int dh = d / H;
+  const float scale2 = kLog2e / sqrtf(static_cast<float>(dh));
+  const dim3 grid(p.nchunks, L * H, B);
+  if (bf16) {
+    {
+      TimedLaunch t(timer, "score_pass1", s);
+      score_pass1_bf16<<<grid, kScoreThreads, 0, s>>>(static_cast<const bf16_t*>(qa),
+          static_cast<const bf16_t*>(kc), B, H, N, A, d, p.chunk_keys, p.nchunks, scale2, ms);
+    }
+    TimedLaunch t(timer, "score_pass2", s);
+    score_pass2_bf16<<<grid, kScoreThreads, 0, s>>>(static_cast<const bf16_t*>(qa),
+        static_cast<const bf16_t*>(kc), B, H, N, A, d, p.chunk_keys, p.nchunks, scale2, ms, part);
+  } else {
+    {
+      TimedLaunch t(timer, "score_pass1", s);
+      score_pass1_f32<<<grid, 256, 0, s>>>(static_cast<const float*>(qa), static_cast<const float*>(kc),
+          B, H, N, A, d, dh, p.chunk_keys, p.nchunks, scale2, ms);
+    }
+    TimedLaunch t(timer, "score_pass2", s);
+    score_pass2_f32<<<grid, 256, 2 * A * sizeof(float), s>>>(static_cast<const float*>(qa),
+        static_cast<const float*>(kc), B, H, N, A, d, dh, p.chunk_keys, p.nchunks, scale2, ms, part);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score_combine(bool bf16, const float* part, int LH, const float* mass_in,
+                                const void* z, const void* zref, int B, int N, int d, float w_attn_norm,
+                                float w_surprise, const ScorePlan& p, float* mass_tmp, float* surprise_tmp,
+                                float* usum, float* score, float* mass_out, float* surprise_out,
+                                hipStream_t s, KernelTimer* timer) {
+  {
+    TimedLaunch t(timer, "score_combine", s);
+    const dim3 grid(p.comb_blocks, B);
+    if (bf16)
+      score_combine1<bf16_t><<<grid, kCombThreads, 0, s>>>(part, LH, mass_in, static_cast<const bf16_t*>(z),
+          static_cast<const bf16_t*>(zref), N, d, mass_tmp, surprise_tmp, usum);
+    else
+      score_combine1<float><<<grid, kCombThreads, 0, s>>>(part, LH, mass_in, static_cast<const float*>(z),
+          static_cast<const float*>(zref), N, d, mass_tmp, surprise_tmp, usum);
+  }
+  TimedLaunch t(timer, "score_combine", s);
+  score_combine2<<<dim3((N + 255) / 256, B), 256, 0, s>>>(mass_tmp, surprise_tmp, usum, p.comb_blocks, N,
+      w_attn_norm, w_surprise, score, mass_out, surprise_out);
+  return hipGetLastError();
+}
+
+}  // namespace wamc

@@ -1,0 +1,250 @@
+// Refresh-set selection with the age bound, and age bookkeeping.
+//
+// WAM-Cache (paperpeel 2610.11401) §1 and §4.4: tokens whose age counter
+// reached the bound G are forced into the refresh set; the set is filled by
+// score.  RealtimeWAM App. D.3 "Recursive reuse": an age cap of G permits at
+// most G consecutive reuses, so age is reset on refresh and incremented on
+// reuse.
+//
+// Design (one workgroup of 1024 threads per episode):
+//  * every token gets a unique 64-bit key  forced(1) | orderable score(32) |
+//    (2^31-1 - index)(31), so "largest key" = forced first, then higher
+//    score, then lower index; keys live in registers (up to 8 per thread, N <= 8192; larger N
+//    recomputes them from global memory in each pass);
+//  * the k_eff-th largest key is found by an MSB-first radix select: 8 passes
+//    of an 8-bit digit histogram in LDS, the bucket found by a wave-wide
+//    suffix scan -- no sort at all;
+//  * the refresh set = keys >= that threshold, compacted in ascending token
+//    order with a block-wide ballot/popcount scan, which also yields the
+//    new ages.
+// Everything is integer work, so the result is bit-exact by construction.
+#include "common.h"
+#include "launch.h"
+
+namespace wamc {
+
+__device__ __forceinline__ uint64_t rank_key(float s, bool forced, int i) {
+  uint32_t f = __float_as_uint(s);
+  uint32_t ord;
+  if ((f & 0x7fffffffu) > 0x7f800000u) {
+    ord = 0u;                       // NaN: below every number
+  } else {
+    if (f == 0x80000000u) f = 0u;   // -0.0 ranks equal to +0.0
+    ord = (f & 0x80000000u) ? ~f : (f | 0x80000000u);
+  }
+  return (static_cast<uint64_t>(forced) << 63) | (static_cast<uint64_t>(ord) << 31) |
+         static_cast<uint64_t>(0x7fffffffu - static_cast<uint32_t>(i));
+}
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+
+// KPT = keys held per thread in registers (N <= KPT * 1024); 0 = recompute
+// the keys from global memory in every pass (any N).
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
+    const float* __restrict__ score, int32_t* __restrict__ age, int N, int k, int G, int rows_cap,
+    int32_t* __restrict__ idx, int32_t* __restrict__ k_eff_out, int32_t* __restrict__ n_forced_out) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  score += static_cast<size_t>(b) * N;
+  age += static_cast<size_t>(b) * N;
+  idx += static_cast<size_t>(b) * N;
+
+  __shared__ uint32_t hist[256];
+  __shared__ int red[kSelWaves];
+  __shared__ uint32_t s_sel, s_rem;
+
+  constexpr int NK = KPT > 0 ? KPT : 1;
+  uint64_t keys[NK];
+  int nf = 0;
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int i = tid + j * kSelThreads;
+      keys[j] = 0;
+      if (i < N) {
+        const bool f = age[i] >= G;
+        nf += f;
+        keys[j] = rank_key(score[i], f, i);
+      }
+    }
+  } else {
+    keys[0] = 0;
+    for (int i = tid; i < N; i += kSelThreads) nf += age[i] >= G;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) nf += __shfl_xor(nf, o, kWave);
+  if (lane == 0) red[wid] = nf;
+  __syncthreads();
+  int n_forced = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) n_forced += red[w];
+  __syncthreads();
+
+  int ke = k > n_forced ? k : n_forced;
+  if (ke > rows_cap) ke = rows_cap;
+  const bool take_all = ke >= N, take_none = ke <= 0;
+
+  uint64_t thr = 0;
+  if (!take_all && !take_none) {
+    uint64_t prefix = 0;
+    uint32_t remaining = static_cast<uint32_t>(ke);
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      const uint64_t hi_mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      if constexpr (KPT > 0) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const int i = tid + j * kSelThreads;
+          if (i < N && (keys[j] & hi_mask) == prefix)
+            atomicAdd(&hist[(keys[j] >> shift) & 255u], 1u);
+        }
+      } else {
+        for (int i = tid; i < N; i += kSelThreads) {
+          const uint64_t key = rank_key(score[i], age[i] >= G, i);
+          if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+      }
+      __syncthreads();
+      if (wid == 0) {
+        // lane l owns bins 4l..4l+3; suffix sums find the bucket that holds
+        // the remaining-th largest key
+        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+        const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        const uint32_t s = h0 + h1 + h2 + h3;
+        uint32_t suf = s;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const uint32_t v = __shfl_down(suf, o, kWave);
+          if (lane + o < kWave) suf += v;
+        }
+        const uint32_t above = suf - s;
+        if (above < remaining && remaining <= suf) {
+          uint32_t c = above;
+          uint32_t sel;
+          if (c + h3 >= remaining) {
+            sel = 4 * lane + 3;
+          } else {
+            c += h3;
+            if (c + h2 >= remaining) {
+              sel = 4 * lane + 2;
+            } else {
+              c += h2;
+              if (c + h1 >= remaining) {
+                sel = 4 * lane + 1;
+              } else {
+                c += h1;
+                sel = 4 * lane;
+              }
+            }
+          }
+          s_sel = sel;
+          s_rem = remaining - c;
+        }
+      }
+      __syncthreads();
+      prefix |= static_cast<uint64_t>(s_sel) << shift;
+      remaining = s_rem;
+    }
+    thr = prefix;
+  }
+
+  // ascending-order compaction and age update, one 1024-token tile at a time
+  int base = 0;
+  auto compact = [&](int i, bool flag) {
+    const uint64_t ball = __ballot(flag);
+    const int wpre = __popcll(ball & ((1ull << lane) - 1ull));
+    if (lane == 0) red[wid] = __popcll(ball);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      const int c = red[w];
+      off += w < wid ? c : 0;
+      tot += c;
+    }
+    if (flag) idx[base + off + wpre] = i;
+    if (i < N) age[i] = flag ? 0 : age[i] + 1;
+    base += tot;
+    __syncthreads();
+  };
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (j * kSelThreads >= N) break;
+      const int i = tid + j * kSelThreads;
+      const bool flag = i < N && (take_all || (!take_none && keys[j] >= thr));
+      compact(i, flag);
+    }
+  } else {
+    for (int t0 = 0; t0 < N; t0 += kSelThreads) {
+      const int i = t0 + tid;
+      const bool flag = i < N && (take_all || (!take_none && rank_key(score[i], age[i] >= G, i) >= thr));
+      compact(i, flag);
+    }
+  }
+  for (int i = ke + tid; i < N; i += kSelThreads) idx[i] = -1;
+  if (tid == 0) {
+    k_eff_out[b] = ke;
+    if (n_forced_out) n_forced_out[b] = n_forced;
+  }
+}
+
+hipError_t launch_select(const float* score, int32_t* age, int B, int N, int k, int G, int rows_cap,
+                         int32_t* idx, int32_t* k_eff, int32_t* n_forced, hipStream_t s) {
+  const dim3 grid(B), block(kSelThreads);
+  if (N <= 1024)
+    select_topk_kernel<1><<<grid, block, 0, s>>>(score, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+  else if (N <= 2048)
+    select_topk_kernel<2><<<grid, block, 0, s>>>(score, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+  else if (N <= 4096)
+    select_topk_kernel<4><<<grid, block, 0, s>>>(score, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+  else if (N <= 8192)
+    select_topk_kernel<8><<<grid, block, 0, s>>>(score, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+  else
+    select_topk_kernel<0><<<grid, block, 0, s>>>(score, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Ages from a caller-given refresh set (idx_override): copy the set into the
+// output buffers, then age + 1 everywhere and 0 on the set.
+// ---------------------------------------------------------------------------
+
+__global__ void copy_set_kernel(const int32_t* __restrict__ idx_in, const int32_t* __restrict__ k_in,
+                                int B, int N, int rows_cap, int32_t* __restrict__ idx_out,
+                                int32_t* __restrict__ k_out) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < static_cast<size_t>(B) * N) idx_out[i] = idx_in[i];
+  if (i < static_cast<size_t>(B)) k_out[i] = rows_of(k_in, static_cast<int>(i), rows_cap);
+}
+
+__global__ void age_increment_kernel(int32_t* __restrict__ age, size_t total) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < total) age[i] += 1;
+}
+
+__global__ void age_reset_kernel(int32_t* __restrict__ age, const int32_t* __restrict__ idx,
+                                 const int32_t* __restrict__ k_eff, int N, int rows_cap) {
+  const int b = blockIdx.y;
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows_of(k_eff, b, rows_cap)) return;
+  const int t = idx[static_cast<size_t>(b) * N + r];
+  if (t >= 0 && t < N) age[static_cast<size_t>(b) * N + t] = 0;
+}
+
+hipError_t launch_ages_from_set(const int32_t* idx_in, const int32_t* k_in, int B, int N, int rows_cap,
+                                int32_t* idx_out, int32_t* k_out, int32_t* age, hipStream_t s) {
+  const size_t total = static_cast<size_t>(B) * N;
+  const int t = 256;
+  const unsigned g = static_cast<unsigned>((total + t - 1) / t);
+  if (idx_in != idx_out || k_in != k_out)
+    copy_set_kernel<<<g, t, 0, s>>>(idx_in, k_in, B, N, rows_cap, idx_out, k_out);
+  age_increment_kernel<<<g, t, 0, s>>>(age, total);
+  age_reset_kernel<<<dim3((rows_cap + t - 1) / t, B), t, 0, s>>>(age, idx_out, k_out, N, rows_cap);
+  return hipGetLastError();
+}
+
+}  // namespace wamc

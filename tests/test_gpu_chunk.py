@@ -1,0 +1,191 @@
+"""Whole refresh chunks on the GPU against the oracle (WAM-Cache §4.1-§4.4).
+
+* Rollouts driven by the oracle-chosen refresh set (idx_override): K/V cache,
+  every layer's output rows, ages and reference embeddings per chunk.
+* Rollouts with the library's own selection: the selected set is exactly the
+  oracle's selection applied to the GPU's scores, ages never exceed the bound.
+* Invariants on the GPU: k = N equals the dense prefill bitwise; k = 0 from
+  ages below the bound leaves the cache bitwise unchanged; a chunk replayed
+  from a snapshot is bitwise identical (fixed-order reductions).
+* The single-layer d=1536 workload at full size (N=4096, k=2458), in the
+  launch configuration the benchmark times, and a 4-layer slice of the
+  30-layer d=1536 stack (N=4680, k=2808).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import wamc_oracle as O
+from sparse_kv_refresh_amd import inputs as W
+from sparse_kv_refresh_amd import wamc
+
+from gpu_util import DEV, act, batch_q, batch_z, close, engine, max_rel, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_states(wl, r, prec):
+    out = []
+    for e in range(wl.batch):
+        st, _ = O.dense_prefill(r.z[e][0], r.weights, wl.n_heads, wl.ln_eps, prec)
+        st.age = r.ages0[e].astype(np.int64)
+        out.append(st)
+    return out
+
+
+def _compare_chunk(wl, eng, states, res, lo, t):
+    for b in range(wl.batch):
+        st, rs = states[b], res[b]
+        ke = int(eng.k_eff[b])
+        assert ke == rs.k_eff
+        assert np.array_equal(to_np(eng.idx[b])[:ke], rs.idx)
+        assert np.array_equal(to_np(eng.age[b]), st.age)
+        assert np.array_equal(to_np(eng.zref[b]), st.zref.astype(np.float32))
+        for l in range(wl.n_layers):
+            for nm, g, o in (("K", to_np(eng.k_cache[l, b]), st.K[l]), ("V", to_np(eng.v_cache[l, b]), st.V[l]),
+                             ("X", to_np(lo[l, b, :ke]), rs.outs[l])):
+                ok, err = close(wl, g, o)
+                assert ok, f"chunk {t} episode {b} layer {l} {nm}: error {err}"
+
+
+def _run_override_rollout(wl, chunks):
+    r = W.make_rollout(wl, chunks=chunks)
+    prec = O.Precision(wl.dtype)
+    states = _oracle_states(wl, r, prec)
+    eng = engine(wl, r)
+    L, B, N, d = wl.n_layers, wl.batch, wl.n_tokens, wl.d_model
+    eng.dense(batch_z(wl, r, 0))
+    eng.age.copy_(to_dev(np.stack(r.ages0)))
+    lo = torch.zeros((L, B, eng.rows_cap, d), dtype=torch.float32, device=DEV)
+    for t in range(1, chunks):
+        res = [O.refresh_chunk(states[e], r.z[e][t], r.qa[e][t], r.weights, wl.k, wl.age_bound, wl.n_heads,
+                               wl.ln_eps, wl.w_attn, wl.w_surprise, prec) for e in range(B)]
+        ov = np.full((B, N), -1, dtype=np.int32)
+        kk = np.zeros(B, dtype=np.int32)
+        for e in range(B):
+            ov[e, :res[e].k_eff] = res[e].idx
+            kk[e] = res[e].k_eff
+        eng.chunk(batch_z(wl, r, t), batch_q(wl, r, t), wl.k, idx_override=to_dev(ov), k_eff_override=to_dev(kk),
+                  layer_out=lo)
+        torch.cuda.synchronize()
+        _compare_chunk(wl, eng, states, res, lo, t)
+
+
+@pytest.mark.parametrize("name", ["c1_tiny", "t_fp32_ragged", "t_bf16_small", "t_bf16_batch"])
+def test_rollout_oracle_refresh_set(name):
+    wl = W.preset(name)
+    _run_override_rollout(wl, wl.chunks)
+
+
+def test_bench_workload_full_size():
+    """d=1536, 12 heads, FFN 8960, N=4096, k=2458 (60 %), ages U{0..3} after
+    the dense chunk: dense parity, then one refresh chunk with the oracle's
+    refresh set; rows_cap = k as the benchmark runs it."""
+    wl = W.preset("c2_layer")
+    r = W.make_rollout(wl, chunks=2)
+    prec = O.Precision(wl.dtype)
+    states = _oracle_states(wl, r, prec)
+    res = O.refresh_chunk(states[0], r.z[0][1], r.qa[0][1], r.weights, wl.k, wl.age_bound, wl.n_heads,
+                          wl.ln_eps, wl.w_attn, wl.w_surprise, prec)
+    assert res.k_eff == wl.k
+    eng = engine(wl, r, rows_cap=wl.k)
+    eng.dense(batch_z(wl, r, 0))
+    eng.age.copy_(to_dev(np.stack(r.ages0)))
+    lo = torch.zeros((1, 1, wl.k, wl.d_model), dtype=torch.float32, device=DEV)
+    # the library's own selection, checked against the oracle's on the GPU scores
+    age_before = to_np(eng.age[0]).copy()
+    eng.chunk(batch_z(wl, r, 1), batch_q(wl, r, 1), wl.k, layer_out=lo)
+    torch.cuda.synchronize()
+    gscore = to_np(eng.score[0])
+    assert max_rel(gscore, res.score) < 1e-4
+    sel_idx, sel_k, sel_age, _ = O.select(gscore, age_before, wl.k, wl.age_bound, cap=wl.k)
+    assert int(eng.k_eff[0]) == sel_k and np.array_equal(to_np(eng.idx[0])[:sel_k], sel_idx)
+    assert np.array_equal(to_np(eng.age[0]), sel_age)
+    if np.array_equal(sel_idx, res.idx):
+        _compare_chunk(wl, eng, states, [res], lo, 1)
+    # and driven by the oracle's refresh set
+    eng2 = engine(wl, r, rows_cap=wl.k)
+    eng2.dense(batch_z(wl, r, 0))
+    eng2.age.copy_(to_dev(np.stack(r.ages0)))
+    ov = np.full((1, wl.n_tokens), -1, dtype=np.int32)
+    ov[0, :res.k_eff] = res.idx
+    eng2.chunk(batch_z(wl, r, 1), batch_q(wl, r, 1), wl.k, idx_override=to_dev(ov),
+               k_eff_override=to_dev(np.array([res.k_eff], dtype=np.int32)), layer_out=lo)
+    torch.cuda.synchronize()
+    _compare_chunk(wl, eng2, states, [res], lo, 1)
+
+
+def test_stack_slice_d1536():
+    _run_override_rollout(W.preset("t_bf16_stack"), 3)
+
+
+@pytest.mark.parametrize("name", ["c1_tiny", "t_bf16_batch"])
+def test_own_selection_rollout(name):
+    wl = W.preset(name)
+    r = W.make_rollout(wl)
+    eng = engine(wl, r)
+    eng.dense(batch_z(wl, r, 0))
+    for t in range(1, wl.chunks):
+        age_before = to_np(eng.age).copy()
+        eng.chunk(batch_z(wl, r, t), batch_q(wl, r, t), wl.k)
+        torch.cuda.synchronize()
+        for b in range(wl.batch):
+            idx, k_eff, age, _ = O.select(to_np(eng.score[b]), age_before[b], wl.k, wl.age_bound)
+            assert int(eng.k_eff[b]) == k_eff
+            assert np.array_equal(to_np(eng.idx[b])[:k_eff], idx)
+            assert (to_np(eng.idx[b])[k_eff:] == -1).all()
+            assert np.array_equal(to_np(eng.age[b]), age)
+        assert int(eng.age.max()) <= wl.age_bound
+
+
+@pytest.mark.parametrize("name", ["c1_tiny", "t_bf16_small"])
+def test_full_refresh_equals_dense_on_gpu(name):
+    wl = W.preset(name)
+    r = W.make_rollout(wl, chunks=3)
+    eng = engine(wl, r)
+    L, B, N, d = wl.n_layers, wl.batch, wl.n_tokens, wl.d_model
+    eng.dense(batch_z(wl, r, 0))
+    eng.chunk(batch_z(wl, r, 1), batch_q(wl, r, 1), wl.k)        # stale mixture
+    eng.age.zero_()
+    lo = torch.zeros((L, B, N, d), dtype=torch.float32, device=DEV)
+    eng.chunk(batch_z(wl, r, 2), batch_q(wl, r, 2), N, layer_out=lo)
+    ref = engine(wl, r)
+    lo_ref = torch.zeros_like(lo)
+    ref.dense(batch_z(wl, r, 2), layer_out=lo_ref)
+    torch.cuda.synchronize()
+    assert int(eng.k_eff[0]) == N
+    assert torch.equal(eng.k_cache, ref.k_cache) and torch.equal(eng.v_cache, ref.v_cache)
+    assert torch.equal(lo, lo_ref)
+    assert torch.equal(eng.zref, ref.zref) and (eng.age == 0).all()
+
+
+def test_zero_refresh_keeps_cache_on_gpu():
+    wl = W.preset("t_bf16_small")
+    r = W.make_rollout(wl, chunks=2)
+    eng = engine(wl, r)
+    eng.dense(batch_z(wl, r, 0))
+    snap = eng.snapshot()
+    eng.chunk(batch_z(wl, r, 1), batch_q(wl, r, 1), 0)
+    torch.cuda.synchronize()
+    assert int(eng.k_eff[0]) == 0
+    assert torch.equal(eng.k_cache, snap["k_cache"]) and torch.equal(eng.v_cache, snap["v_cache"])
+    assert torch.equal(eng.zref, snap["zref"])
+    assert torch.equal(eng.age, snap["age"] + 1)
+
+
+@pytest.mark.parametrize("name", ["c1_tiny", "t_bf16_batch"])
+def test_replay_is_bitwise(name):
+    wl = W.preset(name)
+    r = W.make_rollout(wl, chunks=2)
+    eng = engine(wl, r)
+    eng.dense(batch_z(wl, r, 0))
+    snap = eng.snapshot()
+    outs = []
+    for _ in range(2):
+        eng.restore(snap)
+        lo = torch.zeros((wl.n_layers, wl.batch, eng.rows_cap, wl.d_model), dtype=torch.float32, device=DEV)
+        eng.chunk(batch_z(wl, r, 1), batch_q(wl, r, 1), wl.k, layer_out=lo)
+        torch.cuda.synchronize()
+        outs.append([lo.clone(), eng.k_cache.clone(), eng.v_cache.clone(), eng.score.clone(), eng.idx.clone()])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

@@ -1,0 +1,75 @@
+"""GPU DiT layers against the oracle: the dense prefill (every token through
+every layer, WAM-Cache §4.1) and a single refresh layer on a given row set
+(§3, §4.4: fresh K/V written before attention over all N keys)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import wamc_oracle as O
+from sparse_kv_refresh_amd import inputs as W
+from sparse_kv_refresh_amd import wamc
+
+from gpu_util import DEV, act, batch_z, close, engine, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["c1_tiny", "t_fp32_ragged", "t_bf16_small", "t_bf16_batch"])
+def test_dense_parity(name):
+    wl = W.preset(name)
+    r = W.make_rollout(wl, chunks=1)
+    prec = O.Precision(wl.dtype)
+    eng = engine(wl, r)
+    L, B, N, d = wl.n_layers, wl.batch, wl.n_tokens, wl.d_model
+    lo = torch.zeros((L, B, N, d), dtype=torch.float32, device=DEV)
+    z0 = batch_z(wl, r, 0)
+    eng.age.fill_(5)
+    eng.dense(z0, layer_out=lo)
+    torch.cuda.synchronize()
+    assert (eng.age == 0).all()
+    assert torch.equal(eng.zref, z0)
+    for b in range(B):
+        st, outs = O.dense_prefill(r.z[b][0], r.weights, wl.n_heads, wl.ln_eps, prec)
+        for l in range(L):
+            for name_, g, o in (("K", eng.k_cache[l, b], st.K[l]), ("V", eng.v_cache[l, b], st.V[l]),
+                                ("X", lo[l, b], outs[l])):
+                ok, err = close(wl, to_np(g), o)
+                assert ok, f"{name_} layer {l} episode {b}: error {err}"
+
+
+@pytest.mark.parametrize("name", ["c1_tiny", "t_bf16_small"])
+def test_refresh_layer_parity(name):
+    """One layer on 3/8 of the tokens, ascending ids, over a cache that holds
+    other values everywhere else."""
+    wl = W.preset(name)
+    r = W.make_rollout(wl, chunks=1)
+    prec = O.Precision(wl.dtype)
+    N, d = wl.n_tokens, wl.d_model
+    rng = np.random.default_rng(3)
+    m = (3 * N) // 8
+    idx = np.sort(rng.choice(N, size=m, replace=False)).astype(np.int32)
+    Kc = prec.store(rng.standard_normal((N, d)).astype(np.float32) * 0.5)
+    Vc = prec.store(rng.standard_normal((N, d)).astype(np.float32) * 0.5)
+    X = rng.standard_normal((m, d)).astype(np.float32)
+    Ko, Vo = Kc.astype(prec.acc).copy(), Vc.astype(prec.acc).copy()
+    want = O.block(X.astype(prec.acc), idx, r.weights[0], Ko, Vo, wl.n_heads, wl.ln_eps, prec)
+
+    dims = wamc.dims_for(wl)
+    w = wamc.Engine.upload_weights(r.weights, act(wl), DEV)[0]
+    rows_cap = m + 5                      # spare rows beyond k_eff stay untouched
+    x = torch.zeros((1, rows_cap, d), dtype=torch.float32, device=DEV)
+    x[0, :m] = torch.from_numpy(X).to(DEV)
+    x[0, m:] = 123.0
+    idx_full = np.full((1, N), -1, dtype=np.int32)
+    idx_full[0, :m] = idx
+    kc, vc = to_dev(Kc, act(wl))[None].contiguous(), to_dev(Vc, act(wl))[None].contiguous()
+    keff = torch.tensor([m], dtype=torch.int32, device=DEV)
+    ws = torch.empty(wamc.workspace_bytes(dims, rows_cap), dtype=torch.uint8, device=DEV)
+    wamc.refresh_layer(dims, 0, w, x, to_dev(idx_full), keff, rows_cap, kc, vc, ws)
+    torch.cuda.synchronize()
+    for nm, g, o in (("X", to_np(x[0, :m]), want), ("K", to_np(kc[0]), Ko), ("V", to_np(vc[0]), Vo)):
+        ok, err = close(wl, g, o)
+        assert ok, f"{nm}: {err}"
+    assert (x[0, m:] == 123.0).all()
+    untouched = np.setdiff1d(np.arange(N), idx)
+    assert np.array_equal(to_np(kc[0])[untouched], Kc[untouched])

@@ -1,0 +1,89 @@
+"""GPU refresh-set selection is bit-exact against the oracle (WAM-Cache §1,
+§4.4: forced tokens first, then score with a lower-index tie-break), on the
+oracle's own scores: idx, k_eff, forced counts and the updated ages."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import wamc_oracle as O
+from sparse_kv_refresh_amd import wamc
+
+from gpu_util import DEV
+
+pytestmark = pytest.mark.gpu
+
+
+def _dims(B, N, G):
+    return wamc.make_dims(B, 1, 128, 1, 128, N, 1, "fp32", G)
+
+
+def _scores(rng, B, N, kind):
+    if kind == "ties":
+        s = rng.choice(np.array([0.0, -0.0, 0.5, 1.0, np.nan, -2.0], dtype=np.float32), size=(B, N))
+    elif kind == "normal":
+        s = rng.standard_normal((B, N)).astype(np.float32)
+    else:   # mixed magnitudes incl. inf and subnormals
+        s = rng.standard_normal((B, N)).astype(np.float32) * np.float32(10.0) ** rng.integers(-40, 38, (B, N)).astype(np.float32)
+        s[rng.random((B, N)) < 0.05] = np.inf
+        s[rng.random((B, N)) < 0.05] = -np.inf
+        s[rng.random((B, N)) < 0.05] = np.nan
+    return s
+
+
+CASES = [
+    # B, N, k, G, rows_cap, score kind
+    (1, 1, 0, 0, 1, "normal"),
+    (1, 1, 1, 3, 1, "normal"),
+    (1, 7, 3, 2, 7, "ties"),
+    (2, 256, 64, 4, 256, "ties"),
+    (3, 1000, 400, 2, 1000, "mixed"),
+    (1, 1024, 1023, 1, 1024, "normal"),
+    (2, 1025, 1, 3, 1025, "ties"),
+    (1, 4096, 2458, 3, 2458, "normal"),
+    (2, 4680, 2808, 3, 4680, "ties"),
+    (4, 8192, 4096, 4, 4096, "mixed"),
+    (1, 9000, 5000, 2, 9000, "ties"),      # recompute-from-global path
+    (2, 20000, 777, 5, 20000, "mixed"),
+    (1, 3000, 0, 3, 3000, "normal"),       # k = 0: only forced tokens
+    (1, 3000, 3000, 3, 3000, "normal"),    # k = N: everything
+    (2, 3000, 100, 2, 500, "ties"),        # forced overflow beyond the row cap
+]
+
+
+@pytest.mark.parametrize("B,N,k,G,cap,kind", CASES)
+def test_select_bit_exact(B, N, k, G, cap, kind):
+    rng = np.random.default_rng(N * 31 + k)
+    score = _scores(rng, B, N, kind)
+    age = rng.integers(0, G + 2, size=(B, N)).astype(np.int32)
+    dims = _dims(B, N, G)
+    s_d = torch.from_numpy(score).to(DEV)
+    a_d = torch.from_numpy(age).to(DEV)
+    idx = torch.full((B, N), -7, dtype=torch.int32, device=DEV)
+    keff = torch.zeros(B, dtype=torch.int32, device=DEV)
+    nf = torch.zeros(B, dtype=torch.int32, device=DEV)
+    wamc.select(dims, s_d, a_d, k, cap, idx, keff, nf)
+    torch.cuda.synchronize()
+    for b in range(B):
+        want_idx, want_k, want_age, want_nf = O.select(score[b], age[b], k, G, cap=cap)
+        assert int(keff[b]) == want_k
+        assert int(nf[b]) == want_nf
+        got = idx[b].cpu().numpy()
+        assert np.array_equal(got[:want_k], want_idx)
+        assert (got[want_k:] == -1).all()
+        assert np.array_equal(a_d[b].cpu().numpy(), want_age)
+
+
+def test_select_repeatable():
+    rng = np.random.default_rng(5)
+    B, N = 2, 5000
+    score = torch.from_numpy(_scores(rng, B, N, "ties")).to(DEV)
+    age0 = torch.from_numpy(rng.integers(0, 4, (B, N)).astype(np.int32)).to(DEV)
+    dims = _dims(B, N, 3)
+    outs = []
+    for _ in range(2):
+        a = age0.clone()
+        idx = torch.empty((B, N), dtype=torch.int32, device=DEV)
+        keff = torch.empty(B, dtype=torch.int32, device=DEV)
+        wamc.select(dims, score, a, 1200, N, idx, keff)
+        outs.append((idx.cpu(), keff.cpu(), a.cpu()))
+    assert all(torch.equal(x, y) for x, y in zip(outs[0], outs[1]))

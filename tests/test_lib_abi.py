@@ -1,0 +1,124 @@
+"""The C-ABI library loads on a machine without a GPU, exports every function
+include/wamc.h declares, and rejects bad arguments on the host -- before any
+device call -- with the documented status codes.  (No compute call is made
+here; those run in the GPU tests.)"""
+import ctypes
+
+import pytest
+
+from sparse_kv_refresh_amd import inputs as W
+from sparse_kv_refresh_amd import wamc
+
+FAKE = 0x100000          # aligned dummy device address, never dereferenced
+MISALIGNED = FAKE + 4
+
+
+def _dims(**kw):
+    d = wamc.dims_for(W.preset("t_bf16_small"))
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_exports_every_declared_symbol():
+    L = wamc.lib()
+    names = wamc.header_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    for n in ("wamc_score", "wamc_select", "wamc_refresh_layer", "wamc_prefill_chunk", "wamc_dense_prefill"):
+        assert n in names
+
+
+def test_version_and_status_strings():
+    L = wamc.lib()
+    assert L.wamc_version() == 100
+    assert L.wamc_status_string(0) == b"ok"
+    assert L.wamc_status_string(3) == b"workspace too small"
+
+
+def test_workspace_bytes_grows_with_rows():
+    d = _dims()
+    a, b = wamc.workspace_bytes(d, 10), wamc.workspace_bytes(d, 300)
+    assert 0 < a < b and b % 256 == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("n_heads", 3, 1),          # d != H * dh
+    ("d_model", 260, 1),
+    ("batch", 0, 1),
+    ("age_bound", -1, 1),
+    ("dtype", 7, 1),
+    ("ln_eps", 0.0, 1),
+    ("head_dim", 64, 1),        # 2 * 64 != 256
+])
+def test_bad_dims(field, value, code):
+    d = _dims(**{field: value})
+    out = ctypes.c_size_t()
+    st = wamc.lib().wamc_workspace_bytes(ctypes.byref(d), 1, ctypes.byref(out))
+    assert st == code, wamc.lib().wamc_last_error()
+    assert wamc.lib().wamc_last_error() != b""
+
+
+def test_unsupported_head_dim_bf16():
+    d = _dims(n_heads=4, head_dim=64)
+    out = ctypes.c_size_t()
+    assert wamc.lib().wamc_workspace_bytes(ctypes.byref(d), 1, ctypes.byref(out)) == 2
+
+
+def test_select_argument_errors():
+    L = wamc.lib()
+    d = _dims()
+    N = d.n_tokens
+    # k out of range
+    assert L.wamc_select(ctypes.byref(d), FAKE, FAKE, N + 1, N, FAKE, FAKE, None, None) == 1
+    # rows_cap < k
+    assert L.wamc_select(ctypes.byref(d), FAKE, FAKE, 50, 40, FAKE, FAKE, None, None) == 1
+    # null / misaligned pointers
+    assert L.wamc_select(ctypes.byref(d), None, FAKE, 5, N, FAKE, FAKE, None, None) == 1
+    assert L.wamc_select(ctypes.byref(d), MISALIGNED, FAKE, 5, N, FAKE, FAKE, None, None) == 4
+    assert b"score" in L.wamc_last_error()
+
+
+def test_workspace_too_small():
+    L = wamc.lib()
+    d = _dims()
+    need = wamc.workspace_bytes(d, d.n_tokens)
+    lw = wamc.LayerW(*([FAKE] * 9))
+    arr = (wamc.LayerW * d.n_layers)(*([lw] * d.n_layers))
+    st = L.wamc_dense_prefill(ctypes.byref(d), arr, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1, None)
+    assert st == 3
+
+
+def test_refresh_layer_errors():
+    L = wamc.lib()
+    d = _dims()
+    lw = wamc.LayerW(*([FAKE] * 9))
+    ws = wamc.workspace_bytes(d, 100)
+    # layer out of range
+    assert L.wamc_refresh_layer(ctypes.byref(d), 5, ctypes.byref(lw), FAKE, FAKE, FAKE, 100, FAKE, FAKE,
+                                FAKE, ws, None) == 1
+    # rows_cap beyond N
+    assert L.wamc_refresh_layer(ctypes.byref(d), 0, ctypes.byref(lw), FAKE, FAKE, FAKE, d.n_tokens + 1, FAKE,
+                                FAKE, FAKE, ws, None) == 1
+    # a missing weight
+    bad = wamc.LayerW(*([FAKE] * 8 + [None]))
+    assert L.wamc_refresh_layer(ctypes.byref(d), 0, ctypes.byref(bad), FAKE, FAKE, FAKE, 100, FAKE, FAKE,
+                                FAKE, ws, None) == 1
+
+
+def test_prefill_chunk_override_needs_counts():
+    L = wamc.lib()
+    d = _dims()
+    lw = wamc.LayerW(*([FAKE] * 9))
+    arr = (wamc.LayerW * d.n_layers)(*([lw] * d.n_layers))
+    ws = wamc.workspace_bytes(d, d.n_tokens)
+    st = L.wamc_prefill_chunk(ctypes.byref(d), arr, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, FAKE, None,
+                              FAKE, FAKE, None, None, d.n_tokens, FAKE, ws, None)
+    assert st == 1 and b"k_eff_override" in L.wamc_last_error()
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        wamc._ptr(torch.zeros(4))
