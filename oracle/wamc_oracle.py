@@ -245,12 +245,20 @@ def combine(P: np.ndarray, U: np.ndarray, n_layers: int, n_heads: int, n_action:
 
 
 def score(z, zref, qa, K, n_heads: int, w_attn: float, w_surprise: float,
-          prec: Precision, mass: Optional[np.ndarray] = None):
+          prec: Precision, mass: Optional[np.ndarray] = None, n_action: Optional[int] = None):
     """Returns (score float32 [N], P, U).  `mass` replaces P when an action
-    expert supplies its own attention mass."""
+    expert supplies its own attention mass: it is the same sum over layers,
+    heads and action queries, so it is normalised by the same L*H*A
+    (`n_action` = A must then be given)."""
     L = K.shape[0]
-    A = qa.shape[1] if qa is not None else 1
-    P = attention_mass(qa, K, n_heads, prec) if mass is None else prec.load(mass)
+    if mass is None:
+        A = qa.shape[1]
+        P = attention_mass(qa, K, n_heads, prec)
+    else:
+        if n_action is None:
+            raise ValueError("a supplied attention mass needs n_action")
+        A = n_action
+        P = prec.load(mass)
     U = surprise(z, zref, prec)
     return combine(P, U, L, n_heads, A, w_attn, w_surprise), P, U
 
@@ -319,7 +327,8 @@ def refresh_chunk(state: State, z: np.ndarray, qa: Optional[np.ndarray], weights
     """Score against the current cache, select, gather the refreshed rows
     (and store their reference embedding), then run every layer on them.
     `state` is updated in place."""
-    s, P, U = score(z, state.zref, qa, state.K, n_heads, w_attn, w_surprise, prec, mass)
+    s, P, U = score(z, state.zref, qa, state.K, n_heads, w_attn, w_surprise, prec, mass,
+                    n_action=None if qa is None else qa.shape[1])
     if idx_override is None:
         idx, k_eff, age, n_forced = select(s, state.age, k, G, cap)
     else:

@@ -56,7 +56,7 @@ def test_score_with_supplied_mass():
     score = torch.empty((1, N), dtype=torch.float32, device=DEV)
     wamc.score(dims, z1, zref, None, None, score, ws, mass_in=to_dev(mass))
     s_o, _, _ = O.score(r.z[0][1], states[0].zref, None, states[0].K, wl.n_heads, wl.w_attn, wl.w_surprise,
-                        prec, mass=mass[0])
+                        prec, mass=mass[0], n_action=wl.n_action)
     assert max_rel(to_np(score[0]), s_o) < 1e-5
 
 

@@ -170,3 +170,16 @@ def test_cost_model_against_pages():
     # per-chunk FLOPs of the 30-layer stack: dense 14.416 TF, 60 % refresh 8.650 TF
     assert abs(O.prefill_flops(N, N, L, d, F) / 1e12 - 14.416) < 1e-3
     assert abs(O.prefill_flops(2808, N, L, d, F) / 1e12 - 8.650) < 1e-3
+
+
+def test_supplied_mass_matches_computed_mass():
+    """An action expert that supplies exactly the attention mass the oracle
+    would compute must get exactly the same scores (same L*H*A normaliser)."""
+    wl, r, prec = _setup()
+    st, _ = O.dense_prefill(r.z[0][0], r.weights, wl.n_heads, wl.ln_eps, prec)
+    s, P, U = O.score(r.z[0][1], st.zref, r.qa[0][1], st.K, wl.n_heads, wl.w_attn, wl.w_surprise, prec)
+    s2, _, _ = O.score(r.z[0][1], st.zref, None, st.K, wl.n_heads, wl.w_attn, wl.w_surprise, prec,
+                       mass=P, n_action=wl.n_action)
+    assert np.array_equal(s, s2)
+    with pytest.raises(ValueError):
+        O.score(r.z[0][1], st.zref, None, st.K, wl.n_heads, wl.w_attn, wl.w_surprise, prec, mass=P)
