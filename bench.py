@@ -1,0 +1,277 @@
+"""Benchmark of the sparse KV-refresh prefill on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2_layer]
+
+A step is one refresh chunk: token scores (attention mass + surprise),
+selection with the age bound, gather, then every layer on the refreshed rows
+(WAM-Cache, paperpeel 2610.11401, §4).  The default workload is the single
+bf16 layer with d=1536, 12 heads, FFN 8960, N=4096 visual tokens and k=2458
+(60 % refresh), 64 action queries, age bound 3.  Inputs are seeded synthetic
+data already resident in HBM; the state after the dense chunk carries random
+ages U{0..3} so some tokens are forced.
+
+Printed as one JSON line: ms per refresh chunk (the metric), the library's own
+dense prefill of the same chunk, the speedup and its k_eff/N bound, refreshed
+tokens/s, the roofline of the dominant kernel (HIP events around every launch
+in a second pass of the same K steps), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2_layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--profile-steps", action="store_true",
+                    help="only run warmup + timed refresh steps (for rocprofv3 runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_work(wl, k_eff_total: int):
+    """Algorithmic work per launch of each kernel kind: FLOPs for the MFMA
+    kernels, HBM bytes for the memory-bound ones (act = 2 bytes in bf16)."""
+    L, B, N, d, F, H, A = wl.n_layers, wl.batch, wl.n_tokens, wl.d_model, wl.d_ffn, wl.n_heads, wl.n_action
+    M = k_eff_total
+    es = 2 if wl.dtype == "bf16" else 4
+    return {
+        "gemm_qkv": ("flop", 2.0 * M * 3 * d * d),
+        "gemm_out_resid": ("flop", 2.0 * M * d * d),
+        "gemm_up_gelu": ("flop", 2.0 * M * F * d),
+        "gemm_down_resid": ("flop", 2.0 * M * d * F),
+        "attention": ("flop", 4.0 * M * N * d),
+        # K cache once (+ queries) per pass
+        "score_pass1": ("byte", float(L * B * N * d * es + L * B * A * d * es)),
+        "score_pass2": ("byte", float(L * B * N * d * es + L * B * A * d * es + L * H * B * N * 4)),
+        "gather": ("byte", float(M * d * (es + 4 + es))),
+        "ln_mod": ("byte", float(M * d * (4 + es))),
+        "select": ("byte", float(B * N * (4 + 4 + 4 + 4))),
+    }
+
+
+def source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "sparse_kv_refresh_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+KERNEL_SOURCE = {"gemm_qkv": "gemm.hip", "gemm_out_resid": "gemm.hip", "gemm_up_gelu": "gemm.hip",
+                 "gemm_down_resid": "gemm.hip", "attention": "attention.hip", "score_pass1": "score.hip",
+                 "score_pass2": "score.hip", "select": "select.hip", "gather": "rows.hip", "ln_mod": "rows.hip"}
+
+
+def measured_traffic(kind: str, config: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kind}_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCE[kind]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds: float):
+    """The oracle as it stands, on the host cores: one dense chunk to build the
+    state, then refresh chunks of the same workload until ~`seconds`."""
+    from oracle import wamc_oracle as O
+    from sparse_kv_refresh_amd import inputs as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    r = W.make_rollout(wl, chunks=2)
+    prec = O.Precision(wl.dtype)
+    t0 = time.perf_counter()
+    st, _ = O.dense_prefill(r.z[0][0], r.weights, wl.n_heads, wl.ln_eps, prec)
+    dense_s = time.perf_counter() - t0
+    st.age = r.ages0[0].astype(np.int64)
+    times = []
+    while True:
+        s = st.copy()
+        t0 = time.perf_counter()
+        O.refresh_chunk(s, r.z[0][1], r.qa[0][1], r.weights, wl.k, wl.age_bound, wl.n_heads, wl.ln_eps,
+                        wl.w_attn, wl.w_surprise, prec)
+        times.append(time.perf_counter() - t0)
+        if sum(times) + dense_s >= seconds or len(times) >= 5:
+            break
+    return {"value": 1e3 * float(np.median(times)), "unit": "ms/chunk", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} refresh chunk(s) of the {wl.name} workload (score + select + "
+                      f"{wl.n_layers} layer(s), k={wl.k} of N={wl.n_tokens}), numpy "
+                      f"{'float32+bf16 rounding' if wl.dtype == 'bf16' else 'float64'}; the oracle's dense "
+                      f"chunk took {1e3 * dense_s:.0f} ms"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); episodes shard across GPUs "
+              "with no exchange, so the per-GPU figure at --gpus 1 is the whole story", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_kv_refresh_amd import inputs as W
+    from sparse_kv_refresh_amd import wamc
+
+    wl = W.preset(args.config)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    adt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    r = W.make_rollout(wl, chunks=2)
+    dims = wamc.dims_for(wl)
+    weights = wamc.Engine.upload_weights(r.weights, adt, dev)
+    rows_cap = wl.k if wl.k >= (wl.n_tokens + 1) // 2 else wl.n_tokens
+    eng = wamc.Engine(dims, weights, rows_cap, dev)
+
+    def bz(t):
+        return torch.from_numpy(np.stack([r.z[e][t] for e in range(wl.batch)])).to(dev, adt).contiguous()
+
+    z0, z1 = bz(0), bz(1)
+    qa = torch.from_numpy(np.stack([r.qa[e][1] for e in range(wl.batch)], axis=1)).to(dev, adt).contiguous()
+    stream = torch.cuda.current_stream()
+
+    eng.dense(z0)
+    eng.age.copy_(torch.from_numpy(np.stack(r.ages0)).to(dev))
+    torch.cuda.synchronize()
+
+    def refresh_step():
+        eng.chunk(z1, qa, wl.k, stream=stream)
+
+    def dense_step():
+        eng.dense(z1, stream=stream)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return a.elapsed_time(b) / steps, 1e3 * wall / steps
+
+    if args.profile_steps:
+        ms, _ = timed(refresh_step, args.steps, args.warmup)
+        if args.copy_calibration:
+            src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.steps, "ms_per_step": ms}))
+        return
+
+    ms_refresh, wall_refresh = timed(refresh_step, args.steps, args.warmup)
+    k_eff = eng.k_eff.cpu().numpy().astype(np.int64)
+    k_total = int(k_eff.sum())
+    ms_dense, _ = timed(dense_step, args.steps, max(1, args.warmup // 2))
+    # restore a refresh-ready state (the dense steps reset every age to 0)
+    eng.dense(z0)
+    eng.age.copy_(torch.from_numpy(np.stack(r.ages0)).to(dev))
+    for _ in range(args.warmup):
+        refresh_step()
+    torch.cuda.synchronize()
+
+    # per-kernel pass: HIP events around every launch, same K steps
+    wamc.timing_enable(True)
+    for _ in range(args.steps):
+        refresh_step()
+    torch.cuda.synchronize()
+    kt = wamc.timing_read()
+    wamc.timing_enable(False)
+
+    work = kernel_work(wl, k_total)
+    kernels = {}
+    for kind, (n, tot) in kt.items():
+        entry = {"launches": n, "avg_us": 1e3 * tot / max(n, 1), "ms_per_step": tot / args.steps}
+        if kind in work:
+            unit, amount = work[kind]
+            avg_s = tot / max(n, 1) / 1e3
+            if unit == "flop":
+                entry["tflops"] = amount / avg_s / 1e12
+                entry["frac_bf16_peak"] = entry["tflops"] / PEAK_BF16_TFLOPS
+            else:
+                entry["gbs"] = amount / avg_s / 1e9
+                entry["frac_hbm_peak"] = entry["gbs"] / PEAK_HBM_GBS
+        kernels[kind] = entry
+    dominant = max((k for k in kernels if k in work), key=lambda k: kernels[k]["ms_per_step"])
+    unit, amount = work[dominant]
+    avg_s = kernels[dominant]["avg_us"] / 1e6
+    if unit == "flop":
+        ach = amount / avg_s / 1e12
+        peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
+    else:
+        ach = amount / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
+    roof["traffic"] = measured_traffic(dominant, args.config)
+    roof["kernel"] = dominant
+    roof["work_per_launch"] = amount
+    roof["avg_launch_us"] = kernels[dominant]["avg_us"]
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_seconds)
+
+    bound = wl.n_tokens * wl.batch / max(k_total, 1)
+    line = {
+        "metric": "refresh-prefill ms/chunk & speedup vs dense at 60% refresh; MFMA/HBM % peak",
+        "value": ms_refresh,
+        "unit": "ms/chunk",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_refresh,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_layers": wl.n_layers, "d_model": wl.d_model, "n_heads": wl.n_heads,
+                   "d_ffn": wl.d_ffn, "n_tokens": wl.n_tokens, "k": wl.k, "k_eff": k_eff.tolist(),
+                   "n_action": wl.n_action, "age_bound": wl.age_bound, "batch": wl.batch,
+                   "rows_cap": rows_cap, "parallelism": "single GPU"},
+        "dense_ms_per_chunk": ms_dense,
+        "speedup_vs_dense": ms_dense / ms_refresh,
+        "speedup_bound": bound,
+        "speedup_frac_of_bound": (ms_dense / ms_refresh) / bound,
+        "refreshed_tokens_per_s": k_total / (ms_refresh / 1e3),
+        "wall_ms_per_step": wall_refresh,
+        "roofline": roof,
+        "kernels": kernels,
+        "kernel_timing": "second pass of the same steps with HIP events around every launch on the launch stream",
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

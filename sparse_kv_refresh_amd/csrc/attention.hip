@@ -16,10 +16,17 @@
 //     accumulator registers (converted to bf16), V^T comes from a transposed
 //     copy of the V tile in LDS; each A fragment is two 8-byte LDS reads.
 //   * The next tile's K/V rows are fetched into registers while the current
-//     tile is multiplied (single LDS buffer, two barriers per tile).
+//     tile is multiplied (single LDS buffer, two barriers per tile); V is
+//     transposed in registers (4 keys x 8 dh per thread) and written to LDS
+//     as 8-byte rows of V^T.
+//   * Softmax VALU work is kept minimal: the scale is folded into one FMA
+//     feeding v_exp_f32, only the last (ragged) tile is masked, and the
+//     output rescale is lazy.
 // fp32 path: one wavefront per query row with a VALU online softmax.
 #include "common.h"
 #include "launch.h"
+
+#include <type_traits>
 
 namespace wamc {
 
@@ -29,138 +36,208 @@ constexpr int kAttnThreads = 256;
 constexpr int kAttnQ = 128;            // queries per workgroup
 constexpr int kAttnKeys = 64;          // keys per tile
 constexpr int kDh = 128;
-constexpr int kKsStride = kDh + 8;     // padded LDS rows (bf16)
 constexpr int kVtStride = kAttnKeys + 4;
 
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a, float scale2) {
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+// Lazy rescaling: the running max only moves when a tile's max exceeds it by
+// more than 2^kLazy in probability (log2 units), so most tiles skip the
+// rescale of the output accumulators; exp2 arguments stay <= kLazy.
+constexpr float kLazy = 8.0f;
+constexpr int kGroups = 2;                      // key-split groups of 4 waves
+constexpr int kAttnThreads2 = kAttnThreads * kGroups;
+constexpr int kKsBytes = kAttnKeys * kDh * 2;   // one K tile, 256-byte rows, XOR-swizzled chunks
+constexpr int kVtElems = kDh * kVtStride;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16-byte chunk c (0..15) of K row r lives at chunk c ^ (r & 15): the 16 rows
+// of one ds_read_b128 phase then cover all 64 banks.
+__device__ __forceinline__ int ks_chunk(int row, int c) { return row * 16 + (c ^ (row & 15)); }
+
+__global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a, float scale2) {
+  // 1-D grid over (q-tile, head, episode), q-tile fastest, remapped so the
+  // q-tiles of one head run on one XCD and share its K/V in that L2
+  const int qtiles = (a.rows_cap + kAttnQ - 1) / kAttnQ;
+  const int id = xcd_remap(blockIdx.x, qtiles * a.H * a.B);
+  const int qt = id % qtiles, h = (id / qtiles) % a.H, b = id / (qtiles * a.H);
   const int rows = rows_of(a.k_eff, b, a.rows_cap);
   const int q0 = qt * kAttnQ;
   if (q0 >= rows) return;
 
-  __shared__ bf16_t Ks[kAttnKeys * kKsStride];
-  __shared__ bf16_t Vt[kDh * kVtStride];
+  // per group: K tiles double-buffered (filled by direct-to-LDS loads), V^T
+  // single-buffered (written from registers)
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kGroups * (2 * kKsBytes + kVtElems * 2)];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int grp = wid >> 2, gw = wid & 3, gtid = tid & (kAttnThreads - 1);
   const int half = lane >> 5, col = lane & 31;
   const int N = a.N, d = a.d;
+  unsigned char* gbase = smem + grp * (2 * kKsBytes + kVtElems * 2);
+  uint4* Ks0 = reinterpret_cast<uint4*>(gbase);
+  bf16_t* Vt = reinterpret_cast<bf16_t*>(gbase + 2 * kKsBytes);
   const bf16_t* Kc = static_cast<const bf16_t*>(a.k_cache) + static_cast<size_t>(b) * N * d + h * kDh;
   const bf16_t* Vc = static_cast<const bf16_t*>(a.v_cache) + static_cast<size_t>(b) * N * d + h * kDh;
 
-  // Q^T fragments: lane (half, col) = query q0 + wid*32 + col,
+  // Q^T fragments: lane (half, col) = query q0 + gw*32 + col,
   // k-step s slot j <-> dh = s*16 + half*8 + j
-  const int qrow = q0 + wid * 32 + col;
+  const int qrow = q0 + gw * 32 + col;
   const bf16_t* Qp = static_cast<const bf16_t*>(a.q) + (static_cast<size_t>(b) * a.rows_cap + qrow) * d + h * kDh;
   uint4 qf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s)
     qf[s] = qrow < rows ? *reinterpret_cast<const uint4*>(Qp + s * 16 + half * 8) : make_uint4(0, 0, 0, 0);
 
-  uint4 rk[4], rv[4];
-  auto load_tile = [&](int kbase) {
+  const int ntiles = (N + kAttnKeys - 1) / kAttnKeys;
+  const int iters = (ntiles + kGroups - 1) / kGroups;
+  // group grp takes tiles grp, grp + 2, grp + 4, ...
+  auto issue_k = [&](int it, int stage) {
+    const int t = it * kGroups + grp;
+    if (t >= ntiles) return;
+    // 64 rows x 16 chunks = 1024 chunks, 4 per thread; instruction i of wave
+    // gw fills LDS chunks (i*4 + gw)*64 + lane
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int chunk = tid + i * kAttnThreads;
-      const int kk = kbase + (chunk >> 4), c8 = (chunk & 15) * 8;          // K: 16 threads per row
-      rk[i] = kk < N ? *reinterpret_cast<const uint4*>(Kc + static_cast<size_t>(kk) * d + c8)
-                     : make_uint4(0, 0, 0, 0);
-      const int kv = kbase + (chunk & 63), c8v = (chunk >> 6) * 8;        // V: a wave spans 64 keys
-      rv[i] = kv < N ? *reinterpret_cast<const uint4*>(Vc + static_cast<size_t>(kv) * d + c8v)
-                     : make_uint4(0, 0, 0, 0);
+      const int c = (i * 4 + gw) * 64 + lane;
+      const int row = c >> 4, ch = (c & 15) ^ (row & 15);
+      const int key = min(t * kAttnKeys + row, N - 1);   // rows past N: a valid row, masked later
+      const bf16_t* src = Kc + static_cast<size_t>(key) * d + ch * 8;
+      uint4* dst = Ks0 + stage * (kKsBytes / 16) + (i * 4 + gw) * 64;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
     }
   };
-  auto store_tile = [&]() {
+  const int vkb = gtid & 15, vdb = gtid >> 4;
+  uint4 rv[4];
+  auto load_v = [&](int it) {
+    const int t = it * kGroups + grp;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int chunk = tid + i * kAttnThreads;
-      *reinterpret_cast<uint4*>(&Ks[(chunk >> 4) * kKsStride + (chunk & 15) * 8]) = rk[i];
-      const int kv = chunk & 63, c8v = (chunk >> 6) * 8;
-      const uint32_t w[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+      const int kv = t * kAttnKeys + vkb * 4 + i;
+      rv[i] = (t < ntiles && kv < N) ? *reinterpret_cast<const uint4*>(Vc + static_cast<size_t>(kv) * d + vdb * 8)
+                                     : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_v = [&]() {
+    // Vt[dh][key]: for each of the 8 dh of this block, the 4 keys' values
+    const uint32_t w0[4] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w};
+    const uint32_t w1[4] = {rv[1].x, rv[1].y, rv[1].z, rv[1].w};
+    const uint32_t w2[4] = {rv[2].x, rv[2].y, rv[2].z, rv[2].w};
+    const uint32_t w3[4] = {rv[3].x, rv[3].y, rv[3].z, rv[3].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Vt[(c8v + 2 * j) * kVtStride + kv] = static_cast<bf16_t>(w[j] & 0xffffu);
-        Vt[(c8v + 2 * j + 1) * kVtStride + kv] = static_cast<bf16_t>(w[j] >> 16);
-      }
+    for (int j = 0; j < 4; ++j) {
+      uint2 ev, od;
+      ev.x = __byte_perm(w0[j], w1[j], 0x5410);   // dh 2j:   keys 0, 1
+      ev.y = __byte_perm(w2[j], w3[j], 0x5410);   //          keys 2, 3
+      od.x = __byte_perm(w0[j], w1[j], 0x7632);   // dh 2j+1: keys 0, 1
+      od.y = __byte_perm(w2[j], w3[j], 0x7632);
+      *reinterpret_cast<uint2*>(&Vt[(vdb * 8 + 2 * j) * kVtStride + vkb * 4]) = ev;
+      *reinterpret_cast<uint2*>(&Vt[(vdb * 8 + 2 * j + 1) * kVtStride + vkb * 4]) = od;
     }
   };
 
+  // running max in raw logit units (the softmax scale is folded into exp2)
   float m_run = -INFINITY, l_run = 0.f;
+  const float lazy = kLazy / scale2;
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
 
-  const int ntiles = (N + kAttnKeys - 1) / kAttnKeys;
-  load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile((t + 1) * kAttnKeys);
-
-    f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
+  // one 32-key half (kb) of tile t held in LDS stage `stage`
+  auto half_tile = [&](int t, int stage, int kb) {
+    const uint4* Ks = Ks0 + stage * (kKsBytes / 16);
+    f32x16_t sacc = f32x16_t{};
+    const int krow = kb * 32 + col;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16_t* kr = &Ks[(kb * 32 + col) * kKsStride + half * 8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kr + s * 16));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8_t, qf[s]), sacc[kb], 0, 0, 0);
-      }
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, Ks[ks_chunk(krow, 2 * s + half)]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8_t, qf[s]), sacc, 0, 0, 0);
     }
-    // sacc[kb][v]: key t*64 + kb*32 + (v/4)*8 + half*4 + v%4, query col
-    const int kbase = t * kAttnKeys;
-    float tmax = -INFINITY;
+    // sacc[v]: key t*64 + kb*32 + (v/4)*8 + half*4 + v%4, query col
+    const int kbase = t * kAttnKeys + kb * 32;
+    if (kbase + 32 > N) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int v = 0; v < 16; ++v)
+        if (kbase + (v / 4) * 8 + half * 4 + (v % 4) >= N) sacc[v] = -INFINITY;
+    }
+    float tmax = sacc[0];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = kbase + kb * 32 + (v / 4) * 8 + half * 4 + (v % 4);
-        const float sv = key < N ? sacc[kb][v] * scale2 : -INFINITY;
-        sacc[kb][v] = sv;
-        tmax = fmaxf(tmax, sv);
-      }
+    for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, sacc[v]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    float psum = 0.f;
+    if (__ballot(tmax > m_run + lazy)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale2);
+      l_run *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    const float mb = -m_run * scale2;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = exp2f(sacc[kb][v] - m_new);
-        sacc[kb][v] = p;
-        psum += p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= alpha;
-
-    // O^T[dh][q] += V^T[dh][key] P^T[key][q]; step (kb, tt) covers keys
+    for (int v = 0; v < 16; ++v) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale2, mb));
+      sacc[v] = p;
+      l_run += p;
+    }
+    // O^T[dh][q] += V^T[dh][key] P^T[key][q]; step tt covers keys
     // kb*32 + 16*tt + (j/4)*8 + half*4 + j%4 for slot j
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int tt = 0; tt < 2; ++tt) {
+      uint4 pk;
+      pk.x = pack_bf16x2(sacc[8 * tt + 0], sacc[8 * tt + 1]);
+      pk.y = pack_bf16x2(sacc[8 * tt + 2], sacc[8 * tt + 3]);
+      pk.z = pack_bf16x2(sacc[8 * tt + 4], sacc[8 * tt + 5]);
+      pk.w = pack_bf16x2(sacc[8 * tt + 6], sacc[8 * tt + 7]);
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pk);
+      const int koff = kb * 32 + 16 * tt + half * 4;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        uint4 pk;
-        pk.x = pack_bf16x2(sacc[kb][8 * tt + 0], sacc[kb][8 * tt + 1]);
-        pk.y = pack_bf16x2(sacc[kb][8 * tt + 2], sacc[kb][8 * tt + 3]);
-        pk.z = pack_bf16x2(sacc[kb][8 * tt + 4], sacc[kb][8 * tt + 5]);
-        pk.w = pack_bf16x2(sacc[kb][8 * tt + 6], sacc[kb][8 * tt + 7]);
-        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pk);
-        const int koff = kb * 32 + 16 * tt + half * 4;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16_t* vr = &Vt[(db * 32 + col) * kVtStride + koff];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < 4; ++db) {
+        const bf16_t* vr = &Vt[(db * 32 + col) * kVtStride + koff];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
       }
+    }
+  };
+
+  issue_k(0, 0);
+  load_v(0);
+  for (int it = 0; it < iters; ++it) {
+    // K tile `it` (direct to LDS) and the V rows in registers have landed ...
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));   // vmcnt(0)
+    // ... and every wave is done with the previous tile's LDS
+    __builtin_amdgcn_s_barrier();
+    store_v();
+    issue_k(it + 1, (it + 1) & 1);
+    load_v(it + 1);
+    __syncthreads();
+    const int t = it * kGroups + grp;
+    if (t < ntiles) {
+      half_tile(t, it & 1, 0);
+      half_tile(t, it & 1, 1);
+    }
   }
 
-  const float l = l_run + __shfl_xor(l_run, 32, kWave);
+  // merge the two key groups: group 1 hands (o, m, l) to group 0 through LDS
+  __syncthreads();
+  float* xch = reinterpret_cast<float*>(smem);
+  constexpr int kX = 66;   // floats per lane: 64 of o, m, l
+  if (grp == 1) {
+    float* dst = xch + static_cast<size_t>(gw) * kX * 64 + lane;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) dst[(db * 16 + v) * 64] = o[db][v];
+    dst[64 * 64] = m_run;
+    dst[65 * 64] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  const float* src = xch + static_cast<size_t>(gw) * kX * 64 + lane;
+  const float m1 = src[64 * 64], l1 = src[65 * 64];
+  const float m = fmaxf(m_run, m1);
+  const float e0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m) * scale2);
+  const float e1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * scale2);
+  const float lsum = l_run * e0 + l1 * e1;
+  const float l = lsum + __shfl_xor(lsum, 32, kWave);
   if (qrow >= rows) return;
   const float inv = 1.0f / l;
   bf16_t* Op = static_cast<bf16_t*>(a.o) + (static_cast<size_t>(b) * a.rows_cap + qrow) * d + h * kDh;
@@ -169,9 +246,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a, 
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       // elements v = g4*4 .. g4*4+3: dh rows db*32 + g4*8 + half*4 + 0..3
+      float r[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = g4 * 4 + e;
+        r[e] = (o[db][v] * e0 + src[(db * 16 + v) * 64] * e1) * inv;
+      }
       uint2 w;
-      w.x = pack_bf16x2(o[db][g4 * 4 + 0] * inv, o[db][g4 * 4 + 1] * inv);
-      w.y = pack_bf16x2(o[db][g4 * 4 + 2] * inv, o[db][g4 * 4 + 3] * inv);
+      w.x = pack_bf16x2(r[0], r[1]);
+      w.y = pack_bf16x2(r[2], r[3]);
       *reinterpret_cast<uint2*>(Op + db * 32 + g4 * 8 + half * 4) = w;
     }
 }
@@ -231,8 +314,8 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s, KernelT
   TimedLaunch t(timer, "attention", s);
   const float scale2 = kLog2e / sqrtf(static_cast<float>(a.dh));
   if (bf16) {
-    const dim3 grid((a.rows_cap + kAttnQ - 1) / kAttnQ, a.H, a.B);
-    attn_bf16_kernel<<<grid, kAttnThreads, 0, s>>>(a, scale2);
+    const unsigned grid = static_cast<unsigned>(((a.rows_cap + kAttnQ - 1) / kAttnQ) * a.H * a.B);
+    attn_bf16_kernel<<<grid, kAttnThreads2, 0, s>>>(a, scale2);
   } else {
     const dim3 grid((a.rows_cap + 3) / 4, a.H, a.B);
     attn_f32_kernel<<<grid, 256, 0, s>>>(a, scale2);

@@ -83,13 +83,8 @@ __device__ __forceinline__ bool tile_empty(const GemmArgs& g, int m0, int rows) 
 // XCD-aware remap of a linear workgroup id, then grouped (GM row-tiles)
 // ordering over a tiles_m x tiles_n grid.
 __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int kXcd = 8, GM = 8;
-  const int T = tiles_m * tiles_n;
-  const int per = (T + kXcd - 1) / kXcd;
-  int tall = T % kXcd;
-  if (tall == 0) tall = kXcd;
-  const int xcd = pid % kXcd, local = pid / kXcd;
-  const int id = xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+  constexpr int GM = 8;
+  const int id = xcd_remap(pid, tiles_m * tiles_n);
   const int group = id / (GM * tiles_n);
   const int first_m = group * GM;
   const int gsize = min(tiles_m - first_m, GM);
@@ -105,6 +100,18 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kLdsK = kBK + 8;   // padded LDS row (bf16 elements)
 constexpr int kGemmThreads = 256;
+#ifndef WAMC_GEMM_STAGES
+#define WAMC_GEMM_STAGES 3
+#endif
+#ifndef WAMC_GEMM_BK
+#define WAMC_GEMM_BK 64
+#endif
+constexpr int kGemmStages = WAMC_GEMM_STAGES;
+constexpr int kDtlBK = WAMC_GEMM_BK;
+#ifndef WAMC_GEMM_GENERIC
+#define WAMC_GEMM_GENERIC 0
+#endif
+constexpr bool kForceGeneric = WAMC_GEMM_GENERIC != 0;
 
 __device__ __forceinline__ bf16x8_t frag(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
@@ -199,6 +206,148 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) 
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA GEMM with direct-to-LDS loads (K % 64 == 0)
+//
+// Global tiles go straight into LDS with global_load_lds_dwordx4 (no VGPR
+// staging), STAGES k-tiles in flight in a ring of LDS buffers.  A direct-to-
+// LDS instruction writes 16 bytes per lane at consecutive LDS addresses, so
+// the tile layout in LDS is chosen by *which* global chunk each lane fetches:
+// chunk (row, kc) of a tile lives at LDS chunk row*CPR + swz_kc(row, kc), an
+// XOR swizzle under which the rows of an MFMA fragment read hit distinct
+// banks.  Rows past M / Nout load a clamped (valid) row whose
+// results are never stored.
+// ---------------------------------------------------------------------------
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt vmcnt(N) with expcnt / lgkmcnt left at their maxima (gfx9 encoding)
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Column key of element chunk (row, kc) in a tile with CPR 16-byte chunks per
+// row.  gfx950 LDS has 64 banks (a 256-byte window) and serves ds_read_b128
+// 16 lanes at a time; an MFMA fragment read has 16 consecutive rows at the
+// same kc in each phase, so the XOR key makes those 16 rows land in 16
+// different 16-byte bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz_kc(int row, int kc) {
+  if constexpr (CPR == 8) return kc ^ ((row >> 1) & 7);   // 128-byte rows: 2 rows per window
+  else return kc ^ ((row >> 2) & 3);                      // 64-byte rows: 4 rows per window
+}
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int kc) {
+  return row * CPR + swz_kc<CPR>(row, kc);
+}
+
+template <int EPI, int BK, int STAGES>
+__global__ __launch_bounds__(kGemmThreads, (STAGES * 256 * BK * 2 <= 80 * 1024) ? 2 : 1)
+void gemm_bf16_dtl_kernel(GemmArgs g) {
+  constexpr int CPR = BK / 8;                       // 16-byte chunks per tile row
+  constexpr int CHUNKS = kBM * CPR;                 // per operand per stage
+  constexpr int LOADS = 2 * CHUNKS / kGemmThreads;  // direct-to-LDS loads per thread per k-tile
+  constexpr int LOADS_A = LOADS / 2;
+  const int tiles_m = (g.M + kBM - 1) / kBM, tiles_n = (g.Nout + kBN - 1) / kBN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  if (tile_empty(g, m0, kBM)) return;
+
+  __shared__ uint4 lds[STAGES][2][CHUNKS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int half = lane >> 5, col = lane & 31;
+  const bf16_t* A = static_cast<const bf16_t*>(g.a);
+  const bf16_t* W = static_cast<const bf16_t*>(g.w);
+  const int K = g.K;
+
+  // load i of this thread fills LDS chunk c = ((i % LOADS_A)*4 + wid)*64 + lane
+  // of operand i / LOADS_A; it fetches the element chunk that the swizzle
+  // maps there
+  int goff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int c = ((i % LOADS_A) * 4 + wid) * 64 + lane;
+    const int row = c / CPR;
+    const int kc = swz_kc<CPR>(row, c % CPR);   // the XOR key is its own inverse
+    if (i < LOADS_A) goff[i] = min(m0 + row, g.M - 1) * K + kc * 8;
+    else goff[i] = min(n0 + row, g.Nout - 1) * K + kc * 8;
+  }
+  auto issue = [&](int kt, int stage) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const bf16_t* src = (i < LOADS_A ? A : W) + goff[i] + kt * BK;
+      uint4* dst = &lds[stage][i / LOADS_A][((i % LOADS_A) * 4 + wid) * 64];
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+
+  const int ra0 = wm * 64 + col, ra1 = ra0 + 32;
+  const int rb0 = wn * 64 + col, rb1 = rb0 + 32;
+
+  const int nk = K / BK;
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < nk) issue(p, p);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this thread's chunks of tile kt have landed in LDS (tiles issued after
+    // it may still be in flight) ...
+    const int ahead = min(STAGES - 2, nk - 1 - kt);
+    if constexpr (STAGES >= 4) {
+      if (ahead >= 2) wait_vmcnt<2 * LOADS>();
+      else if (ahead == 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+    } else if constexpr (STAGES == 3) {
+      if (ahead >= 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    // ... and everybody's: a plain s_barrier, without the memory fence of
+    // __syncthreads() that would also drain the loads still in flight
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const uint4* as = lds[kt % STAGES][0];
+    const uint4* ws = lds[kt % STAGES][1];
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int kc = 2 * s + half;
+      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, as[swz<CPR>(ra0, kc)]);
+      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, as[swz<CPR>(ra1, kc)]);
+      const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, ws[swz<CPR>(rb0, kc)]);
+      const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, ws[swz<CPR>(rb1, kc)]);
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + wm * 64 + i * 32 + (v / 4) * 8 + half * 4 + (v % 4);
+      const RowInfo ri = row_info(g, m);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * 64 + j * 32 + col;
+        epilogue<EPI, bf16_t>(g, ri, m, n, acc[i][j][v]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 GEMM (VALU)
 // ---------------------------------------------------------------------------
 
@@ -259,7 +408,14 @@ static const char* gemm_name(const GemmArgs& g, GemmEpi e) {
 hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer) {
   if (g.M <= 0 || g.Nout <= 0) return hipSuccess;
   TimedLaunch t(timer, gemm_name(g, epi), s);
-  if (bf16) {
+  if (bf16 && g.K % 64 == 0 && !kForceGeneric) {
+    const unsigned grid = static_cast<unsigned>(((g.M + kBM - 1) / kBM) * ((g.Nout + kBN - 1) / kBN));
+    switch (epi) {
+      case EPI_QKV: gemm_bf16_dtl_kernel<EPI_QKV, kDtlBK, kGemmStages><<<grid, kGemmThreads, 0, s>>>(g); break;
+      case EPI_RESID: gemm_bf16_dtl_kernel<EPI_RESID, kDtlBK, kGemmStages><<<grid, kGemmThreads, 0, s>>>(g); break;
+      case EPI_GELU: gemm_bf16_dtl_kernel<EPI_GELU, kDtlBK, kGemmStages><<<grid, kGemmThreads, 0, s>>>(g); break;
+    }
+  } else if (bf16) {
     const unsigned grid = static_cast<unsigned>(((g.M + kBM - 1) / kBM) * ((g.Nout + kBN - 1) / kBN));
     switch (epi) {
       case EPI_QKV: gemm_bf16_kernel<EPI_QKV><<<grid, kGemmThreads, 0, s>>>(g); break;

@@ -259,58 +259,90 @@ __global__ __launch_bounds__(256) void score_pass2_f32(
 // combine
 // ---------------------------------------------------------------------------
 
-constexpr int kCombTokens = 64;     // tokens per combine-1 block
+constexpr int kCombTokens = 16;     // tokens per combine-1 block (4 per wavefront)
 constexpr int kCombThreads = 256;
+
+// sum over one 16-byte chunk of (z - zref)^2
+__device__ __forceinline__ float sq_diff16(const bf16_t* z, const bf16_t* r) {
+  const uint4 a = *reinterpret_cast<const uint4*>(z);
+  const uint4 b = *reinterpret_cast<const uint4*>(r);
+  const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float d0 = __uint_as_float(wa[i] << 16) - __uint_as_float(wb[i] << 16);
+    const float d1 = __uint_as_float(wa[i] & 0xffff0000u) - __uint_as_float(wb[i] & 0xffff0000u);
+    acc = fmaf(d0, d0, acc);
+    acc = fmaf(d1, d1, acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ float sq_diff16(const float* z, const float* r) {
+  const float4 a = *reinterpret_cast<const float4*>(z);
+  const float4 b = *reinterpret_cast<const float4*>(r);
+  const float d0 = a.x - b.x, d1 = a.y - b.y, d2 = a.z - b.z, d3 = a.w - b.w;
+  return fmaf(d0, d0, fmaf(d1, d1, fmaf(d2, d2, d3 * d3)));
+}
 
 template <typename T>
 __global__ __launch_bounds__(kCombThreads) void score_combine1(
     const float* __restrict__ part, int LH, const float* __restrict__ mass_in,
     const T* __restrict__ z, const T* __restrict__ zref, int N, int d,
     float* __restrict__ mass, float* __restrict__ surprise, float* __restrict__ usum_blocks) {
+  constexpr int kPer = 16 / sizeof(T);   // elements per 16-byte chunk
   const int b = blockIdx.y;
   const int t0 = blockIdx.x * kCombTokens;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  __shared__ float sp[4][kCombTokens];
+  __shared__ float sp[16][kCombTokens];
   __shared__ float su[kCombTokens];
 
-  // P: 4 interleaved groups of L*H rows, combined in fixed order
+  // P: 16 interleaved groups of the L*H partial rows, combined in fixed order
   {
-    const int tok = t0 + lane;
+    const int tk = tid & (kCombTokens - 1), grp = tid / kCombTokens;
+    const int tok = t0 + tk;
     float acc = 0.f;
     if (tok < N) {
       if (mass_in) {
-        if (wid == 0) acc = mass_in[static_cast<size_t>(b) * N + tok];
+        if (grp == 0) acc = mass_in[static_cast<size_t>(b) * N + tok];
       } else {
-        for (int r = wid; r < LH; r += 4) acc += part[(static_cast<size_t>(b) * LH + r) * N + tok];
+        for (int r = grp; r < LH; r += 16) acc += part[(static_cast<size_t>(b) * LH + r) * N + tok];
       }
     }
-    sp[wid][lane] = acc;
+    sp[grp][tk] = acc;
   }
-  // U: one wavefront per token, lanes over channels
-  for (int i = wid; i < kCombTokens; i += 4) {
-    const int tok = t0 + i;
+  // U: each wavefront takes 4 tokens, lanes stride over 16-byte chunks
+  const int chunks = d / kPer;
+  float u[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tok = t0 + wid * 4 + j;
     float acc = 0.f;
     if (tok < N) {
       const T* zr = z + (static_cast<size_t>(b) * N + tok) * d;
       const T* rr = zref + (static_cast<size_t>(b) * N + tok) * d;
-      for (int cc = lane; cc < d; cc += kWave) {
-        const float df = Elem<T>::load(zr, cc) - Elem<T>::load(rr, cc);
-        acc = fmaf(df, df, acc);
-      }
+      for (int c = lane; c < chunks; c += kWave) acc += sq_diff16(zr + c * kPer, rr + c * kPer);
     }
-    acc = wave_sum(acc);
-    if (lane == 0) su[i] = acc;
+    u[j] = acc;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float v = wave_sum(u[j]);
+    if (lane == 0) su[wid * 4 + j] = v;
   }
   __syncthreads();
-  if (wid == 0) {
-    const int tok = t0 + lane;
-    const float p = ((sp[0][lane] + sp[1][lane]) + sp[2][lane]) + sp[3][lane];
-    const float u = su[lane];
+  if (tid < kCombTokens) {
+    const int tok = t0 + tid;
+    float p = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < 16; ++gi) p += sp[gi][tid];
     if (tok < N) {
       mass[static_cast<size_t>(b) * N + tok] = p;
-      surprise[static_cast<size_t>(b) * N + tok] = u;
+      surprise[static_cast<size_t>(b) * N + tok] = su[tid];
     }
-    const float bs = wave_sum(tok < N ? u : 0.f);
+  }
+  if (wid == 0) {
+    const float v = lane < kCombTokens && t0 + lane < N ? su[lane] : 0.f;
+    const float bs = wave_sum(v);
     if (lane == 0) usum_blocks[static_cast<size_t>(b) * gridDim.x + blockIdx.x] = bs;
   }
 }
