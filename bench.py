@@ -156,7 +156,9 @@ def main():
     qa = torch.from_numpy(np.stack([r.qa[e][1] for e in range(wl.batch)], axis=1)).to(dev, adt).contiguous()
     stream = torch.cuda.current_stream()
 
-    eng.dense(z0)
+    if not args.profile_steps:
+        # profiled runs skip the dense chunk so every traced launch is a refresh launch
+        eng.dense(z0)
     eng.age.copy_(torch.from_numpy(np.stack(r.ages0)).to(dev))
     torch.cuda.synchronize()
 

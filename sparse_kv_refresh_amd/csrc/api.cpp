@@ -328,7 +328,7 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
 
   g.a = hbuf; g.w = w->w_o; g.bias = w->b_o; g.Nout = D; g.K = D;
   g.resid_in = x_in; g.resid_out = x_out; g.gate = gate1;
-  e = launch_gemm(bf16, EPI_RESID, g, s, tm);
+  e = launch_gemm(bf16, EPI_RESID_OUT, g, s, tm);
   if (e != hipSuccess) return e;
 
   e = launch_ln_mod(bf16, x_out, shift2, scale2, B, rows_cap, k_eff, D, d->ln_eps, hbuf, s, tm);
@@ -340,7 +340,7 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
 
   g.a = gbuf; g.w = w->w_2; g.bias = w->b_2; g.Nout = D; g.K = F;
   g.resid_in = x_out; g.resid_out = x_out; g.gate = gate2;
-  return launch_gemm(bf16, EPI_RESID, g, s, tm);
+  return launch_gemm(bf16, EPI_RESID_DOWN, g, s, tm);
 }
 
 hipError_t run_score(const wamc_dims* d, const void* z, const void* zref, const void* q_act,

@@ -80,4 +80,23 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
 }
 
+// erf by the rational approximation of Abramowitz & Stegun, Handbook of
+// Mathematical Functions (1964), formula 7.1.26: for x >= 0,
+//   erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
+//   t = 1 / (1 + p x),  |error| <= 1.5e-7,
+// extended to x < 0 by oddness.  Used where the result is rounded to bf16
+// (relative precision 2^-8), so the approximation error is invisible.
+__device__ __forceinline__ float erf_as7126(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
+                                       -0.284496736f), 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
+  return copysignf(1.0f - poly * e, x);
+}
+
+__device__ __forceinline__ float gelu_erf_fast(float x) {
+  return 0.5f * x * (1.0f + erf_as7126(x * 0.70710678118654752440f));
+}
+
 }  // namespace wamc

@@ -9,7 +9,7 @@
 // Epilogues (applied to acc + bias, all in f32):
 //   EPI_QKV   : Q -> q_out (act), K/V -> written straight into this layer's
 //               cache at the row's token index (the scatter is fused here);
-//   EPI_RESID : out = in + gate * v        (gated residual, f32 stream);
+//   EPI_RESID_OUT / EPI_RESID_DOWN : out = in + gate * v   (gated residual, f32 stream);
 //   EPI_GELU  : g = act(GELU_erf(v)).
 //
 // bf16 path: 128x128x64 tiles, 4 waves in a 2x2 layout, each wave 64x64 as
@@ -59,7 +59,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const RowInfo& ri, i
       T* cache = static_cast<T*>(which == 1 ? g.k_cache : g.v_cache);
       Elem<T>::store(cache, (static_cast<size_t>(ri.b) * g.n_tokens + tok) * d + c, v);
     }
-  } else if constexpr (EPI == EPI_RESID) {
+  } else if constexpr (EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN) {
     const size_t o = static_cast<size_t>(m) * g.Nout + n;
     g.resid_out[o] = g.resid_in[o] + Elem<T>::load(static_cast<const T*>(g.gate), n) * v;
   } else {
@@ -93,15 +93,11 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
   tn = in_group / gsize;
 }
 
-// ---------------------------------------------------------------------------
-// bf16 MFMA GEMM
-// ---------------------------------------------------------------------------
-
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kLdsK = kBK + 8;   // padded LDS row (bf16 elements)
 constexpr int kGemmThreads = 256;
 #ifndef WAMC_GEMM_STAGES
-#define WAMC_GEMM_STAGES 3
+#define WAMC_GEMM_STAGES 2
 #endif
 #ifndef WAMC_GEMM_BK
 #define WAMC_GEMM_BK 64
@@ -112,6 +108,109 @@ constexpr int kDtlBK = WAMC_GEMM_BK;
 #define WAMC_GEMM_GENERIC 0
 #endif
 constexpr bool kForceGeneric = WAMC_GEMM_GENERIC != 0;
+
+// ---------------------------------------------------------------------------
+// tile epilogue of the bf16 kernels
+//
+// One pass over the 128 rows of the tile fills a row table in LDS (row
+// validity, the episode/row split and, for QKV, the cache row of the row's
+// token), so the per-element work is a table read, the bias and the store.
+// ---------------------------------------------------------------------------
+
+template <int EPI>
+__device__ __forceinline__ void fill_row_table(const GemmArgs& g, int m0, int* tab) {
+  const int t = threadIdx.x;
+  if (t < kBM) {
+    const int m = m0 + t;
+    const RowInfo ri = row_info(g, m);
+    int r0 = -1, r1 = -1;
+    if (ri.valid) {
+      r0 = m;
+      if constexpr (EPI == EPI_QKV) {
+        const int tok = g.idx ? g.idx[static_cast<size_t>(ri.b) * g.n_tokens + ri.r] : ri.r;
+        r1 = (tok >= 0 && tok < g.n_tokens) ? ri.b * g.n_tokens + tok : -1;
+      }
+    }
+    tab[t] = r0;
+    tab[kBM + t] = r1;
+  }
+}
+
+// acc[i][j][v] of wave (wm, wn): row lr = wm*64 + i*32 + (v/4)*8 + half*4 + v%4,
+// column n0 + wn*64 + j*32 + col.
+template <int EPI>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t (&acc)[2][2], int m0, int n0,
+                                              int wm, int wn, int half, int col, const int* tab) {
+  float bias[2];
+  int ncol[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    ncol[j] = n0 + wn * 64 + j * 32 + col;
+    bias[j] = ncol[j] < g.Nout ? bf16_to_f32(static_cast<const bf16_t*>(g.bias)[ncol[j]]) : 0.f;
+  }
+  if constexpr (EPI == EPI_QKV) {
+    const int d = g.d_model;
+    bf16_t* dst[2];
+    int cc[2];
+    bool use_tok[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int which = ncol[j] / d;
+      cc[j] = ncol[j] - which * d;
+      use_tok[j] = which != 0;
+      dst[j] = static_cast<bf16_t*>(which == 0 ? g.q_out : (which == 1 ? g.k_cache : g.v_cache));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr = wm * 64 + i * 32 + (v / 4) * 8 + half * 4 + (v % 4);
+        const int rq = tab[lr], rkv = tab[kBM + lr];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = use_tok[j] ? rkv : rq;
+          if (r >= 0 && ncol[j] < g.Nout)
+            dst[j][static_cast<size_t>(r) * d + cc[j]] = f32_to_bf16(acc[i][j][v] + bias[j]);
+        }
+      }
+  } else if constexpr (EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN) {
+    float gate[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      gate[j] = ncol[j] < g.Nout ? bf16_to_f32(static_cast<const bf16_t*>(g.gate)[ncol[j]]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr = wm * 64 + i * 32 + (v / 4) * 8 + half * 4 + (v % 4);
+        const int r = tab[lr];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (r >= 0 && ncol[j] < g.Nout) {
+            const size_t o = static_cast<size_t>(r) * g.Nout + ncol[j];
+            g.resid_out[o] = g.resid_in[o] + gate[j] * (acc[i][j][v] + bias[j]);
+          }
+        }
+      }
+  } else {
+    bf16_t* out = static_cast<bf16_t*>(g.g_out);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr = wm * 64 + i * 32 + (v / 4) * 8 + half * 4 + (v % 4);
+        const int r = tab[lr];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (r >= 0 && ncol[j] < g.Nout)
+            out[static_cast<size_t>(r) * g.Nout + ncol[j]] = f32_to_bf16(gelu_erf_fast(acc[i][j][v] + bias[j]));
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA GEMM
+// ---------------------------------------------------------------------------
 
 __device__ __forceinline__ bf16x8_t frag(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
@@ -190,19 +289,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) 
 
   // C layout of a 32x32 block: lane (half, col), element v ->
   // row (v/4)*8 + half*4 + v%4, column col.
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * 64 + i * 32 + (v / 4) * 8 + half * 4 + (v % 4);
-      const RowInfo ri = row_info(g, m);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + col;
-        epilogue<EPI, bf16_t>(g, ri, m, n, acc[i][j][v]);
-      }
-    }
-  }
+  int* tab = reinterpret_cast<int*>(&As[0][0]);   // the last k-tile ended with a barrier
+  fill_row_table<EPI>(g, m0, tab);
+  __syncthreads();
+  tile_epilogue<EPI>(g, acc, m0, n0, wm, wn, half, col, tab);
 }
 
 // ---------------------------------------------------------------------------
@@ -332,19 +422,11 @@ void gemm_bf16_dtl_kernel(GemmArgs g) {
     }
   }
 
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * 64 + i * 32 + (v / 4) * 8 + half * 4 + (v % 4);
-      const RowInfo ri = row_info(g, m);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + col;
-        epilogue<EPI, bf16_t>(g, ri, m, n, acc[i][j][v]);
-      }
-    }
-  }
+  __syncthreads();   // every wave is done with the LDS stages
+  int* tab = reinterpret_cast<int*>(&lds[0][0][0]);
+  fill_row_table<EPI>(g, m0, tab);
+  __syncthreads();
+  tile_epilogue<EPI>(g, acc, m0, n0, wm, wn, half, col, tab);
 }
 
 // ---------------------------------------------------------------------------
@@ -402,7 +484,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 static const char* gemm_name(const GemmArgs& g, GemmEpi e) {
   if (e == EPI_QKV) return "gemm_qkv";
   if (e == EPI_GELU) return "gemm_up_gelu";
-  return g.K == g.d_model ? "gemm_out_resid" : "gemm_down_resid";
+  return e == EPI_RESID_OUT ? "gemm_out_resid" : "gemm_down_resid";
 }
 
 hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer) {
@@ -412,21 +494,24 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
     const unsigned grid = static_cast<unsigned>(((g.M + kBM - 1) / kBM) * ((g.Nout + kBN - 1) / kBN));
     switch (epi) {
       case EPI_QKV: gemm_bf16_dtl_kernel<EPI_QKV, kDtlBK, kGemmStages><<<grid, kGemmThreads, 0, s>>>(g); break;
-      case EPI_RESID: gemm_bf16_dtl_kernel<EPI_RESID, kDtlBK, kGemmStages><<<grid, kGemmThreads, 0, s>>>(g); break;
+      case EPI_RESID_OUT: gemm_bf16_dtl_kernel<EPI_RESID_OUT, kDtlBK, kGemmStages><<<grid, kGemmThreads, 0, s>>>(g); break;
+      case EPI_RESID_DOWN: gemm_bf16_dtl_kernel<EPI_RESID_DOWN, kDtlBK, kGemmStages><<<grid, kGemmThreads, 0, s>>>(g); break;
       case EPI_GELU: gemm_bf16_dtl_kernel<EPI_GELU, kDtlBK, kGemmStages><<<grid, kGemmThreads, 0, s>>>(g); break;
     }
   } else if (bf16) {
     const unsigned grid = static_cast<unsigned>(((g.M + kBM - 1) / kBM) * ((g.Nout + kBN - 1) / kBN));
     switch (epi) {
       case EPI_QKV: gemm_bf16_kernel<EPI_QKV><<<grid, kGemmThreads, 0, s>>>(g); break;
-      case EPI_RESID: gemm_bf16_kernel<EPI_RESID><<<grid, kGemmThreads, 0, s>>>(g); break;
+      case EPI_RESID_OUT: gemm_bf16_kernel<EPI_RESID_OUT><<<grid, kGemmThreads, 0, s>>>(g); break;
+      case EPI_RESID_DOWN: gemm_bf16_kernel<EPI_RESID_DOWN><<<grid, kGemmThreads, 0, s>>>(g); break;
       case EPI_GELU: gemm_bf16_kernel<EPI_GELU><<<grid, kGemmThreads, 0, s>>>(g); break;
     }
   } else {
     const unsigned grid = static_cast<unsigned>(((g.M + kFBM - 1) / kFBM) * ((g.Nout + kFBN - 1) / kFBN));
     switch (epi) {
       case EPI_QKV: gemm_f32_kernel<EPI_QKV><<<grid, 256, 0, s>>>(g); break;
-      case EPI_RESID: gemm_f32_kernel<EPI_RESID><<<grid, 256, 0, s>>>(g); break;
+      case EPI_RESID_OUT: gemm_f32_kernel<EPI_RESID_OUT><<<grid, 256, 0, s>>>(g); break;
+      case EPI_RESID_DOWN: gemm_f32_kernel<EPI_RESID_DOWN><<<grid, 256, 0, s>>>(g); break;
       case EPI_GELU: gemm_f32_kernel<EPI_GELU><<<grid, 256, 0, s>>>(g); break;
     }
   }

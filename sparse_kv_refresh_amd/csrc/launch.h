@@ -60,7 +60,9 @@ hipError_t launch_ln_mod(bool bf16, const float* x, const void* shift, const voi
                          KernelTimer* timer);
 
 // ----- GEMM (gemm.hip) -----
-enum GemmEpi { EPI_QKV = 0, EPI_RESID = 1, EPI_GELU = 2 };
+// EPI_RESID_OUT and EPI_RESID_DOWN share one epilogue; they are separate
+// instances so profilers tell the two projections apart.
+enum GemmEpi { EPI_QKV = 0, EPI_RESID_OUT = 1, EPI_GELU = 2, EPI_RESID_DOWN = 3 };
 struct GemmArgs {
   const void* a;        // [M, K] act, row-major
   const void* w;        // [Nout, K] act, row-major (linear-layer layout)
@@ -74,7 +76,7 @@ struct GemmArgs {
   void* v_cache;
   const int32_t* idx;   // nullable: [B, N] token of each row (identity when null)
   int n_tokens, d_model;
-  // EPI_RESID: out[m, c] = in[m, c] + gate[c] * (acc + bias[c])   (f32)
+  // EPI_RESID_*: out[m, c] = in[m, c] + gate[c] * (acc + bias[c])   (f32)
   const float* resid_in;
   float* resid_out;
   const void* gate;     // [Nout] act
