@@ -12,14 +12,15 @@
 //   EPI_RESID_OUT / EPI_RESID_DOWN : out = in + gate * v   (gated residual, f32 stream);
 //   EPI_GELU  : g = act(GELU_erf(v)).
 //
-// bf16 path: 128x128x64 tiles, 4 waves in a 2x2 layout, each wave 64x64 as
-// 2x2 v_mfma_f32_32x32x16_bf16 blocks; A and W tiles double-buffered in LDS
-// (rows padded by 16 bytes so the 32 lanes of a fragment read hit distinct
-// banks), one barrier per k-tile, global loads for tile k+1 in flight while
-// tile k is multiplied.  The tile order is XCD-aware: consecutive workgroup
-// ids go round-robin over the 8 XCDs, so ids are remapped to give each XCD a
+// bf16 path (K % 64 == 0): BM x BN tiles (128x128, 128x256 or 256x128,
+// picked per GEMM shape), 4 waves in a 2x2 layout, each wave (BM/2) x (BN/2)
+// as blocks of v_mfma_f32_32x32x16_bf16.  Global tiles go straight into LDS
+// (global_load_lds_dwordx4), STAGES k-tiles in flight, one s_barrier per
+// k-tile.  The tile order is XCD-aware: consecutive workgroup ids go
+// round-robin over the 8 XCDs, so ids are remapped to give each XCD a
 // contiguous range of tiles, then grouped 8 row-tiles at a time so tiles that
-// share weight columns run close together in the same L2.
+// share weight columns run close together in the same L2.  A register-staged
+// 128x128 kernel with padded LDS rows covers K % 64 != 0.
 // fp32 path: 64x64x16 LDS tiles on VALU FMAs (correctness path for the small
 // fp32 workloads).
 #include "common.h"
@@ -117,10 +118,9 @@ constexpr bool kForceGeneric = WAMC_GEMM_GENERIC != 0;
 // token), so the per-element work is a table read, the bias and the store.
 // ---------------------------------------------------------------------------
 
-template <int EPI>
+template <int EPI, int BM>
 __device__ __forceinline__ void fill_row_table(const GemmArgs& g, int m0, int* tab) {
-  const int t = threadIdx.x;
-  if (t < kBM) {
+  for (int t = threadIdx.x; t < BM; t += kGemmThreads) {
     const int m = m0 + t;
     const RowInfo ri = row_info(g, m);
     int r0 = -1, r1 = -1;
@@ -132,79 +132,89 @@ __device__ __forceinline__ void fill_row_table(const GemmArgs& g, int m0, int* t
       }
     }
     tab[t] = r0;
-    tab[kBM + t] = r1;
+    tab[BM + t] = r1;
   }
 }
 
-// acc[i][j][v] of wave (wm, wn): row lr = wm*64 + i*32 + (v/4)*8 + half*4 + v%4,
-// column n0 + wn*64 + j*32 + col.
-template <int EPI>
-__device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t (&acc)[2][2], int m0, int n0,
+// The bf16 kernels issue the MFMA with the weight fragment as operand A and
+// the activation fragment as operand B, i.e. they compute C^T blocks.  In the
+// 32x32 output layout that gives lane (half, col) ONE output row per block
+//   lr = wm*(BM/2) + i*32 + col
+// and, for element group g (v = 4g..4g+3), FOUR consecutive output columns
+//   n = n0 + wn*(BN/2) + j*32 + g*8 + half*4 + (0..3),
+// so each lane checks its row once and stores 4 columns with one 8-byte
+// (bf16) or 16-byte (f32) access.
+template <int EPI, int BM, int BN, int TI, int TJ>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t (&acc)[TI][TJ], int m0, int n0,
                                               int wm, int wn, int half, int col, const int* tab) {
-  float bias[2];
-  int ncol[2];
+  const bool full_n = n0 + BN <= g.Nout;   // Nout % 4 == 0: groups never straddle Nout
+  const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    ncol[j] = n0 + wn * 64 + j * 32 + col;
-    bias[j] = ncol[j] < g.Nout ? bf16_to_f32(static_cast<const bf16_t*>(g.bias)[ncol[j]]) : 0.f;
-  }
-  if constexpr (EPI == EPI_QKV) {
-    const int d = g.d_model;
-    bf16_t* dst[2];
-    int cc[2];
-    bool use_tok[2];
+  for (int i = 0; i < TI; ++i) {
+    const int lr = wm * (BM / 2) + i * 32 + col;
+    const int rq = tab[lr];
+    if constexpr (EPI == EPI_QKV) {
+      const int rkv = tab[BM + lr];
+      const int d = g.d_model;
+      // a tile crosses at most one of the Q|K|V boundaries (d >= BN / 2... and
+      // d >= 128 in the bf16 path; BN <= 256 <= 2d)
+      const int which0 = n0 / d, edge = (which0 + 1) * d;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int which = ncol[j] / d;
-      cc[j] = ncol[j] - which * d;
-      use_tok[j] = which != 0;
-      dst[j] = static_cast<bf16_t*>(which == 0 ? g.q_out : (which == 1 ? g.k_cache : g.v_cache));
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int n = n0 + wn * (BN / 2) + j * 32 + gg * 8 + half * 4;
+          if (!full_n && n >= g.Nout) continue;
+          const int which = which0 + (n >= edge ? 1 : 0), c = n - which * d;
+          const int r = which == 0 ? rq : rkv;
+          if (r < 0) continue;
+          const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+          uint2 w;
+          w.x = pack_bf16x2(acc[i][j][4 * gg + 0] + __uint_as_float(bb.x << 16),
+                            acc[i][j][4 * gg + 1] + __uint_as_float(bb.x & 0xffff0000u));
+          w.y = pack_bf16x2(acc[i][j][4 * gg + 2] + __uint_as_float(bb.y << 16),
+                            acc[i][j][4 * gg + 3] + __uint_as_float(bb.y & 0xffff0000u));
+          bf16_t* dst = static_cast<bf16_t*>(which == 0 ? g.q_out : (which == 1 ? g.k_cache : g.v_cache));
+          *reinterpret_cast<uint2*>(dst + static_cast<size_t>(r) * d + c) = w;
+        }
+    } else if constexpr (EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN) {
+      if (rq < 0) continue;
+      const bf16_t* gate = static_cast<const bf16_t*>(g.gate);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int n = n0 + wn * (BN / 2) + j * 32 + gg * 8 + half * 4;
+          if (!full_n && n >= g.Nout) continue;
+          const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+          const uint2 gt = *reinterpret_cast<const uint2*>(gate + n);
+          const size_t o = static_cast<size_t>(rq) * g.Nout + n;
+          const float4 xin = *reinterpret_cast<const float4*>(g.resid_in + o);
+          float4 xo;
+          xo.x = fmaf(__uint_as_float(gt.x << 16), acc[i][j][4 * gg + 0] + __uint_as_float(bb.x << 16), xin.x);
+          xo.y = fmaf(__uint_as_float(gt.x & 0xffff0000u), acc[i][j][4 * gg + 1] + __uint_as_float(bb.x & 0xffff0000u), xin.y);
+          xo.z = fmaf(__uint_as_float(gt.y << 16), acc[i][j][4 * gg + 2] + __uint_as_float(bb.y << 16), xin.z);
+          xo.w = fmaf(__uint_as_float(gt.y & 0xffff0000u), acc[i][j][4 * gg + 3] + __uint_as_float(bb.y & 0xffff0000u), xin.w);
+          *reinterpret_cast<float4*>(g.resid_out + o) = xo;
+        }
+    } else {
+      if (rq < 0) continue;
+      bf16_t* out = static_cast<bf16_t*>(g.g_out);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int n = n0 + wn * (BN / 2) + j * 32 + gg * 8 + half * 4;
+          if (!full_n && n >= g.Nout) continue;
+          const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+          uint2 w;
+          w.x = pack_bf16x2(gelu_erf_fast(acc[i][j][4 * gg + 0] + __uint_as_float(bb.x << 16)),
+                            gelu_erf_fast(acc[i][j][4 * gg + 1] + __uint_as_float(bb.x & 0xffff0000u)));
+          w.y = pack_bf16x2(gelu_erf_fast(acc[i][j][4 * gg + 2] + __uint_as_float(bb.y << 16)),
+                            gelu_erf_fast(acc[i][j][4 * gg + 3] + __uint_as_float(bb.y & 0xffff0000u)));
+          *reinterpret_cast<uint2*>(out + static_cast<size_t>(rq) * g.Nout + n) = w;
+        }
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int lr = wm * 64 + i * 32 + (v / 4) * 8 + half * 4 + (v % 4);
-        const int rq = tab[lr], rkv = tab[kBM + lr];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int r = use_tok[j] ? rkv : rq;
-          if (r >= 0 && ncol[j] < g.Nout)
-            dst[j][static_cast<size_t>(r) * d + cc[j]] = f32_to_bf16(acc[i][j][v] + bias[j]);
-        }
-      }
-  } else if constexpr (EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN) {
-    float gate[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      gate[j] = ncol[j] < g.Nout ? bf16_to_f32(static_cast<const bf16_t*>(g.gate)[ncol[j]]) : 0.f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int lr = wm * 64 + i * 32 + (v / 4) * 8 + half * 4 + (v % 4);
-        const int r = tab[lr];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (r >= 0 && ncol[j] < g.Nout) {
-            const size_t o = static_cast<size_t>(r) * g.Nout + ncol[j];
-            g.resid_out[o] = g.resid_in[o] + gate[j] * (acc[i][j][v] + bias[j]);
-          }
-        }
-      }
-  } else {
-    bf16_t* out = static_cast<bf16_t*>(g.g_out);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int lr = wm * 64 + i * 32 + (v / 4) * 8 + half * 4 + (v % 4);
-        const int r = tab[lr];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          if (r >= 0 && ncol[j] < g.Nout)
-            out[static_cast<size_t>(r) * g.Nout + ncol[j]] = f32_to_bf16(gelu_erf_fast(acc[i][j][v] + bias[j]));
-      }
   }
 }
 
@@ -278,21 +288,19 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) 
     for (int s = 0; s < kBK / 16; ++s) {
       const bf16x8_t a0 = frag(as + s * 16), a1 = frag(as + 32 * kLdsK + s * 16);
       const bf16x8_t b0 = frag(ws + s * 16), b1 = frag(ws + 32 * kLdsK + s * 16);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, a0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, a0, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, a1, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, a1, acc[1][1], 0, 0, 0);
     }
     if (kt + 1 < nk) store_tile(cur ^ 1);
     __syncthreads();
   }
 
-  // C layout of a 32x32 block: lane (half, col), element v ->
-  // row (v/4)*8 + half*4 + v%4, column col.
   int* tab = reinterpret_cast<int*>(&As[0][0]);   // the last k-tile ended with a barrier
-  fill_row_table<EPI>(g, m0, tab);
+  fill_row_table<EPI, kBM>(g, m0, tab);
   __syncthreads();
-  tile_epilogue<EPI>(g, acc, m0, n0, wm, wn, half, col, tab);
+  tile_epilogue<EPI, kBM, kBN, 2, 2>(g, acc, m0, n0, wm, wn, half, col, tab);
 }
 
 // ---------------------------------------------------------------------------
@@ -332,20 +340,23 @@ __device__ __forceinline__ int swz(int row, int kc) {
   return row * CPR + swz_kc<CPR>(row, kc);
 }
 
-template <int EPI, int BK, int STAGES>
-__global__ __launch_bounds__(kGemmThreads, (STAGES * 256 * BK * 2 <= 80 * 1024) ? 2 : 1)
+template <int EPI, int BM, int BN, int BK, int STAGES>
+__global__ __launch_bounds__(kGemmThreads, (STAGES * (BM + BN) * BK * 2 <= 80 * 1024) ? 2 : 1)
 void gemm_bf16_dtl_kernel(GemmArgs g) {
-  constexpr int CPR = BK / 8;                       // 16-byte chunks per tile row
-  constexpr int CHUNKS = kBM * CPR;                 // per operand per stage
-  constexpr int LOADS = 2 * CHUNKS / kGemmThreads;  // direct-to-LDS loads per thread per k-tile
-  constexpr int LOADS_A = LOADS / 2;
-  const int tiles_m = (g.M + kBM - 1) / kBM, tiles_n = (g.Nout + kBN - 1) / kBN;
+  constexpr int CPR = BK / 8;                          // 16-byte chunks per tile row
+  constexpr int CHUNKS_A = BM * CPR, CHUNKS_B = BN * CPR;
+  constexpr int LOADS_A = CHUNKS_A / kGemmThreads;     // direct-to-LDS loads per thread per k-tile
+  constexpr int LOADS_B = CHUNKS_B / kGemmThreads;
+  constexpr int LOADS = LOADS_A + LOADS_B;
+  constexpr int TI = BM / 64, TJ = BN / 64;            // 32x32 blocks per wave
+  static_assert(LOADS_A * kGemmThreads == CHUNKS_A && LOADS_B * kGemmThreads == CHUNKS_B, "tile/threads");
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.Nout + BN - 1) / BN;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * kBM, n0 = tn * kBN;
-  if (tile_empty(g, m0, kBM)) return;
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (tile_empty(g, m0, BM)) return;
 
-  __shared__ uint4 lds[STAGES][2][CHUNKS];
+  __shared__ uint4 lds[STAGES][CHUNKS_A + CHUNKS_B];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
@@ -354,13 +365,14 @@ void gemm_bf16_dtl_kernel(GemmArgs g) {
   const bf16_t* W = static_cast<const bf16_t*>(g.w);
   const int K = g.K;
 
-  // load i of this thread fills LDS chunk c = ((i % LOADS_A)*4 + wid)*64 + lane
-  // of operand i / LOADS_A; it fetches the element chunk that the swizzle
-  // maps there
+  // load i of this thread fills LDS chunk c = (il*4 + wid)*64 + lane of its
+  // operand (il = i for A, i - LOADS_A for W); it fetches the element chunk
+  // that the swizzle maps there
   int goff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int c = ((i % LOADS_A) * 4 + wid) * 64 + lane;
+    const int il = i < LOADS_A ? i : i - LOADS_A;
+    const int c = (il * 4 + wid) * 64 + lane;
     const int row = c / CPR;
     const int kc = swz_kc<CPR>(row, c % CPR);   // the XOR key is its own inverse
     if (i < LOADS_A) goff[i] = min(m0 + row, g.M - 1) * K + kc * 8;
@@ -370,19 +382,20 @@ void gemm_bf16_dtl_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const bf16_t* src = (i < LOADS_A ? A : W) + goff[i] + kt * BK;
-      uint4* dst = &lds[stage][i / LOADS_A][((i % LOADS_A) * 4 + wid) * 64];
+      const int il = i < LOADS_A ? i : i - LOADS_A;
+      uint4* dst = &lds[stage][(i < LOADS_A ? 0 : CHUNKS_A) + (il * 4 + wid) * 64];
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
     }
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
 
-  const int ra0 = wm * 64 + col, ra1 = ra0 + 32;
-  const int rb0 = wn * 64 + col, rb1 = rb0 + 32;
+  const int ra = wm * (BM / 2) + col;
+  const int rb = wn * (BN / 2) + col;
 
   const int nk = K / BK;
 #pragma unroll
@@ -406,27 +419,29 @@ void gemm_bf16_dtl_kernel(GemmArgs g) {
     // __syncthreads() that would also drain the loads still in flight
     __builtin_amdgcn_s_barrier();
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-    const uint4* as = lds[kt % STAGES][0];
-    const uint4* ws = lds[kt % STAGES][1];
+    const uint4* as = lds[kt % STAGES];
+    const uint4* ws = as + CHUNKS_A;
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       const int kc = 2 * s + half;
-      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, as[swz<CPR>(ra0, kc)]);
-      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, as[swz<CPR>(ra1, kc)]);
-      const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, ws[swz<CPR>(rb0, kc)]);
-      const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, ws[swz<CPR>(rb1, kc)]);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+      bf16x8_t af[TI], bfr[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) af[i] = __builtin_bit_cast(bf16x8_t, as[swz<CPR>(ra + 32 * i, kc)]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) bfr[j] = __builtin_bit_cast(bf16x8_t, ws[swz<CPR>(rb + 32 * j, kc)]);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
   }
 
   __syncthreads();   // every wave is done with the LDS stages
-  int* tab = reinterpret_cast<int*>(&lds[0][0][0]);
-  fill_row_table<EPI>(g, m0, tab);
+  int* tab = reinterpret_cast<int*>(&lds[0][0]);
+  fill_row_table<EPI, BM>(g, m0, tab);
   __syncthreads();
-  tile_epilogue<EPI>(g, acc, m0, n0, wm, wn, half, col, tab);
+  tile_epilogue<EPI, BM, BN, TI, TJ>(g, acc, m0, n0, wm, wn, half, col, tab);
 }
 
 // ---------------------------------------------------------------------------
@@ -487,16 +502,40 @@ static const char* gemm_name(const GemmArgs& g, GemmEpi e) {
   return e == EPI_RESID_OUT ? "gemm_out_resid" : "gemm_down_resid";
 }
 
+template <int BM, int BN, int BK, int STAGES>
+static void launch_dtl(GemmEpi epi, const GemmArgs& g, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>(((g.M + BM - 1) / BM) * ((g.Nout + BN - 1) / BN));
+  switch (epi) {
+    case EPI_QKV: gemm_bf16_dtl_kernel<EPI_QKV, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
+    case EPI_RESID_OUT: gemm_bf16_dtl_kernel<EPI_RESID_OUT, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
+    case EPI_RESID_DOWN: gemm_bf16_dtl_kernel<EPI_RESID_DOWN, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
+    case EPI_GELU: gemm_bf16_dtl_kernel<EPI_GELU, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
+  }
+}
+
+#ifndef WAMC_GEMM_TILE
+#define WAMC_GEMM_TILE 0
+#endif
+
+// Tile shape per GEMM.  128x256 / 256x128 tiles stage a third fewer bytes per
+// FLOP through LDS, but measured on the d=1536 shapes (M ~ 2.5k) every GEMM
+// ran faster on 128x128 tiles, so that is the default; the others stay
+// selectable for larger workloads.
+static int pick_tile(const GemmArgs& g) {
+  (void)g;
+  return WAMC_GEMM_TILE != 0 ? WAMC_GEMM_TILE : 1;
+}
+
 hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer) {
   if (g.M <= 0 || g.Nout <= 0) return hipSuccess;
   TimedLaunch t(timer, gemm_name(g, epi), s);
   if (bf16 && g.K % 64 == 0 && !kForceGeneric) {
-    const unsigned grid = static_cast<unsigned>(((g.M + kBM - 1) / kBM) * ((g.Nout + kBN - 1) / kBN));
-    switch (epi) {
-      case EPI_QKV: gemm_bf16_dtl_kernel<EPI_QKV, kDtlBK, kGemmStages><<<grid, kGemmThreads, 0, s>>>(g); break;
-      case EPI_RESID_OUT: gemm_bf16_dtl_kernel<EPI_RESID_OUT, kDtlBK, kGemmStages><<<grid, kGemmThreads, 0, s>>>(g); break;
-      case EPI_RESID_DOWN: gemm_bf16_dtl_kernel<EPI_RESID_DOWN, kDtlBK, kGemmStages><<<grid, kGemmThreads, 0, s>>>(g); break;
-      case EPI_GELU: gemm_bf16_dtl_kernel<EPI_GELU, kDtlBK, kGemmStages><<<grid, kGemmThreads, 0, s>>>(g); break;
+    switch (pick_tile(g)) {
+      case 2: launch_dtl<128, 256, 32, 3>(epi, g, s); break;
+      case 3: launch_dtl<256, 128, 32, 3>(epi, g, s); break;
+      case 4: launch_dtl<128, 256, 64, 2>(epi, g, s); break;
+      case 5: launch_dtl<256, 128, 64, 2>(epi, g, s); break;
+      default: launch_dtl<128, 128, kDtlBK, kGemmStages>(epi, g, s); break;
     }
   } else if (bf16) {
     const unsigned grid = static_cast<unsigned>(((g.M + kBM - 1) / kBM) * ((g.Nout + kBN - 1) / kBN));
