@@ -67,6 +67,7 @@ def kernel_work(wl, k_eff_total: int):
         "score_pass1": ("byte", float(L * B * N * d * es + L * B * A * d * es)),
         "score_pass2": ("byte", float(L * B * N * d * es + L * B * A * d * es + L * H * B * N * 4)),
         "gather": ("byte", float(M * d * (es + 4 + es))),
+        "gather_ln": ("byte", float(M * d * (es + 4 + es + es))),
         "ln_mod": ("byte", float(M * d * (4 + es))),
         "select": ("byte", float(B * N * (4 + 4 + 4 + 4))),
     }
@@ -80,7 +81,7 @@ def source_hash(name: str) -> str:
 
 KERNEL_SOURCE = {"gemm_qkv": "gemm.hip", "gemm_out_resid": "gemm.hip", "gemm_up_gelu": "gemm.hip",
                  "gemm_down_resid": "gemm.hip", "attention": "attention.hip", "score_pass1": "score.hip",
-                 "score_pass2": "score.hip", "select": "select.hip", "gather": "rows.hip", "ln_mod": "rows.hip"}
+                 "score_pass2": "score.hip", "select": "select.hip", "gather": "rows.hip", "gather_ln": "rows.hip", "ln_mod": "rows.hip"}
 
 
 def measured_traffic(kind: str, config: str):

@@ -286,7 +286,7 @@ int check_layer_w(const char* fn, const wamc_layer_w* w) {
 // x_out (may alias x_in).
 hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_in, float* x_out,
                      const int32_t* idx, const int32_t* k_eff, int32_t rows_cap, void* kc, void* vc,
-                     void* ws, const WsLayout& L, hipStream_t s) {
+                     void* ws, const WsLayout& L, hipStream_t s, bool h1_ready = false) {
   const bool bf16 = d->dtype == WAMC_BF16;
   const size_t es = act_size(d);
   const int D = d->d_model, F = d->d_ffn, B = d->batch;
@@ -303,8 +303,10 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
   const int M = B * rows_cap;
   hipError_t e;
 
-  e = launch_ln_mod(bf16, x_in, shift1, scale1, B, rows_cap, k_eff, D, d->ln_eps, hbuf, s, tm);
-  if (e != hipSuccess) return e;
+  if (!h1_ready) {
+    e = launch_ln_mod(bf16, x_in, shift1, scale1, B, rows_cap, k_eff, D, d->ln_eps, hbuf, s, tm);
+    if (e != hipSuccess) return e;
+  }
 
   GemmArgs g{};
   g.rows_cap = rows_cap;
@@ -343,9 +345,10 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
   return launch_gemm(bf16, EPI_RESID_DOWN, g, s, tm);
 }
 
-hipError_t run_score(const wamc_dims* d, const void* z, const void* zref, const void* q_act,
-                     const void* k_cache, const float* mass_in, float* score, float* mass_out,
-                     float* surprise_out, void* ws, const WsLayout& L, hipStream_t s) {
+// Attention mass (unless supplied) and the per-token P, U partials.
+hipError_t run_score_partials(const wamc_dims* d, const void* z, const void* zref, const void* q_act,
+                              const void* k_cache, const float* mass_in, void* ws, const WsLayout& L,
+                              hipStream_t s) {
   const bool bf16 = d->dtype == WAMC_BF16;
   KernelTimer* tm = active_timer();
   const int LH = d->n_layers * d->n_heads;
@@ -355,10 +358,22 @@ hipError_t run_score(const wamc_dims* d, const void* z, const void* zref, const 
                                      d->n_action, d->d_model, L.sp, at<float2>(ws, L.ms), part, s, tm);
     if (e != hipSuccess) return e;
   }
-  const float w_norm = d->w_attn / (static_cast<float>(LH) * static_cast<float>(d->n_action));
-  return launch_score_combine(bf16, part, LH, mass_in, z, zref, d->batch, d->n_tokens, d->d_model, w_norm,
-                              d->w_surprise, L.sp, at<float>(ws, L.mass_tmp), at<float>(ws, L.surp_tmp),
-                              at<float>(ws, L.usum), score, mass_out, surprise_out, s, tm);
+  return launch_score_partials(bf16, part, LH, mass_in, z, zref, d->batch, d->n_tokens, d->d_model, L.sp,
+                               at<float>(ws, L.mass_tmp), at<float>(ws, L.surp_tmp), at<float>(ws, L.usum), s, tm);
+}
+
+float attn_weight_norm(const wamc_dims* d) {
+  return d->w_attn / (static_cast<float>(d->n_layers * d->n_heads) * static_cast<float>(d->n_action));
+}
+
+hipError_t run_score(const wamc_dims* d, const void* z, const void* zref, const void* q_act,
+                     const void* k_cache, const float* mass_in, float* score, float* mass_out,
+                     float* surprise_out, void* ws, const WsLayout& L, hipStream_t s) {
+  hipError_t e = run_score_partials(d, z, zref, q_act, k_cache, mass_in, ws, L, s);
+  if (e != hipSuccess) return e;
+  return launch_score_finish(at<float>(ws, L.mass_tmp), at<float>(ws, L.surp_tmp), at<float>(ws, L.usum), d->batch,
+                             d->n_tokens, attn_weight_norm(d), d->w_surprise, L.sp, score, mass_out, surprise_out, s,
+                             active_timer());
 }
 
 }  // namespace
@@ -537,17 +552,30 @@ int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const 
     TimedLaunch t(tm, "ages_from_set", s);
     e = launch_ages_from_set(idx_override, k_eff_override, B, N, rows_cap, idx_out, k_eff_out, age, s);
   } else {
-    float* sc = score_out ? score_out : at<float>(ws, L.score_tmp);
-    e = run_score(dims, z, zref, q_act, k_cache, mass_in, sc, nullptr, nullptr, ws, L, s);
+    // scoring's last step (sum of U, the weighted sum) runs inside the selection kernel
+    e = run_score_partials(dims, z, zref, q_act, k_cache, mass_in, ws, L, s);
     if (e == hipSuccess) {
+      ScoreInputs si;
+      si.mass = at<float>(ws, L.mass_tmp);
+      si.surprise = at<float>(ws, L.surp_tmp);
+      si.usum = at<float>(ws, L.usum);
+      si.nblocks = L.sp.comb_blocks;
+      si.w_attn_norm = attn_weight_norm(dims);
+      si.w_surprise = dims->w_surprise;
+      si.score_out = score_out ? score_out : at<float>(ws, L.score_tmp);
       TimedLaunch t(tm, "select", s);
-      e = launch_select(sc, age, B, N, k, dims->age_bound, rows_cap, idx_out, k_eff_out, nullptr, s);
+      e = launch_select_scored(si, age, B, N, k, dims->age_bound, rows_cap, idx_out, k_eff_out, nullptr, s);
     }
   }
   if (e != hipSuccess) return hip_status(fn, e, s);
   float* x = at<float>(ws, L.x);
-  e = launch_gather(bf16, z, zref, idx_out, k_eff_out, B, N, D, rows_cap, x, nullptr, s, tm);
   const size_t es = act_size(dims);
+  const bool fuse_ln = D <= 4096;
+  if (fuse_ln)
+    e = launch_gather_ln(bf16, z, zref, idx_out, k_eff_out, B, N, D, rows_cap, x, nullptr, offset(layers[0].mod, 0, es),
+                         offset(layers[0].mod, D, es), dims->ln_eps, at<char>(ws, L.hbuf), s, tm);
+  else
+    e = launch_gather(bf16, z, zref, idx_out, k_eff_out, B, N, D, rows_cap, x, nullptr, s, tm);
   const size_t layer_elems = static_cast<size_t>(B) * N * D;
   const size_t out_elems = static_cast<size_t>(B) * rows_cap * D;
   for (int l = 0; l < dims->n_layers && e == hipSuccess; ++l) {
@@ -555,7 +583,7 @@ int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const 
     float* xout = layer_out ? layer_out + l * out_elems : x;
     void* kc = static_cast<char*>(k_cache) + l * layer_elems * es;
     void* vc = static_cast<char*>(v_cache) + l * layer_elems * es;
-    e = run_layer(dims, &layers[l], xin, xout, idx_out, k_eff_out, rows_cap, kc, vc, ws, L, s);
+    e = run_layer(dims, &layers[l], xin, xout, idx_out, k_eff_out, rows_cap, kc, vc, ws, L, s, l == 0 && fuse_ln);
   }
   return hip_status(fn, e, s);
 }
@@ -587,15 +615,21 @@ int wamc_dense_prefill(const wamc_dims* dims, const wamc_layer_w* layers, const 
   const bool bf16 = dims->dtype == WAMC_BF16;
   const int B = dims->batch, D = dims->d_model;
   float* x = at<float>(ws, L.x);
-  hipError_t e = launch_gather(bf16, z, zref, nullptr, nullptr, B, N, D, N, x, age, s, tm);
   const size_t es = act_size(dims);
+  const bool fuse_ln = D <= 4096;
+  hipError_t e;
+  if (fuse_ln)
+    e = launch_gather_ln(bf16, z, zref, nullptr, nullptr, B, N, D, N, x, age, offset(layers[0].mod, 0, es),
+                         offset(layers[0].mod, D, es), dims->ln_eps, at<char>(ws, L.hbuf), s, tm);
+  else
+    e = launch_gather(bf16, z, zref, nullptr, nullptr, B, N, D, N, x, age, s, tm);
   const size_t layer_elems = static_cast<size_t>(B) * N * D;
   for (int l = 0; l < dims->n_layers && e == hipSuccess; ++l) {
     const float* xin = (layer_out && l > 0) ? layer_out + (l - 1) * layer_elems : x;
     float* xout = layer_out ? layer_out + l * layer_elems : x;
     void* kc = static_cast<char*>(k_cache) + l * layer_elems * es;
     void* vc = static_cast<char*>(v_cache) + l * layer_elems * es;
-    e = run_layer(dims, &layers[l], xin, xout, nullptr, nullptr, N, kc, vc, ws, L, s);
+    e = run_layer(dims, &layers[l], xin, xout, nullptr, nullptr, N, kc, vc, ws, L, s, l == 0 && fuse_ln);
   }
   return hip_status(fn, e, s);
 }

@@ -63,6 +63,26 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Sum over the per-block surprise partials of one episode, by threads
+// 0..255 of the calling block in a fixed order (so every kernel that needs
+// sum_j U_j gets the same bits).  All threads of the block must call it.
+__device__ __forceinline__ float usum_total(const float* __restrict__ usum_blocks, int nblocks, float* red4) {
+  float acc = 0.f;
+  if (threadIdx.x < 256)
+    for (int i = threadIdx.x; i < nblocks; i += 256) acc += usum_blocks[i];
+  acc = wave_sum(acc);
+  if (threadIdx.x < 256 && (threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  return ((red4[0] + red4[1]) + red4[2]) + red4[3];
+}
+
+// score = w_a P / (L H A) + w_s U / sum(U)   (w_attn_norm = w_a / (L H A))
+__device__ __forceinline__ float combine_score(float p, float u, float total, float w_attn_norm, float w_surprise) {
+  float s = w_attn_norm * p;
+  if (total > 0.f) s += w_surprise * (u / total);
+  return s;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8), each XCD
 // with its own L2.  Remap a linear id so that XCD x receives the contiguous
 // range [x*per, (x+1)*per) of work items (a bijection on [0, total)): work

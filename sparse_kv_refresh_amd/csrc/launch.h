@@ -30,6 +30,19 @@ struct TimedLaunch {
 // ----- selection (select.hip) -----
 hipError_t launch_select(const float* score, int32_t* age, int B, int N, int k, int G, int rows_cap,
                          int32_t* idx, int32_t* k_eff, int32_t* n_forced, hipStream_t s);
+// Selection fused with the last scoring step: the scores are formed from the
+// per-token P, U and the per-block U partials (nblocks per episode), written
+// to score_out, and selected on in the same kernel.
+struct ScoreInputs {
+  const float* mass;
+  const float* surprise;
+  const float* usum;
+  int nblocks;
+  float w_attn_norm, w_surprise;
+  float* score_out;
+};
+hipError_t launch_select_scored(const ScoreInputs& si, int32_t* age, int B, int N, int k, int G, int rows_cap,
+                                int32_t* idx, int32_t* k_eff, int32_t* n_forced, hipStream_t s);
 hipError_t launch_ages_from_set(const int32_t* idx_in, const int32_t* k_in, int B, int N, int rows_cap,
                                 int32_t* idx_out, int32_t* k_out, int32_t* age, hipStream_t s);
 
@@ -42,11 +55,14 @@ ScorePlan plan_score(int B, int L, int H, int N, int A, bool bf16);
 hipError_t launch_score_mass(bool bf16, const void* qa, const void* kc, int B, int L, int H, int N,
                              int A, int d, const ScorePlan& p, float2* ms, float* part,
                              hipStream_t s, KernelTimer* timer);
-hipError_t launch_score_combine(bool bf16, const float* part, int LH, const float* mass_in,
-                                const void* z, const void* zref, int B, int N, int d, float w_attn_norm,
-                                float w_surprise, const ScorePlan& p, float* mass_tmp, float* surprise_tmp,
-                                float* usum, float* score, float* mass_out, float* surprise_out,
-                                hipStream_t s, KernelTimer* timer);
+// per-token P (sum over L*H) and U, and per-block partial sums of U
+hipError_t launch_score_partials(bool bf16, const float* part, int LH, const float* mass_in, const void* z,
+                                 const void* zref, int B, int N, int d, const ScorePlan& p, float* mass_tmp,
+                                 float* surprise_tmp, float* usum, hipStream_t s, KernelTimer* timer);
+// score = w_a P/(LHA) + w_s U / sum(U)
+hipError_t launch_score_finish(const float* mass_tmp, const float* surprise_tmp, const float* usum, int B, int N,
+                               float w_attn_norm, float w_surprise, const ScorePlan& p, float* score,
+                               float* mass_out, float* surprise_out, hipStream_t s, KernelTimer* timer);
 
 // ----- row kernels (rows.hip) -----
 // x[b*rows_cap + r] = float(z[b, idx[b,r]]), zref[b, idx] = z[b, idx]
@@ -54,6 +70,11 @@ hipError_t launch_score_combine(bool bf16, const float* part, int LH, const floa
 hipError_t launch_gather(bool bf16, const void* z, void* zref, const int32_t* idx, const int32_t* k_eff,
                          int B, int N, int d, int rows_cap, float* x, int32_t* age_zero, hipStream_t s,
                          KernelTimer* timer);
+// gather fused with the first modulated LayerNorm (d <= 4096): also writes
+// h = act(LN(x) * (1 + scale) + shift)
+hipError_t launch_gather_ln(bool bf16, const void* z, void* zref, const int32_t* idx, const int32_t* k_eff, int B,
+                            int N, int d, int rows_cap, float* x, int32_t* age_zero, const void* shift,
+                            const void* scale, float eps, void* h, hipStream_t s, KernelTimer* timer);
 // h[m] = act(LN(x_in[m]) * (1 + scale) + shift) for valid rows.
 hipError_t launch_ln_mod(bool bf16, const float* x, const void* shift, const void* scale, int B,
                          int rows_cap, const int32_t* k_eff, int d, float eps, void* h, hipStream_t s,

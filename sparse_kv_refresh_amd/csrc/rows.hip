@@ -68,6 +68,94 @@ hipError_t launch_gather(bool bf16, const void* z, void* zref, const int32_t* id
   return hipGetLastError();
 }
 
+// Gather fused with the first modulated LayerNorm of layer 0: the row is
+// held in registers, x and zref are written, and h = LN(x)(1+scale)+shift is
+// produced in the same pass.  Each lane owns elements lane*4 + 256*j + 0..3,
+// the assignment (and so the summation order) of the stand-alone LayerNorm
+// kernel below, so both give the same bits.
+constexpr int kMaxRowChunks = 16;   // d <= 4096
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void gather_ln_kernel(
+    const T* __restrict__ z, T* __restrict__ zref, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ k_eff, int N, int d, int rows_cap, float* __restrict__ x,
+    int32_t* __restrict__ age_zero, const T* __restrict__ shift, const T* __restrict__ scale, float eps,
+    T* __restrict__ h) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int r = blockIdx.x * (kRowThreads / kWave) + wid;
+  if (r >= rows_of(k_eff, b, rows_cap)) return;
+  const int t = idx ? idx[static_cast<size_t>(b) * N + r] : r;
+  if (t < 0 || t >= N) return;
+  const size_t src = (static_cast<size_t>(b) * N + t) * d;
+  const size_t row = static_cast<size_t>(b) * rows_cap + r;
+  float* xr = x + row * d;
+  T* hr = h + row * d;
+  float v[kMaxRowChunks][4];
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxRowChunks; ++j) {
+    const int c = lane * 4 + j * 256;
+    if (c < d) {
+      if constexpr (sizeof(T) == 2) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(z + src + c);
+        v[j][0] = __uint_as_float(raw.x << 16);
+        v[j][1] = __uint_as_float(raw.x & 0xffff0000u);
+        v[j][2] = __uint_as_float(raw.y << 16);
+        v[j][3] = __uint_as_float(raw.y & 0xffff0000u);
+        *reinterpret_cast<uint2*>(zref + src + c) = raw;
+      } else {
+        const float4 f = *reinterpret_cast<const float4*>(z + src + c);
+        v[j][0] = f.x; v[j][1] = f.y; v[j][2] = f.z; v[j][3] = f.w;
+        *reinterpret_cast<float4*>(zref + src + c) = f;
+      }
+      *reinterpret_cast<float4*>(xr + c) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+      sum += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
+    }
+  }
+  if (age_zero && lane == 0) age_zero[static_cast<size_t>(b) * N + t] = 0;
+  const float mean = wave_sum(sum) / static_cast<float>(d);
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxRowChunks; ++j) {
+    if (lane * 4 + j * 256 < d) {
+      const float a0 = v[j][0] - mean, a1 = v[j][1] - mean, a2 = v[j][2] - mean, a3 = v[j][3] - mean;
+      q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+    }
+  }
+  const float var = wave_sum(q) / static_cast<float>(d);
+  const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int j = 0; j < kMaxRowChunks; ++j) {
+    const int c = lane * 4 + j * 256;
+    if (c < d) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float n = (v[j][i] - mean) * rstd;
+        const float y = n * (1.0f + Elem<T>::load(scale, c + i)) + Elem<T>::load(shift, c + i);
+        Elem<T>::store(hr, c + i, y);
+      }
+    }
+  }
+}
+
+hipError_t launch_gather_ln(bool bf16, const void* z, void* zref, const int32_t* idx, const int32_t* k_eff, int B,
+                            int N, int d, int rows_cap, float* x, int32_t* age_zero, const void* shift,
+                            const void* scale, float eps, void* h, hipStream_t s, KernelTimer* timer) {
+  if (d > kMaxRowChunks * 256) return hipErrorInvalidValue;
+  TimedLaunch t(timer, "gather_ln", s);
+  const dim3 grid((rows_cap + 3) / 4, B);
+  if (bf16)
+    gather_ln_kernel<bf16_t><<<grid, kRowThreads, 0, s>>>(static_cast<const bf16_t*>(z), static_cast<bf16_t*>(zref),
+        idx, k_eff, N, d, rows_cap, x, age_zero, static_cast<const bf16_t*>(shift),
+        static_cast<const bf16_t*>(scale), eps, static_cast<bf16_t*>(h));
+  else
+    gather_ln_kernel<float><<<grid, kRowThreads, 0, s>>>(static_cast<const float*>(z), static_cast<float*>(zref),
+        idx, k_eff, N, d, rows_cap, x, age_zero, static_cast<const float*>(shift),
+        static_cast<const float*>(scale), eps, static_cast<float*>(h));
+  return hipGetLastError();
+}
+
 // LayerNorm without affine (biased variance), then *(1 + scale) + shift,
 // rounded to the activation type.
 template <typename T>

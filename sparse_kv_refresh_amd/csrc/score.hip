@@ -353,19 +353,12 @@ __global__ __launch_bounds__(256) void score_combine2(
     float* __restrict__ score, float* __restrict__ mass_out, float* __restrict__ surprise_out) {
   const int b = blockIdx.y;
   __shared__ float red[4];
-  float acc = 0.f;
-  for (int i = threadIdx.x; i < nblocks; i += blockDim.x) acc += usum_blocks[static_cast<size_t>(b) * nblocks + i];
-  acc = wave_sum(acc);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  const float total = ((red[0] + red[1]) + red[2]) + red[3];
+  const float total = usum_total(usum_blocks + static_cast<size_t>(b) * nblocks, nblocks, red);
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N) return;
   const size_t o = static_cast<size_t>(b) * N + i;
   const float p = mass[o], u = surprise[o];
-  float s = w_attn_norm * p;
-  if (total > 0.f) s += w_surprise * (u / total);
-  score[o] = s;
+  score[o] = combine_score(p, u, total, w_attn_norm, w_surprise);
   if (mass_out) mass_out[o] = p;
   if (surprise_out) surprise_out[o] = u;
 }
@@ -425,21 +418,23 @@ hipError_t launch_score_mass(bool bf16, const void* qa, const void* kc, int B, i
   return hipGetLastError();
 }
 
-hipError_t launch_score_combine(bool bf16, const float* part, int LH, const float* mass_in,
-                                const void* z, const void* zref, int B, int N, int d, float w_attn_norm,
-                                float w_surprise, const ScorePlan& p, float* mass_tmp, float* surprise_tmp,
-                                float* usum, float* score, float* mass_out, float* surprise_out,
-                                hipStream_t s, KernelTimer* timer) {
-  {
-    TimedLaunch t(timer, "score_combine", s);
-    const dim3 grid(p.comb_blocks, B);
-    if (bf16)
-      score_combine1<bf16_t><<<grid, kCombThreads, 0, s>>>(part, LH, mass_in, static_cast<const bf16_t*>(z),
-          static_cast<const bf16_t*>(zref), N, d, mass_tmp, surprise_tmp, usum);
-    else
-      score_combine1<float><<<grid, kCombThreads, 0, s>>>(part, LH, mass_in, static_cast<const float*>(z),
-          static_cast<const float*>(zref), N, d, mass_tmp, surprise_tmp, usum);
-  }
+hipError_t launch_score_partials(bool bf16, const float* part, int LH, const float* mass_in, const void* z,
+                                 const void* zref, int B, int N, int d, const ScorePlan& p, float* mass_tmp,
+                                 float* surprise_tmp, float* usum, hipStream_t s, KernelTimer* timer) {
+  TimedLaunch t(timer, "score_combine", s);
+  const dim3 grid(p.comb_blocks, B);
+  if (bf16)
+    score_combine1<bf16_t><<<grid, kCombThreads, 0, s>>>(part, LH, mass_in, static_cast<const bf16_t*>(z),
+        static_cast<const bf16_t*>(zref), N, d, mass_tmp, surprise_tmp, usum);
+  else
+    score_combine1<float><<<grid, kCombThreads, 0, s>>>(part, LH, mass_in, static_cast<const float*>(z),
+        static_cast<const float*>(zref), N, d, mass_tmp, surprise_tmp, usum);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_finish(const float* mass_tmp, const float* surprise_tmp, const float* usum, int B, int N,
+                               float w_attn_norm, float w_surprise, const ScorePlan& p, float* score,
+                               float* mass_out, float* surprise_out, hipStream_t s, KernelTimer* timer) {
   TimedLaunch t(timer, "score_combine", s);
   score_combine2<<<dim3((N + 255) / 256, B), 256, 0, s>>>(mass_tmp, surprise_tmp, usum, p.comb_blocks, N,
       w_attn_norm, w_surprise, score, mass_out, surprise_out);

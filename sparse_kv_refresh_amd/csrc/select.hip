@@ -41,19 +41,32 @@ constexpr int kSelWaves = kSelThreads / kWave;
 
 // KPT = keys held per thread in registers (N <= KPT * 1024); 0 = recompute
 // the keys from global memory in every pass (any N).
-template <int KPT>
+// SCORED: the scores are formed here from P, U and the U partials (the last
+// scoring step fused in) and written to si.score_out; otherwise read.
+template <int KPT, bool SCORED>
 __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
-    const float* __restrict__ score, int32_t* __restrict__ age, int N, int k, int G, int rows_cap,
-    int32_t* __restrict__ idx, int32_t* __restrict__ k_eff_out, int32_t* __restrict__ n_forced_out) {
+    const float* __restrict__ score, ScoreInputs si, int32_t* __restrict__ age, int N, int k, int G,
+    int rows_cap, int32_t* __restrict__ idx, int32_t* __restrict__ k_eff_out,
+    int32_t* __restrict__ n_forced_out) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  score += static_cast<size_t>(b) * N;
-  age += static_cast<size_t>(b) * N;
-  idx += static_cast<size_t>(b) * N;
+  const size_t eoff = static_cast<size_t>(b) * N;
+  age += eoff;
+  idx += eoff;
 
   __shared__ uint32_t hist[256];
   __shared__ int red[kSelWaves];
   __shared__ uint32_t s_sel, s_rem;
+  __shared__ float red4[4];
+
+  float total = 0.f;
+  if constexpr (SCORED) total = usum_total(si.usum + static_cast<size_t>(b) * si.nblocks, si.nblocks, red4);
+  auto get_score = [&](int i) -> float {
+    if constexpr (SCORED)
+      return combine_score(si.mass[eoff + i], si.surprise[eoff + i], total, si.w_attn_norm, si.w_surprise);
+    else
+      return score[eoff + i];
+  };
 
   constexpr int NK = KPT > 0 ? KPT : 1;
   uint64_t keys[NK];
@@ -66,12 +79,17 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
       if (i < N) {
         const bool f = age[i] >= G;
         nf += f;
-        keys[j] = rank_key(score[i], f, i);
+        const float sc = get_score(i);
+        if constexpr (SCORED) si.score_out[eoff + i] = sc;
+        keys[j] = rank_key(sc, f, i);
       }
     }
   } else {
     keys[0] = 0;
-    for (int i = tid; i < N; i += kSelThreads) nf += age[i] >= G;
+    for (int i = tid; i < N; i += kSelThreads) {
+      nf += age[i] >= G;
+      if constexpr (SCORED) si.score_out[eoff + i] = get_score(i);
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) nf += __shfl_xor(nf, o, kWave);
@@ -103,7 +121,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         }
       } else {
         for (int i = tid; i < N; i += kSelThreads) {
-          const uint64_t key = rank_key(score[i], age[i] >= G, i);
+          const uint64_t key = rank_key(get_score(i), age[i] >= G, i);
           if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
         }
       }
@@ -181,7 +199,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
   } else {
     for (int t0 = 0; t0 < N; t0 += kSelThreads) {
       const int i = t0 + tid;
-      const bool flag = i < N && (take_all || (!take_none && rank_key(score[i], age[i] >= G, i) >= thr));
+      const bool flag = i < N && (take_all || (!take_none && rank_key(get_score(i), age[i] >= G, i) >= thr));
       compact(i, flag);
     }
   }
@@ -192,19 +210,31 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
   }
 }
 
-hipError_t launch_select(const float* score, int32_t* age, int B, int N, int k, int G, int rows_cap,
-                         int32_t* idx, int32_t* k_eff, int32_t* n_forced, hipStream_t s) {
+template <bool SCORED>
+static void launch_select_impl(const float* score, const ScoreInputs& si, int32_t* age, int B, int N, int k, int G,
+                               int rows_cap, int32_t* idx, int32_t* k_eff, int32_t* n_forced, hipStream_t s) {
   const dim3 grid(B), block(kSelThreads);
   if (N <= 1024)
-    select_topk_kernel<1><<<grid, block, 0, s>>>(score, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+    select_topk_kernel<1, SCORED><<<grid, block, 0, s>>>(score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
   else if (N <= 2048)
-    select_topk_kernel<2><<<grid, block, 0, s>>>(score, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+    select_topk_kernel<2, SCORED><<<grid, block, 0, s>>>(score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
   else if (N <= 4096)
-    select_topk_kernel<4><<<grid, block, 0, s>>>(score, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+    select_topk_kernel<4, SCORED><<<grid, block, 0, s>>>(score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
   else if (N <= 8192)
-    select_topk_kernel<8><<<grid, block, 0, s>>>(score, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+    select_topk_kernel<8, SCORED><<<grid, block, 0, s>>>(score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
   else
-    select_topk_kernel<0><<<grid, block, 0, s>>>(score, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+    select_topk_kernel<0, SCORED><<<grid, block, 0, s>>>(score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+}
+
+hipError_t launch_select(const float* score, int32_t* age, int B, int N, int k, int G, int rows_cap,
+                         int32_t* idx, int32_t* k_eff, int32_t* n_forced, hipStream_t s) {
+  launch_select_impl<false>(score, ScoreInputs{}, age, B, N, k, G, rows_cap, idx, k_eff, n_forced, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_scored(const ScoreInputs& si, int32_t* age, int B, int N, int k, int G, int rows_cap,
+                                int32_t* idx, int32_t* k_eff, int32_t* n_forced, hipStream_t s) {
+  launch_select_impl<true>(nullptr, si, age, B, N, k, G, rows_cap, idx, k_eff, n_forced, s);
   return hipGetLastError();
 }
 

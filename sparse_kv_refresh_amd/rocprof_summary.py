@@ -33,11 +33,12 @@ KIND_PATTERNS = {
     "score_pass2": "score_pass2_bf16",
     "select": "select_topk_kernel",
     "gather": "gather_kernel",
+    "gather_ln": "gather_ln_kernel",
     "ln_mod": "ln_mod_kernel",
 }
 KERNEL_SOURCE = {"gemm_qkv": "gemm.hip", "gemm_out_resid": "gemm.hip", "gemm_up_gelu": "gemm.hip",
                  "gemm_down_resid": "gemm.hip", "attention": "attention.hip", "score_pass1": "score.hip",
-                 "score_pass2": "score.hip", "select": "select.hip", "gather": "rows.hip", "ln_mod": "rows.hip"}
+                 "score_pass2": "score.hip", "select": "select.hip", "gather": "rows.hip", "gather_ln": "rows.hip", "ln_mod": "rows.hip"}
 
 
 def kernel_stats(db: str):
