@@ -64,16 +64,17 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   if (q0 >= rows) return;
 
   // per group: K tiles double-buffered (filled by direct-to-LDS loads), V^T
-  // single-buffered (written from registers)
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kGroups * (2 * kKsBytes + kVtElems * 2)];
+  // single-buffered (written from registers).  Separate arrays, so the
+  // compiler can see that the K prefetch never writes the V^T it reads.
+  __shared__ uint4 ks_all[kGroups][2][kKsBytes / 16];
+  __shared__ __attribute__((aligned(16))) bf16_t vt_all[kGroups][kVtElems];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int grp = wid >> 2, gw = wid & 3, gtid = tid & (kAttnThreads - 1);
   const int half = lane >> 5, col = lane & 31;
   const int N = a.N, d = a.d;
-  unsigned char* gbase = smem + grp * (2 * kKsBytes + kVtElems * 2);
-  uint4* Ks0 = reinterpret_cast<uint4*>(gbase);
-  bf16_t* Vt = reinterpret_cast<bf16_t*>(gbase + 2 * kKsBytes);
+  uint4* Ks0 = &ks_all[grp][0][0];
+  bf16_t* Vt = vt_all[grp];
   const bf16_t* Kc = static_cast<const bf16_t*>(a.k_cache) + static_cast<size_t>(b) * N * d + h * kDh;
   const bf16_t* Vc = static_cast<const bf16_t*>(a.v_cache) + static_cast<size_t>(b) * N * d + h * kDh;
 
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
     store_v();
     issue_k(it + 1, (it + 1) & 1);
     load_v(it + 1);
-    __syncthreads();
+    lds_barrier();   // V^T visible; the prefetches stay in flight
     const int t = it * kGroups + grp;
     if (t < ntiles) {
       half_tile(t, it & 1, 0);
@@ -217,22 +218,24 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   }
 
   // merge the two key groups: group 1 hands (o, m, l) to group 0 through LDS
+  // (o in the K buffers, 64 floats per lane; m and l in the V^T buffers)
   __syncthreads();
-  float* xch = reinterpret_cast<float*>(smem);
-  constexpr int kX = 66;   // floats per lane: 64 of o, m, l
+  float* xo = reinterpret_cast<float*>(&ks_all[0][0][0]);
+  float* xml = reinterpret_cast<float*>(&vt_all[0][0]);
+  static_assert(4 * 64 * 64 * 4 <= sizeof(ks_all), "exchange of o fits the K buffers");
   if (grp == 1) {
-    float* dst = xch + static_cast<size_t>(gw) * kX * 64 + lane;
+    float* dst = xo + static_cast<size_t>(gw) * 64 * 64 + lane;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int v = 0; v < 16; ++v) dst[(db * 16 + v) * 64] = o[db][v];
-    dst[64 * 64] = m_run;
-    dst[65 * 64] = l_run;
+    xml[(gw * 2 + 0) * 64 + lane] = m_run;
+    xml[(gw * 2 + 1) * 64 + lane] = l_run;
   }
   __syncthreads();
   if (grp == 1) return;
-  const float* src = xch + static_cast<size_t>(gw) * kX * 64 + lane;
-  const float m1 = src[64 * 64], l1 = src[65 * 64];
+  const float* src = xo + static_cast<size_t>(gw) * 64 * 64 + lane;
+  const float m1 = xml[(gw * 2 + 0) * 64 + lane], l1 = xml[(gw * 2 + 1) * 64 + lane];
   const float m = fmaxf(m_run, m1);
   const float e0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m) * scale2);
   const float e1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * scale2);

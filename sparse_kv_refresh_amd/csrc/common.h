@@ -63,6 +63,14 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Workgroup barrier that makes LDS writes visible but leaves vector-memory
+// traffic (prefetches of the next tile) in flight; __syncthreads() would wait
+// for those too.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((0xF) | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));   // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+}
+
 // Sum over the per-block surprise partials of one episode, by threads
 // 0..255 of the calling block in a fixed order (so every kernel that needs
 // sum_j U_j gets the same bits).  All threads of the block must call it.

@@ -87,19 +87,27 @@ __global__ __launch_bounds__(kScoreThreads) void score_pass1_bf16(
   __shared__ bf16_t sq[kMaxQB * 32 * kQaStride];
   __shared__ float2 sms[4][kMaxQB * 32];
 
-  stage_queries(qa + (static_cast<size_t>(l) * B + b) * A * d + h * kScoreDh, A, QB, d, sq);
-  __syncthreads();
-
   const bf16_t* kbase = kc + (static_cast<size_t>(l) * B + b) * N * d + h * kScoreDh;
   const int k0 = c * chunk_keys, k1 = min(N, k0 + chunk_keys);
+  // the first key block's fragments are requested before the queries are
+  // staged, so the two memory round trips overlap
+  uint4 kf[8];
+  {
+    const int key = k0 + wid * 32 + col;
+    load_k_frags(kbase + static_cast<size_t>(key) * d, key < k1, half, kf);
+  }
+  stage_queries(qa + (static_cast<size_t>(l) * B + b) * A * d + h * kScoreDh, A, QB, d, sq);
+  lds_barrier();
+
   float m[kMaxQB], z[kMaxQB];
 #pragma unroll
   for (int q = 0; q < kMaxQB; ++q) { m[q] = -INFINITY; z[q] = 0.f; }
 
   for (int kb = k0 + wid * 32; kb < k1; kb += 4 * 32) {
-    const int key = kb + col;
-    uint4 kf[8];
-    load_k_frags(kbase + static_cast<size_t>(key) * d, key < k1, half, kf);
+    // prefetch the wave's next key block
+    uint4 kn[8];
+    const int nkey = kb + 4 * 32 + col;
+    load_k_frags(kbase + static_cast<size_t>(nkey) * d, kb + 4 * 32 < k1 && nkey < k1, half, kn);
 #pragma unroll
     for (int q = 0; q < kMaxQB; ++q) {
       if (q >= QB) break;
@@ -121,13 +129,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_pass1_bf16(
       }
       if (tmax != -INFINITY) {
         const float mn = fmaxf(m[q], tmax);
-        float zz = m[q] == -INFINITY ? 0.f : z[q] * exp2f(m[q] - mn);
+        float zz = m[q] == -INFINITY ? 0.f : z[q] * __builtin_amdgcn_exp2f(m[q] - mn);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) zz += exp2f(sv[v] - mn);
+        for (int v = 0; v < 16; ++v) zz += __builtin_amdgcn_exp2f(sv[v] - mn);
         m[q] = mn;
         z[q] = zz;
       }
     }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = kn[s];
   }
   // merge the two lane halves (same query, different keys), then the waves
 #pragma unroll
@@ -156,6 +166,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_pass2_bf16(
   __shared__ bf16_t sq[kMaxQB * 32 * kQaStride];
   __shared__ float smax[kMaxQB * 32], sinv[kMaxQB * 32];
 
+  const bf16_t* kbase = kc + (static_cast<size_t>(l) * B + b) * N * d + h * kScoreDh;
+  float* prow = part + (static_cast<size_t>(b) * LH + lh) * N;
+  const int k0 = c * chunk_keys, k1 = min(N, k0 + chunk_keys);
+  uint4 kf[8];
+  {
+    const int key = k0 + wid * 32 + col;
+    load_k_frags(kbase + static_cast<size_t>(key) * d, key < k1, half, kf);
+  }
   stage_queries(qa + (static_cast<size_t>(l) * B + b) * A * d + h * kScoreDh, A, QB, d, sq);
   for (int a = threadIdx.x; a < QB * 32; a += kScoreThreads) {
     float mm = -INFINITY, zz = 0.f;
@@ -167,15 +185,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_pass2_bf16(
     smax[a] = a < A ? mm : INFINITY;   // padded queries contribute exp2(-inf) = 0
     sinv[a] = a < A ? 1.f / zz : 0.f;
   }
-  __syncthreads();
+  lds_barrier();
 
-  const bf16_t* kbase = kc + (static_cast<size_t>(l) * B + b) * N * d + h * kScoreDh;
-  float* prow = part + (static_cast<size_t>(b) * LH + lh) * N;
-  const int k0 = c * chunk_keys, k1 = min(N, k0 + chunk_keys);
   for (int kb = k0 + wid * 32; kb < k1; kb += 4 * 32) {
     const int key = kb + col;
-    uint4 kf[8];
-    load_k_frags(kbase + static_cast<size_t>(key) * d, key < k1, half, kf);
+    uint4 kn[8];
+    const int nkey = kb + 4 * 32 + col;
+    load_k_frags(kbase + static_cast<size_t>(nkey) * d, kb + 4 * 32 < k1 && nkey < k1, half, kn);
     float sum = 0.f;
 #pragma unroll
     for (int q = 0; q < kMaxQB; ++q) {
@@ -191,9 +207,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_pass2_bf16(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int qq = q * 32 + (v / 4) * 8 + half * 4 + (v % 4);
-        sum += exp2f(acc[v] * scale2 - smax[qq]) * sinv[qq];
+        sum += __builtin_amdgcn_exp2f(fmaf(acc[v], scale2, -smax[qq])) * sinv[qq];
       }
     }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = kn[s];
     sum += __shfl_xor(sum, 32, kWave);
     if (half == 0 && key < k1) prow[key] = sum;
   }
