@@ -445,6 +445,136 @@ void gemm_bf16_dtl_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// In-workgroup split-K for outputs too small to put two workgroups on every
+// CU: 8 waves in two groups of 4; group g multiplies k-tiles g, g+2, g+4, ...
+// of the same 128x128 output tile with its own LDS stages, so each SIMD runs
+// two waves; group 1 hands its accumulators to group 0 through LDS and group
+// 0 adds them (fixed order) and runs the epilogue.
+// ---------------------------------------------------------------------------
+
+constexpr int kKs2Threads = 2 * kGemmThreads;
+
+template <int EPI, int BK, int STAGES>
+__global__ __launch_bounds__(kKs2Threads, 1) void gemm_bf16_dtl_ks2_kernel(GemmArgs g) {
+  constexpr int BM = 128, BN = 128;
+  constexpr int CPR = BK / 8;
+  constexpr int CHUNKS_A = BM * CPR, CHUNKS_B = BN * CPR;
+  constexpr int LOADS_A = CHUNKS_A / kGemmThreads;
+  constexpr int LOADS_B = CHUNKS_B / kGemmThreads;
+  constexpr int LOADS = LOADS_A + LOADS_B;
+  constexpr int TI = 2, TJ = 2;
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.Nout + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (tile_empty(g, m0, BM)) return;
+
+  __shared__ uint4 lds[2][STAGES][CHUNKS_A + CHUNKS_B];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int grp = wid >> 2, gw = wid & 3;
+  const int wm = gw >> 1, wn = gw & 1;
+  const int half = lane >> 5, col = lane & 31;
+  const bf16_t* A = static_cast<const bf16_t*>(g.a);
+  const bf16_t* W = static_cast<const bf16_t*>(g.w);
+  const int K = g.K;
+
+  int goff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int il = i < LOADS_A ? i : i - LOADS_A;
+    const int c = (il * 4 + gw) * 64 + lane;
+    const int row = c / CPR;
+    const int kc = swz_kc<CPR>(row, c % CPR);
+    if (i < LOADS_A) goff[i] = min(m0 + row, g.M - 1) * K + kc * 8;
+    else goff[i] = min(n0 + row, g.Nout - 1) * K + kc * 8;
+  }
+  const int nk = K / BK;
+  const int iters = (nk + 1) / 2;
+  // iteration it of group grp multiplies k-tile 2*it + grp
+  auto issue = [&](int it, int stage) {
+    const int kt = 2 * it + grp;
+    if (kt >= nk) return;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const bf16_t* src = (i < LOADS_A ? A : W) + goff[i] + kt * BK;
+      const int il = i < LOADS_A ? i : i - LOADS_A;
+      uint4* dst = &lds[grp][stage][(i < LOADS_A ? 0 : CHUNKS_A) + (il * 4 + gw) * 64];
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
+    }
+  };
+
+  f32x16_t acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
+
+  const int ra = wm * (BM / 2) + col;
+  const int rb = wn * (BN / 2) + col;
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < iters) issue(p, p);
+  for (int it = 0; it < iters; ++it) {
+    // the counts of loads in flight differ between the groups only at the
+    // very end (odd nk), where both wait for everything
+    const int ahead = min(STAGES - 2, iters - 1 - it);
+    if constexpr (STAGES == 3) {
+      if (ahead >= 1 && 2 * (it + 1) + 1 < nk) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (it + STAGES - 1 < iters) issue(it + STAGES - 1, (it + STAGES - 1) % STAGES);
+    if (2 * it + grp < nk) {
+      const uint4* as = lds[grp][it % STAGES];
+      const uint4* ws = as + CHUNKS_A;
+#pragma unroll
+      for (int s = 0; s < BK / 16; ++s) {
+        const int kc = 2 * s + half;
+        bf16x8_t af[TI], bfr[TJ];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) af[i] = __builtin_bit_cast(bf16x8_t, as[swz<CPR>(ra + 32 * i, kc)]);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) bfr[j] = __builtin_bit_cast(bf16x8_t, ws[swz<CPR>(rb + 32 * j, kc)]);
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  __syncthreads();   // both groups are done with their LDS stages
+  float* xch = reinterpret_cast<float*>(&lds[0][0][0]);                 // 64 KB: group 1's partials
+  int* tab = reinterpret_cast<int*>(&lds[1][0][0]);                     // row table past them
+  static_assert(sizeof(lds[0]) >= 4 * 64 * 64 * 4 && sizeof(lds[1]) >= 2 * 128 * 4, "LDS budget");
+  if (grp == 1) {
+    float* dst = xch + static_cast<size_t>(gw) * 64 * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[((i * TJ + j) * 16 + v) * 64] = acc[i][j][v];
+  } else {
+    fill_row_table<EPI, BM>(g, m0, tab);
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  const float* src = xch + static_cast<size_t>(gw) * 64 * 64 + lane;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] += src[((i * TJ + j) * 16 + v) * 64];
+  tile_epilogue<EPI, BM, BN, TI, TJ>(g, acc, m0, n0, wm, wn, half, col, tab);
+}
+
+// ---------------------------------------------------------------------------
 // fp32 GEMM (VALU)
 // ---------------------------------------------------------------------------
 
@@ -516,6 +646,10 @@ static void launch_dtl(GemmEpi epi, const GemmArgs& g, hipStream_t s) {
 #ifndef WAMC_GEMM_TILE
 #define WAMC_GEMM_TILE 0
 #endif
+#ifndef WAMC_GEMM_SPLITK
+#define WAMC_GEMM_SPLITK 1
+#endif
+constexpr bool kSplitK = WAMC_GEMM_SPLITK != 0;
 
 // Tile shape per GEMM.  128x256 / 256x128 tiles stage a third fewer bytes per
 // FLOP through LDS, but measured on the d=1536 shapes (M ~ 2.5k) every GEMM
@@ -529,7 +663,19 @@ static int pick_tile(const GemmArgs& g) {
 hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer) {
   if (g.M <= 0 || g.Nout <= 0) return hipSuccess;
   TimedLaunch t(timer, gemm_name(g, epi), s);
-  if (bf16 && g.K % 64 == 0 && !kForceGeneric) {
+  // When the 128x128 tiles fit on the 256 CUs in one round, plain tiles leave
+  // one wave per SIMD; split-K gives every SIMD two.  (Measured: with more
+  // tiles than CUs, two plain workgroups per CU beat the split kernel.)
+  const long long t128 = static_cast<long long>((g.M + 127) / 128) * ((g.Nout + 127) / 128);
+  if (bf16 && g.K % 64 == 0 && !kForceGeneric && kSplitK && t128 <= 256 && g.K >= 2 * 64) {
+    const unsigned grid = static_cast<unsigned>(t128);
+    switch (epi) {
+      case EPI_QKV: gemm_bf16_dtl_ks2_kernel<EPI_QKV, 64, 2><<<grid, kKs2Threads, 0, s>>>(g); break;
+      case EPI_RESID_OUT: gemm_bf16_dtl_ks2_kernel<EPI_RESID_OUT, 64, 2><<<grid, kKs2Threads, 0, s>>>(g); break;
+      case EPI_RESID_DOWN: gemm_bf16_dtl_ks2_kernel<EPI_RESID_DOWN, 64, 2><<<grid, kKs2Threads, 0, s>>>(g); break;
+      case EPI_GELU: gemm_bf16_dtl_ks2_kernel<EPI_GELU, 64, 2><<<grid, kKs2Threads, 0, s>>>(g); break;
+    }
+  } else if (bf16 && g.K % 64 == 0 && !kForceGeneric) {
     switch (pick_tile(g)) {
       case 2: launch_dtl<128, 256, 32, 3>(epi, g, s); break;
       case 3: launch_dtl<256, 128, 32, 3>(epi, g, s); break;
