@@ -48,6 +48,11 @@ def parse():
                     help="only run warmup + timed refresh steps (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="refresh-fraction x age-bound sweep on the 30-layer stack shapes (one JSON line per point)")
+    ap.add_argument("--plateau", action="store_true",
+                    help="one-layer refresh latency vs refreshed rows, stepped every 32 rows (one JSON line)")
+    ap.add_argument("--sweep-layers", type=int, default=30, help="layers of the stack used by --sweep")
     return ap.parse_args()
 
 
@@ -99,7 +104,9 @@ def measured_traffic(kind: str, config: str):
 
 def cpu_baseline(wl, seconds: float):
     """The oracle as it stands, on the host cores: one dense chunk to build the
-    state, then refresh chunks of the same workload until ~`seconds`."""
+    state, then refresh chunks of the same workload until ~`seconds`.  Stacks
+    deeper than two layers or batches of episodes are sampled on the first two
+    layers of episode 0 and scaled by layers x episodes (stated in `sample`)."""
     from oracle import wamc_oracle as O
     from sparse_kv_refresh_amd import inputs as W
     try:
@@ -107,7 +114,10 @@ def cpu_baseline(wl, seconds: float):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    r = W.make_rollout(wl, chunks=2)
+    L_used = min(2, wl.n_layers)
+    swl = wl.with_(n_layers=L_used, batch=1)
+    scale = (wl.n_layers / L_used) * wl.batch
+    r = W.make_rollout(swl, chunks=2)
     prec = O.Precision(wl.dtype)
     t0 = time.perf_counter()
     st, _ = O.dense_prefill(r.z[0][0], r.weights, wl.n_heads, wl.ln_eps, prec)
@@ -122,11 +132,130 @@ def cpu_baseline(wl, seconds: float):
         times.append(time.perf_counter() - t0)
         if sum(times) + dense_s >= seconds or len(times) >= 5:
             break
-    return {"value": 1e3 * float(np.median(times)), "unit": "ms/chunk", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(times)} refresh chunk(s) of the {wl.name} workload (score + select + "
-                      f"{wl.n_layers} layer(s), k={wl.k} of N={wl.n_tokens}), numpy "
-                      f"{'float32+bf16 rounding' if wl.dtype == 'bf16' else 'float64'}; the oracle's dense "
-                      f"chunk took {1e3 * dense_s:.0f} ms"}
+    what = (f"{len(times)} refresh chunk(s) of the {wl.name} workload (score + select + {wl.n_layers} layer(s), "
+            f"k={wl.k} of N={wl.n_tokens})")
+    if scale != 1:
+        what = (f"{len(times)} refresh chunk(s) of the first {L_used} layers of one episode of the {wl.name} "
+                f"workload (k={wl.k} of N={wl.n_tokens}), scaled x{scale:g} to {wl.n_layers} layers x "
+                f"{wl.batch} episode(s)")
+    return {"value": 1e3 * float(np.median(times)) * scale, "unit": "ms/chunk", "cores": int(threads),
+            "kind": "oracle",
+            "sample": what + f"; numpy {'float32+bf16 rounding' if wl.dtype == 'bf16' else 'float64'}; "
+                             f"the oracle's dense chunk of the sample took {1e3 * dense_s:.0f} ms"}
+
+
+def run_sweep(args):
+    """Refresh fraction k/N x age bound G on the 30-layer stack shapes.  Per
+    point: a dense chunk, then 15 refresh chunks of the moving-blob rollout
+    with rows_cap = N (k_eff is only known on the device).  Reports the mean ms
+    per refresh chunk over chunks 2..15, the realised k_eff per chunk, the dense
+    ms, and two checks on the GPU's own state: k = N reproduces the dense
+    prefill bitwise, and k = 0 from ages below the bound leaves the cache
+    bitwise unchanged."""
+    import torch
+    from sparse_kv_refresh_amd import inputs as W
+    from sparse_kv_refresh_amd import wamc
+    base = W.preset("c3_stack", n_layers=args.sweep_layers)
+    T = base.chunks
+    r = W.make_rollout(base, chunks=T)
+    dev = "cuda:0"
+    weights = wamc.Engine.upload_weights(r.weights, torch.bfloat16, dev)
+    N = base.n_tokens
+    zs = [torch.from_numpy(r.z[0][t]).to(dev, torch.bfloat16)[None].contiguous() for t in range(T)]
+    qs = [None] + [torch.from_numpy(r.qa[0][t]).to(dev, torch.bfloat16)[:, None].contiguous() for t in range(1, T)]
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * T)]
+    for G in (2, 4, 8):
+        wl = base.with_(age_bound=G)
+        eng = wamc.Engine(wamc.dims_for(wl), weights, N, dev)
+        for frac in (0.0, 0.1, 0.25, 0.5, 0.75, 1.0):
+            k = int(round(frac * N))
+            eng.dense(zs[0])
+            before = eng.snapshot() if k == 0 else None
+            check = {}
+            for t in range(1, T):
+                ev[2 * t].record(stream)
+                eng.chunk(zs[t], qs[t], k, stream=stream)
+                ev[2 * t + 1].record(stream)
+                if t == 1 and k == 0:
+                    check["k0_cache_unchanged"] = bool(torch.equal(eng.k_cache, before["k_cache"]) and
+                                                       torch.equal(eng.v_cache, before["v_cache"]) and
+                                                       torch.equal(eng.zref, before["zref"]))
+                    before = None
+                if t == 1 and k == N:
+                    after = eng.snapshot()
+                    eng.dense(zs[1])
+                    check["kN_equals_dense"] = bool(torch.equal(eng.k_cache, after["k_cache"]) and
+                                                    torch.equal(eng.v_cache, after["v_cache"]))
+                    eng.restore(after)
+                    del after
+            torch.cuda.synchronize()
+            ms = [ev[2 * t].elapsed_time(ev[2 * t + 1]) for t in range(2, T)]
+            dms = []
+            for _ in range(3):
+                ev[0].record(stream)
+                eng.dense(zs[T - 1], stream=stream)
+                ev[1].record(stream)
+                torch.cuda.synchronize()
+                dms.append(ev[0].elapsed_time(ev[1]))
+            # k_eff per chunk is re-derived from a replay that records it
+            eng.dense(zs[0])
+            keffs = []
+            for t in range(1, T):
+                eng.chunk(zs[t], qs[t], k, stream=stream)
+                keffs.append(int(eng.k_eff[0]))
+            mean_ms = float(np.mean(ms))
+            print(json.dumps({"sweep": "refresh_fraction_x_age_bound", "layers": wl.n_layers, "n_tokens": N,
+                              "age_bound": G, "k": k, "k_over_n": frac, "k_eff_per_chunk": keffs,
+                              "k_eff_mean": float(np.mean(keffs)), "ms_per_chunk": mean_ms,
+                              "ms_per_chunk_p10_p90": [float(np.percentile(ms, 10)), float(np.percentile(ms, 90))],
+                              "dense_ms": float(np.median(dms)), "speedup_vs_dense": float(np.median(dms)) / mean_ms,
+                              "speedup_bound": N / max(float(np.mean(keffs)), 1.0), **check}), flush=True)
+        del eng
+
+
+def run_plateau(args):
+    """One d=1536 layer over N=4680 cached tokens: wamc_refresh_layer latency
+    as the number of refreshed rows m grows by 32, once with the launch sized
+    for the rows (rows_cap = m) and once sized for all N tokens with k_eff = m
+    read on the device (rows_cap = N)."""
+    import torch
+    from sparse_kv_refresh_amd import inputs as W
+    from sparse_kv_refresh_amd import wamc
+    wl = W.preset("c3_stack", n_layers=1)
+    r = W.make_rollout(wl, chunks=1)
+    dev = "cuda:0"
+    dims = wamc.dims_for(wl)
+    w = wamc.Engine.upload_weights(r.weights, torch.bfloat16, dev)[0]
+    N, d = wl.n_tokens, wl.d_model
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    kc = torch.randn((1, N, d), device=dev, generator=g).to(torch.bfloat16)
+    vc = torch.randn((1, N, d), device=dev, generator=g).to(torch.bfloat16)
+    x0 = torch.randn((1, N, d), device=dev, generator=g)
+    idx = torch.arange(N, dtype=torch.int32, device=dev)[None].contiguous()
+    ws = torch.empty(wamc.workspace_bytes(dims, N), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rows = list(range(32, N + 1, 32)) + ([N] if N % 32 else [])
+    curves = {}
+    for mode in ("rows_cap_m", "rows_cap_N"):
+        times = []
+        for m in rows:
+            cap = m if mode == "rows_cap_m" else N
+            keff = torch.tensor([m], dtype=torch.int32, device=dev)
+            x = x0[:, :cap].contiguous()
+            for _ in range(2):
+                wamc.refresh_layer(dims, 0, w, x, idx, keff, cap, kc, vc, ws, stream=stream)
+            a.record(stream)
+            for _ in range(5):
+                wamc.refresh_layer(dims, 0, w, x, idx, keff, cap, kc, vc, ws, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) / 5)
+        curves[mode] = times
+    print(json.dumps({"plateau": "refresh_layer", "d_model": d, "n_tokens": N, "rows": rows,
+                      "ms_per_layer": curves}), flush=True)
 
 
 def main():
@@ -135,6 +264,11 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); episodes shard across GPUs "
               "with no exchange, so the per-GPU figure at --gpus 1 is the whole story", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        return run_sweep(args)
+    if args.plateau:
+        return run_plateau(args)
 
     import torch
     from sparse_kv_refresh_amd import inputs as W

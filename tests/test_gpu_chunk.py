@@ -77,6 +77,13 @@ def test_rollout_oracle_refresh_set(name):
     _run_override_rollout(wl, wl.chunks)
 
 
+def test_large_model_shapes_reduced_tokens():
+    """The d=3072, 24-head, FFN 12288 layer with 128 action queries and two
+    episodes, on a reduced 2x12x20 token grid (k = N/2, age bound 4)."""
+    wl = W.preset("c5_large", n_layers=1, batch=2, rows=12, cols=20, k=240, chunks=3)
+    _run_override_rollout(wl, wl.chunks)
+
+
 def test_bench_workload_full_size():
     """d=1536, 12 heads, FFN 8960, N=4096, k=2458 (60 %), ages U{0..3} after
     the dense chunk: dense parity, then one refresh chunk with the oracle's

@@ -14,8 +14,8 @@ from gpu_util import DEV, act, batch_q, batch_z, max_rel, to_dev, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _setup(name):
-    wl = W.preset(name)
+def _setup(name, **over):
+    wl = W.preset(name, **over)
     r = W.make_rollout(wl, chunks=2)
     prec = O.Precision(wl.dtype)
     states = [O.dense_prefill(r.z[e][0], r.weights, wl.n_heads, wl.ln_eps, prec)[0] for e in range(wl.batch)]
@@ -24,9 +24,13 @@ def _setup(name):
     return wl, r, prec, states, K, zref
 
 
-@pytest.mark.parametrize("name", ["c1_tiny", "t_fp32_ragged", "t_bf16_small", "t_bf16_batch"])
-def test_score_parity(name):
-    wl, r, prec, states, K, zref = _setup(name)
+@pytest.mark.parametrize("name,over", [("c1_tiny", {}), ("t_fp32_ragged", {}), ("t_bf16_small", {}),
+                                       ("t_bf16_batch", {}),
+                                       # action-query counts: one, ragged, the 128 maximum, fp32 past one tile
+                                       ("t_bf16_small", {"n_action": 1}), ("t_bf16_small", {"n_action": 7}),
+                                       ("t_bf16_batch", {"n_action": 128}), ("t_fp32_ragged", {"n_action": 130})])
+def test_score_parity(name, over):
+    wl, r, prec, states, K, zref = _setup(name, **over)
     dims = wamc.dims_for(wl)
     B, N = wl.batch, wl.n_tokens
     z1, qa = batch_z(wl, r, 1), batch_q(wl, r, 1)
