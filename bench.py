@@ -254,8 +254,26 @@ def run_plateau(args):
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b) / 5)
         curves[mode] = times
+    # per-kernel split of the same calls (HIP events around every launch), every 128 rows
+    kernel_rows = [m for m in rows if m % 128 == 0 or m == 32 or m == N]
+    per_kernel = {}
+    for mode in ("rows_cap_m", "rows_cap_N"):
+        per_kernel[mode] = []
+        for m in kernel_rows:
+            cap = m if mode == "rows_cap_m" else N
+            keff = torch.tensor([m], dtype=torch.int32, device=dev)
+            x = x0[:, :cap].contiguous()
+            wamc.refresh_layer(dims, 0, w, x, idx, keff, cap, kc, vc, ws, stream=stream)
+            torch.cuda.synchronize()
+            wamc.timing_enable(True)
+            for _ in range(3):
+                wamc.refresh_layer(dims, 0, w, x, idx, keff, cap, kc, vc, ws, stream=stream)
+            torch.cuda.synchronize()
+            kt = wamc.timing_read()
+            wamc.timing_enable(False)
+            per_kernel[mode].append({k: 1e3 * tot / max(n, 1) for k, (n, tot) in kt.items()})
     print(json.dumps({"plateau": "refresh_layer", "d_model": d, "n_tokens": N, "rows": rows,
-                      "ms_per_layer": curves}), flush=True)
+                      "ms_per_layer": curves, "kernel_rows": kernel_rows, "kernel_us": per_kernel}), flush=True)
 
 
 def main():

@@ -220,6 +220,8 @@ struct WsLayout {
   ScorePlan sp;
   size_t ms, part, mass_tmp, surp_tmp, usum, score_tmp;   // score region
   size_t x, hbuf, qbuf, gbuf;                              // row region
+  GemmScratch gs;                                          // work-balanced GEMM scratch (bf16)
+  size_t sk_partial, sk_counters;
   size_t score_end, total;
 };
 
@@ -245,6 +247,9 @@ WsLayout ws_layout(const wamc_dims* d, int32_t rows_cap) {
   w.hbuf = take(rows * d->d_model * act_size(d));
   w.qbuf = take(rows * d->d_model * act_size(d));
   w.gbuf = take(rows * d->d_ffn * act_size(d));
+  w.gs = bf16 ? gemm_scratch(d->batch, rows_cap, d->d_model, d->d_ffn) : GemmScratch{};
+  w.sk_partial = take(w.gs.partial_bytes);
+  w.sk_counters = take(w.gs.counter_bytes);
   w.total = off;
   return w;
 }
@@ -282,6 +287,11 @@ int check_layer_w(const char* fn, const wamc_layer_w* w) {
   return WAMC_OK;
 }
 
+// The GEMM arrival counters start every call at zero (the GEMMs leave them so).
+hipError_t clear_gemm_scratch(void* ws, const WsLayout& L, hipStream_t s) {
+  return launch_gemm_scratch_clear(at<int>(ws, L.sk_counters), L.gs.counters, s);
+}
+
 // One layer on rows [b*rows_cap, b*rows_cap + k_eff[b]): reads x_in, writes
 // x_out (may alias x_in).
 hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_in, float* x_out,
@@ -315,6 +325,11 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
   g.n_tokens = d->n_tokens;
   g.d_model = D;
   g.idx = idx;
+  if (L.gs.slots > 0) {
+    g.sk_partial = at<float>(ws, L.sk_partial);
+    g.sk_counters = at<int>(ws, L.sk_counters);
+    g.sk_slots = L.gs.slots;
+  }
 
   g.a = hbuf; g.w = w->w_qkv; g.bias = w->b_qkv; g.Nout = 3 * D; g.K = D;
   g.q_out = qbuf; g.k_cache = kc; g.v_cache = vc;
@@ -503,7 +518,9 @@ int wamc_refresh_layer(const wamc_dims* dims, int32_t layer, const wamc_layer_w*
   OPT_PTR(ws);
   if ((st = check_device(fn))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(fn, run_layer(dims, w, x, x, idx, k_eff, rows_cap, k_cache_l, v_cache_l, ws, L, s), s);
+  hipError_t e = clear_gemm_scratch(ws, L, s);
+  if (e == hipSuccess) e = run_layer(dims, w, x, x, idx, k_eff, rows_cap, k_cache_l, v_cache_l, ws, L, s);
+  return hip_status(fn, e, s);
 }
 
 int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const void* z, void* zref,
@@ -567,6 +584,7 @@ int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const 
       e = launch_select_scored(si, age, B, N, k, dims->age_bound, rows_cap, idx_out, k_eff_out, nullptr, s);
     }
   }
+  if (e == hipSuccess) e = clear_gemm_scratch(ws, L, s);
   if (e != hipSuccess) return hip_status(fn, e, s);
   float* x = at<float>(ws, L.x);
   const size_t es = act_size(dims);
@@ -617,7 +635,8 @@ int wamc_dense_prefill(const wamc_dims* dims, const wamc_layer_w* layers, const 
   float* x = at<float>(ws, L.x);
   const size_t es = act_size(dims);
   const bool fuse_ln = D <= 4096;
-  hipError_t e;
+  hipError_t e = clear_gemm_scratch(ws, L, s);
+  if (e != hipSuccess) return hip_status(fn, e, s);
   if (fuse_ln)
     e = launch_gather_ln(bf16, z, zref, nullptr, nullptr, B, N, D, N, x, age, offset(layers[0].mod, 0, es),
                          offset(layers[0].mod, D, es), dims->ln_eps, at<char>(ws, L.hbuf), s, tm);

@@ -119,12 +119,12 @@ constexpr bool kForceGeneric = WAMC_GEMM_GENERIC != 0;
 // ---------------------------------------------------------------------------
 
 template <int EPI, int BM>
-__device__ __forceinline__ void fill_row_table(const GemmArgs& g, int m0, int* tab) {
+__device__ __forceinline__ void fill_row_table(const GemmArgs& g, int m0, int* tab, int mend = 0x7fffffff) {
   for (int t = threadIdx.x; t < BM; t += kGemmThreads) {
     const int m = m0 + t;
     const RowInfo ri = row_info(g, m);
     int r0 = -1, r1 = -1;
-    if (ri.valid) {
+    if (ri.valid && m < mend) {
       r0 = m;
       if constexpr (EPI == EPI_QKV) {
         const int tok = g.idx ? g.idx[static_cast<size_t>(ri.b) * g.n_tokens + ri.r] : ri.r;
@@ -575,6 +575,301 @@ __global__ __launch_bounds__(kKs2Threads, 1) void gemm_bf16_dtl_ks2_kernel(GemmA
 }
 
 // ---------------------------------------------------------------------------
+// Work-balanced bf16 GEMM over the refreshed rows.
+//
+// The number of refreshed rows exists only on the device (k_eff), so the grid
+// is sized for the most rows and every workgroup derives the work from k_eff:
+// T active output tiles (row tiles of each episode's k_eff rows x column
+// tiles).  With P workgroups resident at once, the first floor(T/P)*P tiles go
+// one per workgroup; the r remaining tiles (the last, partly empty round) are
+// split along K into S equal ranges, S chosen on the device from a cost model
+// (rounds of the r*S pieces x (fixed piece cost + K/S)) and the workgroups
+// the grid has to spare, so a small T, or a k_eff far below the rows the grid
+// was sized for, still fills the CUs.  All pieces of one split index walk the same K range at the same
+// time, so neighbouring tiles keep sharing operand lines in L2.  The last
+// piece of a tile to finish (per-tile arrival counter) adds the S partial
+// accumulators in split order -- independent of arrival order, so results are
+// reproducible -- and runs the epilogue.  No workgroup ever waits for another.
+// ---------------------------------------------------------------------------
+
+#ifndef WAMC_SK_MIN_ITERS
+#define WAMC_SK_MIN_ITERS 8
+#endif
+#ifndef WAMC_GEMM_SK
+#define WAMC_GEMM_SK 1
+#endif
+#ifndef WAMC_SK_MAX_SPLIT
+#define WAMC_SK_MAX_SPLIT 8
+#endif
+constexpr int kSkMinIters = WAMC_SK_MIN_ITERS;   // fewest k-tiles per split range
+constexpr int kSkMaxSplit = WAMC_SK_MAX_SPLIT;   // most pieces per tile
+#ifndef WAMC_SK_PIECE_COST
+#define WAMC_SK_PIECE_COST 16
+#endif
+// fixed cost of one piece (pipeline fill, partial store, arrival, fix-up), in k-tiles
+constexpr int kSkPieceCost = WAMC_SK_PIECE_COST;
+
+struct SkTile {
+  int m0, mend, n0;   // first row, end of the episode's valid rows, first column
+};
+
+// Active tile t (grouped order: 8 row tiles per column sweep) -> its rows/columns.
+template <int BM, int BN>
+__device__ __forceinline__ SkTile sk_tile(const GemmArgs& g, int t, int tiles_m, int tiles_n) {
+  constexpr int GM = 8;
+  const int group = t / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in_group = t - group * GM * tiles_n;
+  int tm = first_m + in_group % gsize;
+  SkTile r{0, 0, (in_group / gsize) * BN};
+  const int B = g.M / g.rows_cap;
+  for (int b = 0; b < B; ++b) {
+    const int rows = rows_of(g.k_eff, b, g.rows_cap);
+    const int rt = (rows + BM - 1) / BM;
+    if (tm < rt) {
+      r.m0 = b * g.rows_cap + tm * BM;
+      r.mend = b * g.rows_cap + rows;
+      break;
+    }
+    tm -= rt;
+  }
+  return r;
+}
+
+template <int EPI, int BM, int BN, int BK, int STAGES>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_sk_kernel(GemmArgs g) {
+  constexpr int CPR = BK / 8;
+  constexpr int CHUNKS_A = BM * CPR, CHUNKS_B = BN * CPR;
+  constexpr int LOADS_A = CHUNKS_A / kGemmThreads;
+  constexpr int LOADS_B = CHUNKS_B / kGemmThreads;
+  constexpr int LOADS = LOADS_A + LOADS_B;
+  constexpr int TI = BM / 64, TJ = BN / 64;
+  constexpr int F4 = TI * TJ * 4;                      // float4 partials per thread
+  static_assert(LOADS_A * kGemmThreads == CHUNKS_A && LOADS_B * kGemmThreads == CHUNKS_B, "tile/threads");
+
+  const int B = g.M / g.rows_cap;
+  int tiles_m = 0;
+  for (int b = 0; b < B; ++b) tiles_m += (rows_of(g.k_eff, b, g.rows_cap) + BM - 1) / BM;
+  const int tiles_n = (g.Nout + BN - 1) / BN;
+  const int tiles = tiles_m * tiles_n;
+  const int P = g.sk_slots;
+  const int ndp = (tiles / P) * P;        // tiles done one per workgroup
+  const int r = tiles - ndp;              // tail tiles, split along K
+  const int nk = g.K / BK;
+  const int h = blockIdx.x;
+  int S = 1, u = 0;
+  if (h >= ndp) {
+    if (r == 0) return;
+    // S minimising (rounds of r*S pieces) x (piece overhead + nk/S k-tiles), with
+    // the pieces within the grid and the partial slots and >= kSkMinIters k-tiles each
+    const int room = min(static_cast<int>(gridDim.x) - ndp, 2 * P);
+    const int smax = max(1, min(min(kSkMaxSplit, nk / kSkMinIters), room / r));
+    float best = static_cast<float>((r + P - 1) / P) * static_cast<float>(kSkPieceCost + nk);
+    for (int c = 2; c <= smax; ++c) {
+      const float cost = static_cast<float>((r * c + P - 1) / P) * (static_cast<float>(kSkPieceCost) +
+                                                                    static_cast<float>(nk) / c);
+      if (cost < best) {
+        best = cost;
+        S = c;
+      }
+    }
+    if (h - ndp >= r * S) return;
+    u = xcd_remap(h - ndp, r * S);
+  }
+
+  // one LDS object only: a second __shared__ variable makes the compiler wait
+  // for the tile loads in flight before every LDS read (it cannot tell the
+  // objects apart from the direct-to-LDS writes)
+  __shared__ uint4 lds[STAGES][CHUNKS_A + CHUNKS_B];
+  int* s_last = reinterpret_cast<int*>(&lds[STAGES - 1][CHUNKS_A + CHUNKS_B - 1]);   // clear of the row table
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int half = lane >> 5, col = lane & 31;
+  const bf16_t* A = static_cast<const bf16_t*>(g.a);
+  const bf16_t* Wt = static_cast<const bf16_t*>(g.w);
+  const int K = g.K;
+
+  // this workgroup's piece: tile tl, k-tiles [kk0, kk1)
+  SkTile tl;
+  int kk0 = 0, kk1 = nk, tt = 0;
+  if (h < ndp) {
+    tl = sk_tile<BM, BN>(g, xcd_remap(h, ndp), tiles_m, tiles_n);
+  } else {
+    tt = u / S;
+    const int sp = u - tt * S;   // split index
+    tl = sk_tile<BM, BN>(g, ndp + tt, tiles_m, tiles_n);
+    kk0 = sp * nk / S;
+    kk1 = (sp + 1) * nk / S;
+  }
+
+  int goff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int il = i < LOADS_A ? i : i - LOADS_A;
+    const int c = (il * 4 + wid) * 64 + lane;
+    const int row = c / CPR;
+    const int kc = swz_kc<CPR>(row, c % CPR);
+    if (i < LOADS_A) goff[i] = min(tl.m0 + row, g.M - 1) * K + kc * 8 + kk0 * BK;
+    else goff[i] = min(tl.n0 + row, g.Nout - 1) * K + kc * 8 + kk0 * BK;
+  }
+  auto issue = [&](int kt, int stage) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const bf16_t* src = (i < LOADS_A ? A : Wt) + goff[i] + kt * BK;
+      const int il = i < LOADS_A ? i : i - LOADS_A;
+      uint4* dst = &lds[stage][(i < LOADS_A ? 0 : CHUNKS_A) + (il * 4 + wid) * 64];
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
+    }
+  };
+
+  f32x16_t acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
+
+  const int ra = wm * (BM / 2) + col;
+  const int rb = wn * (BN / 2) + col;
+  const int n = kk1 - kk0;
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < n) issue(p, p);
+  for (int q = 0; q < n; ++q) {
+    const int ahead = min(STAGES - 2, n - 1 - q);
+    if constexpr (STAGES >= 4) {
+      if (ahead >= 2) wait_vmcnt<2 * LOADS>();
+      else if (ahead == 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+    } else if constexpr (STAGES == 3) {
+      if (ahead >= 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (q + STAGES - 1 < n) issue(q + STAGES - 1, (q + STAGES - 1) % STAGES);
+    const uint4* as = lds[q % STAGES];
+    const uint4* ws = as + CHUNKS_A;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int kc = 2 * s + half;
+      bf16x8_t af[TI], bfr[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) af[i] = __builtin_bit_cast(bf16x8_t, as[swz<CPR>(ra + 32 * i, kc)]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) bfr[j] = __builtin_bit_cast(bf16x8_t, ws[swz<CPR>(rb + 32 * j, kc)]);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  auto finish = [&]() {
+    __syncthreads();   // every wave is done with the LDS stages
+    int* tab = reinterpret_cast<int*>(&lds[0][0]);
+    fill_row_table<EPI, BM>(g, tl.m0, tab, tl.mend);
+    __syncthreads();
+    tile_epilogue<EPI, BM, BN, TI, TJ>(g, acc, tl.m0, tl.n0, wm, wn, half, col, tab);
+  };
+  if (S == 1) {
+    finish();
+    return;
+  }
+  // Partial tiles live in scratch slot u (piece u of the tail).  They are
+  // written and read as relaxed system-scope atomics (sc0 sc1 accesses that go
+  // to the coherence point and back), so no cache-wide write-back or
+  // invalidate is needed between the workgroups of one tile.
+  unsigned long long* part = reinterpret_cast<unsigned long long*>(g.sk_partial);
+  const size_t own = static_cast<size_t>(u) * (BM * BN / 2);   // 8-byte words
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v2 = 0; v2 < 8; ++v2) {
+        const unsigned long long x = (static_cast<unsigned long long>(__float_as_uint(acc[i][j][2 * v2 + 1])) << 32) |
+                                     __float_as_uint(acc[i][j][2 * v2]);
+        __hip_atomic_store(part + own + static_cast<size_t>(((i * TJ + j) * 8 + v2) * kGemmThreads + tid), x,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+  // the stores have reached the coherence point before the arrival is counted
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    int* cnt = &g.sk_counters[ndp + tt];
+    const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int last = old == S - 1 ? 1 : 0;
+    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);   // ready for the next launch
+    *s_last = last;
+  }
+  __syncthreads();
+  if (!*s_last) return;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
+  for (int v = 0; v < S; ++v) {
+    const unsigned long long* src = part + static_cast<size_t>(tt * S + v) * (BM * BN / 2);
+    unsigned long long p[F4 * 2];
+#pragma unroll
+    for (int q = 0; q < F4 * 2; ++q)
+      p[q] = __hip_atomic_load(src + q * kGemmThreads + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int v2 = 0; v2 < 8; ++v2) {
+          const unsigned long long x = p[(i * TJ + j) * 8 + v2];
+          acc[i][j][2 * v2] += __uint_as_float(static_cast<unsigned>(x));
+          acc[i][j][2 * v2 + 1] += __uint_as_float(static_cast<unsigned>(x >> 32));
+        }
+  }
+  finish();
+}
+
+__global__ void zero_ints_kernel(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+GemmScratch gemm_scratch(int B, int rows_cap, int d, int F) {
+  GemmScratch s{};
+  if (rows_cap <= 0) return s;
+  const int widest = max(3 * d, F);
+  s.slots = kGemmSkSlotsMax;
+  s.counters = B * ((rows_cap + 127) / 128) * ((widest + 127) / 128);
+  s.partial_bytes = static_cast<size_t>(2) * s.slots * 128 * 128 * sizeof(float);
+  s.counter_bytes = static_cast<size_t>(s.counters) * sizeof(int);
+  return s;
+}
+
+hipError_t launch_gemm_scratch_clear(int* counters, int n, hipStream_t s) {
+  if (!counters || n <= 0) return hipSuccess;
+  zero_ints_kernel<<<(n + 255) / 256, 256, 0, s>>>(counters, n);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int STAGES>
+static void launch_sk(GemmEpi epi, const GemmArgs& g, hipStream_t s) {
+  const int B = g.M / g.rows_cap;
+  const long long tiles_cap = static_cast<long long>(B) * ((g.rows_cap + BM - 1) / BM) * ((g.Nout + BN - 1) / BN);
+  const int P = g.sk_slots;
+  // one workgroup per tile at the most rows; at least P so few tiles can be split
+  const unsigned grid = static_cast<unsigned>(max(tiles_cap, static_cast<long long>(P)));
+  switch (epi) {
+    case EPI_QKV: gemm_bf16_sk_kernel<EPI_QKV, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
+    case EPI_RESID_OUT: gemm_bf16_sk_kernel<EPI_RESID_OUT, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
+    case EPI_RESID_DOWN: gemm_bf16_sk_kernel<EPI_RESID_DOWN, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
+    case EPI_GELU: gemm_bf16_sk_kernel<EPI_GELU, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 GEMM (VALU)
 // ---------------------------------------------------------------------------
 
@@ -663,11 +958,20 @@ static int pick_tile(const GemmArgs& g) {
 hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer) {
   if (g.M <= 0 || g.Nout <= 0) return hipSuccess;
   TimedLaunch t(timer, gemm_name(g, epi), s);
-  // When the 128x128 tiles fit on the 256 CUs in one round, plain tiles leave
-  // one wave per SIMD; split-K gives every SIMD two.  (Measured: with more
-  // tiles than CUs, two plain workgroups per CU beat the split kernel.)
+  // Kernel choice from the tile count at rows_cap rows (measured on the d=1536
+  // shapes).  When those 128x128 tiles fit the 256 CUs in one round, the
+  // in-workgroup split-K kernel gives every SIMD two waves without a trip
+  // through memory; with a long K and at most half the CUs' worth of tiles the
+  // work-balanced kernel, which splits K over more workgroups, is faster.
+  // Otherwise the work-balanced kernel sizes its work from k_eff on the device.
   const long long t128 = static_cast<long long>((g.M + 127) / 128) * ((g.Nout + 127) / 128);
-  if (bf16 && g.K % 64 == 0 && !kForceGeneric && kSplitK && t128 <= 256 && g.K >= 2 * 64) {
+  const bool dtl_ok = bf16 && g.K % 64 == 0 && !kForceGeneric;
+  const bool use_ks2 = dtl_ok && kSplitK && t128 <= 256 && g.K >= 2 * 64 && (g.K < 4096 || t128 > 128);
+  const bool use_sk = dtl_ok && WAMC_GEMM_SK && g.sk_partial && g.sk_counters && g.sk_slots > 0 &&
+                      g.sk_slots <= kGemmSkSlotsMax;
+  if (!use_ks2 && use_sk) {
+    launch_sk<128, 128, 64, 2>(epi, g, s);
+  } else if (use_ks2) {
     const unsigned grid = static_cast<unsigned>(t128);
     switch (epi) {
       case EPI_QKV: gemm_bf16_dtl_ks2_kernel<EPI_QKV, 64, 2><<<grid, kKs2Threads, 0, s>>>(g); break;
@@ -675,7 +979,7 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
       case EPI_RESID_DOWN: gemm_bf16_dtl_ks2_kernel<EPI_RESID_DOWN, 64, 2><<<grid, kKs2Threads, 0, s>>>(g); break;
       case EPI_GELU: gemm_bf16_dtl_ks2_kernel<EPI_GELU, 64, 2><<<grid, kKs2Threads, 0, s>>>(g); break;
     }
-  } else if (bf16 && g.K % 64 == 0 && !kForceGeneric) {
+  } else if (dtl_ok) {
     switch (pick_tile(g)) {
       case 2: launch_dtl<128, 256, 32, 3>(epi, g, s); break;
       case 3: launch_dtl<256, 128, 32, 3>(epi, g, s); break;

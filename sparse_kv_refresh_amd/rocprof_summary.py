@@ -18,16 +18,17 @@ import collections
 import hashlib
 import json
 import os
+import re
 import sqlite3
 import sys
 
 COPY_BYTES = 1 << 30
 
 KIND_PATTERNS = {
-    "gemm_qkv": "gemm_bf16_dtl_kernel<0",
-    "gemm_out_resid": "gemm_bf16_dtl_kernel<1",
-    "gemm_down_resid": "gemm_bf16_dtl_kernel<3",
-    "gemm_up_gelu": "gemm_bf16_dtl_kernel<2",
+    "gemm_qkv": r"gemm_bf16_\w*kernel<\(?wamc::GemmEpi\)?0|gemm_bf16_\w*kernel<0",
+    "gemm_out_resid": r"gemm_bf16_\w*kernel<\(?wamc::GemmEpi\)?1|gemm_bf16_\w*kernel<1",
+    "gemm_down_resid": r"gemm_bf16_\w*kernel<\(?wamc::GemmEpi\)?3|gemm_bf16_\w*kernel<3",
+    "gemm_up_gelu": r"gemm_bf16_\w*kernel<\(?wamc::GemmEpi\)?2|gemm_bf16_\w*kernel<2",
     "attention": "attn_bf16_kernel",
     "score_pass1": "score_pass1_bf16",
     "score_pass2": "score_pass2_bf16",
@@ -101,7 +102,7 @@ def main(argv=None):
     for key, db, cname in (("fetch", args.fetch_db, "FETCH_SIZE"), ("write", args.write_db, "WRITE_SIZE")):
         vals = counters(db, cname)
         f = copy_factor(vals, cname)
-        launches = [v for kn, vs in vals.items() if pat in kn for v in vs]
+        launches = [v for kn, vs in vals.items() if re.search(pat, kn) for v in vs]
         launches = launches[args.skip_first * args.per_step:]
         launches = launches[args.occurrence::args.per_step]
         if not launches:

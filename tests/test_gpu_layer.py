@@ -73,3 +73,47 @@ def test_refresh_layer_parity(name):
     assert (x[0, m:] == 123.0).all()
     untouched = np.setdiff1d(np.arange(N), idx)
     assert np.array_equal(to_np(kc[0])[untouched], Kc[untouched])
+
+
+@pytest.mark.parametrize("m,spare", [(37, False), (37, True), (300, True), (1100, False), (1100, True),
+                                     (2458, False)])
+def test_refresh_layer_wide(m, spare):
+    """The d=1536, FFN 8960 layer over N=4096 cached tokens with m refreshed
+    rows, the launch sized for the rows (rows_cap = m) or for every token
+    (rows_cap = N, k_eff = m read on the device): covers the GEMM schedules
+    that split K over several workgroups and the one-tile-per-workgroup
+    rounds."""
+    wl = W.preset("c2_layer")
+    r = W.make_rollout(wl, chunks=1)
+    prec = O.Precision(wl.dtype)
+    N, d = wl.n_tokens, wl.d_model
+    rng = np.random.default_rng(m)
+    idx = np.sort(rng.choice(N, size=m, replace=False)).astype(np.int32)
+    Kc = prec.store(rng.standard_normal((N, d)).astype(np.float32) * 0.5)
+    Vc = prec.store(rng.standard_normal((N, d)).astype(np.float32) * 0.5)
+    X = rng.standard_normal((m, d)).astype(np.float32)
+    Ko, Vo = Kc.astype(prec.acc).copy(), Vc.astype(prec.acc).copy()
+    want = O.block(X.astype(prec.acc), idx, r.weights[0], Ko, Vo, wl.n_heads, wl.ln_eps, prec)
+
+    dims = wamc.dims_for(wl)
+    w = wamc.Engine.upload_weights(r.weights, act(wl), DEV)[0]
+    rows_cap = N if spare else m
+    x = torch.full((1, rows_cap, d), 77.0, dtype=torch.float32, device=DEV)
+    x[0, :m] = torch.from_numpy(X).to(DEV)
+    idx_full = np.full((1, N), -1, dtype=np.int32)
+    idx_full[0, :m] = idx
+    kc, vc = to_dev(Kc, act(wl))[None].contiguous(), to_dev(Vc, act(wl))[None].contiguous()
+    keff = torch.tensor([m], dtype=torch.int32, device=DEV)
+    ws = torch.empty(wamc.workspace_bytes(dims, rows_cap), dtype=torch.uint8, device=DEV)
+    for rep in range(2):   # a second call reuses the workspace (arrival counters must be back at zero)
+        if rep:
+            x[0, :m] = torch.from_numpy(X).to(DEV)
+            kc.copy_(to_dev(Kc, act(wl))[None])
+            vc.copy_(to_dev(Vc, act(wl))[None])
+        wamc.refresh_layer(dims, 0, w, x, to_dev(idx_full), keff, rows_cap, kc, vc, ws)
+        torch.cuda.synchronize()
+        for nm, g, o in (("X", to_np(x[0, :m]), want), ("K", to_np(kc[0]), Ko), ("V", to_np(vc[0]), Vo)):
+            ok, err = close(wl, g, o)
+            assert ok, f"call {rep} {nm}: {err}"
+        if spare:
+            assert (x[0, m:] == 77.0).all()
