@@ -222,6 +222,8 @@ struct WsLayout {
   size_t x, hbuf, qbuf, gbuf;                              // row region
   GemmScratch gs;                                          // work-balanced GEMM scratch (bf16)
   size_t sk_partial, sk_counters;
+  AttnScratch as;                                          // key-split attention scratch (bf16)
+  size_t at_part, at_counters;
   size_t score_end, total;
 };
 
@@ -250,6 +252,9 @@ WsLayout ws_layout(const wamc_dims* d, int32_t rows_cap) {
   w.gs = bf16 ? gemm_scratch(d->batch, rows_cap, d->d_model, d->d_ffn) : GemmScratch{};
   w.sk_partial = take(w.gs.partial_bytes);
   w.sk_counters = take(w.gs.counter_bytes);
+  w.as = bf16 && d->head_dim == 128 ? attn_scratch(d->batch, rows_cap, d->n_heads) : AttnScratch{};
+  w.at_part = take(w.as.part_bytes);
+  w.at_counters = take(w.as.counter_bytes);
   w.total = off;
   return w;
 }
@@ -289,7 +294,9 @@ int check_layer_w(const char* fn, const wamc_layer_w* w) {
 
 // The GEMM arrival counters start every call at zero (the GEMMs leave them so).
 hipError_t clear_gemm_scratch(void* ws, const WsLayout& L, hipStream_t s) {
-  return launch_gemm_scratch_clear(at<int>(ws, L.sk_counters), L.gs.counters, s);
+  hipError_t e = launch_gemm_scratch_clear(at<int>(ws, L.sk_counters), L.gs.counters, s);
+  if (e == hipSuccess) e = launch_gemm_scratch_clear(at<int>(ws, L.at_counters), L.as.counters, s);
+  return e;
 }
 
 // One layer on rows [b*rows_cap, b*rows_cap + k_eff[b]): reads x_in, writes
@@ -340,6 +347,11 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
   at_.q = qbuf; at_.k_cache = kc; at_.v_cache = vc; at_.o = hbuf;
   at_.B = B; at_.N = d->n_tokens; at_.H = d->n_heads; at_.dh = d->head_dim; at_.d = D;
   at_.rows_cap = rows_cap; at_.k_eff = k_eff;
+  if (L.as.slots > 0) {
+    at_.part = at<float>(ws, L.at_part);
+    at_.counters = at<int>(ws, L.at_counters);
+    at_.slots = L.as.slots;
+  }
   e = launch_attention(bf16, at_, s, tm);
   if (e != hipSuccess) return e;
 

@@ -26,6 +26,7 @@
 #include "common.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace wamc {
@@ -53,15 +54,78 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // of one ds_read_b128 phase then cover all 64 banks.
 __device__ __forceinline__ int ks_chunk(int row, int c) { return row * 16 + (c ^ (row & 15)); }
 
+// Key-split of the last round: with P workgroups resident (one per CU) and T
+// active (query tile, head, episode) units -- only tiles holding refreshed
+// rows count, read from k_eff on the device -- the first floor(T/P)*P units
+// take one workgroup each over all N keys; each of the r remaining units is
+// cut into C key ranges, C chosen from a cost model (rounds of the r*C pieces
+// x (fixed piece cost + key tiles per piece) + merge cost per piece) within
+// the grid's spare workgroups.  A split unit is completed by the last of its
+// pieces to arrive: it merges the C partial (o, max, sum) in key order, so
+// the result does not depend on arrival order.
+#ifndef WAMC_ATTN_MAX_SPLIT
+#define WAMC_ATTN_MAX_SPLIT 16
+#endif
+#ifndef WAMC_ATTN_PIECE_COST
+#define WAMC_ATTN_PIECE_COST 8
+#endif
+#ifndef WAMC_ATTN_MERGE_COST
+#define WAMC_ATTN_MERGE_COST 2
+#endif
+constexpr int kAttnP = 256;                      // resident workgroups (one per CU)
+constexpr int kAttnMinTiles = 4;                 // fewest key tiles per piece
+constexpr int kAttnMaxSplit = WAMC_ATTN_MAX_SPLIT;
+constexpr int kAttnPieceCost = WAMC_ATTN_PIECE_COST;   // in key tiles
+constexpr int kAttnMergeCost = WAMC_ATTN_MERGE_COST;   // in key tiles, per merged piece
+
 __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a, float scale2) {
-  // 1-D grid over (q-tile, head, episode), q-tile fastest, remapped so the
-  // q-tiles of one head run on one XCD and share its K/V in that L2
-  const int qtiles = (a.rows_cap + kAttnQ - 1) / kAttnQ;
-  const int id = xcd_remap(blockIdx.x, qtiles * a.H * a.B);
-  const int qt = id % qtiles, h = (id / qtiles) % a.H, b = id / (qtiles * a.H);
+  int T = 0;
+  for (int bb = 0; bb < a.B; ++bb) T += (rows_of(a.k_eff, bb, a.rows_cap) + kAttnQ - 1) / kAttnQ;
+  T *= a.H;
+  const int ntiles = (a.N + kAttnKeys - 1) / kAttnKeys;
+  const int ndp = (T / kAttnP) * kAttnP;
+  const int hw = blockIdx.x;
+  int unit, C = 1, piece = 0, c = 0;
+  if (hw < ndp) {
+    unit = xcd_remap(hw, ndp);
+  } else {
+    const int r = T - ndp;
+    if (r == 0) return;
+    if (a.part) {
+      const int room = min(static_cast<int>(gridDim.x) - ndp, a.slots);
+      const int cmax = max(1, min(min(kAttnMaxSplit, ntiles / kAttnMinTiles), room / r));
+      float best = static_cast<float>((r + kAttnP - 1) / kAttnP) * static_cast<float>(kAttnPieceCost + ntiles);
+      for (int cc = 2; cc <= cmax; ++cc) {
+        const float cost = static_cast<float>((r * cc + kAttnP - 1) / kAttnP) *
+                               (static_cast<float>(kAttnPieceCost) + static_cast<float>(ntiles) / cc) +
+                           static_cast<float>(kAttnMergeCost * cc);
+        if (cost < best) {
+          best = cost;
+          C = cc;
+        }
+      }
+    }
+    if (hw - ndp >= r * C) return;
+    piece = xcd_remap(hw - ndp, r * C);
+    unit = ndp + piece / C;
+    c = piece % C;
+  }
+  // unit -> (episode, head, query tile), query tile fastest: the tiles of one
+  // head run on one XCD and share its K/V in that L2
+  int b = 0, rt = 1;
+  {
+    int u = unit;
+    for (b = 0; b < a.B; ++b) {
+      rt = (rows_of(a.k_eff, b, a.rows_cap) + kAttnQ - 1) / kAttnQ;
+      if (u < rt * a.H) break;
+      u -= rt * a.H;
+    }
+    unit = u;   // index within the episode
+  }
+  const int h = unit / rt, qt = unit - h * rt;
   const int rows = rows_of(a.k_eff, b, a.rows_cap);
   const int q0 = qt * kAttnQ;
-  if (q0 >= rows) return;
+  const int kt0 = c * ntiles / C, kt1 = (c + 1) * ntiles / C;   // this piece's key tiles
 
   // per group: K tiles double-buffered (filled by direct-to-LDS loads), V^T
   // single-buffered (written from registers).  Separate arrays, so the
@@ -87,12 +151,11 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   for (int s = 0; s < 8; ++s)
     qf[s] = qrow < rows ? *reinterpret_cast<const uint4*>(Qp + s * 16 + half * 8) : make_uint4(0, 0, 0, 0);
 
-  const int ntiles = (N + kAttnKeys - 1) / kAttnKeys;
-  const int iters = (ntiles + kGroups - 1) / kGroups;
-  // group grp takes tiles grp, grp + 2, grp + 4, ...
+  const int iters = (kt1 - kt0 + kGroups - 1) / kGroups;
+  // group grp takes tiles kt0 + grp, kt0 + grp + 2, ... below kt1
   auto issue_k = [&](int it, int stage) {
-    const int t = it * kGroups + grp;
-    if (t >= ntiles) return;
+    const int t = kt0 + it * kGroups + grp;
+    if (t >= kt1) return;
     // 64 rows x 16 chunks = 1024 chunks, 4 per thread; instruction i of wave
     // gw fills LDS chunks (i*4 + gw)*64 + lane
 #pragma unroll
@@ -108,11 +171,11 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   const int vkb = gtid & 15, vdb = gtid >> 4;
   uint4 rv[4];
   auto load_v = [&](int it) {
-    const int t = it * kGroups + grp;
+    const int t = kt0 + it * kGroups + grp;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kv = t * kAttnKeys + vkb * 4 + i;
-      rv[i] = (t < ntiles && kv < N) ? *reinterpret_cast<const uint4*>(Vc + static_cast<size_t>(kv) * d + vdb * 8)
+      rv[i] = (t < kt1 && kv < N) ? *reinterpret_cast<const uint4*>(Vc + static_cast<size_t>(kv) * d + vdb * 8)
                                      : make_uint4(0, 0, 0, 0);
     }
   };
@@ -210,8 +273,8 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
     issue_k(it + 1, (it + 1) & 1);
     load_v(it + 1);
     lds_barrier();   // V^T visible; the prefetches stay in flight
-    const int t = it * kGroups + grp;
-    if (t < ntiles) {
+    const int t = kt0 + it * kGroups + grp;
+    if (t < kt1) {
       half_tile(t, it & 1, 0);
       half_tile(t, it & 1, 1);
     }
@@ -233,32 +296,117 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
     xml[(gw * 2 + 1) * 64 + lane] = l_run;
   }
   __syncthreads();
-  if (grp == 1) return;
   const float* src = xo + static_cast<size_t>(gw) * 64 * 64 + lane;
-  const float m1 = xml[(gw * 2 + 0) * 64 + lane], l1 = xml[(gw * 2 + 1) * 64 + lane];
-  const float m = fmaxf(m_run, m1);
-  const float e0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m) * scale2);
-  const float e1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * scale2);
-  const float lsum = l_run * e0 + l1 * e1;
-  const float l = lsum + __shfl_xor(lsum, 32, kWave);
-  if (qrow >= rows) return;
-  const float inv = 1.0f / l;
+  float m = 0.f, e0 = 0.f, e1 = 0.f, l = 0.f;
+  if (grp == 0) {
+    const float m1 = xml[(gw * 2 + 0) * 64 + lane], l1 = xml[(gw * 2 + 1) * 64 + lane];
+    m = fmaxf(m_run, m1);
+    e0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m) * scale2);
+    e1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * scale2);
+    const float lsum = l_run * e0 + l1 * e1;
+    l = lsum + __shfl_xor(lsum, 32, kWave);
+  }
   bf16_t* Op = static_cast<bf16_t*>(a.o) + (static_cast<size_t>(b) * a.rows_cap + qrow) * d + h * kDh;
+  if (C == 1) {
+    if (grp == 1 || qrow >= rows) return;
+    const float inv = 1.0f / l;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        // elements v = g4*4 .. g4*4+3: dh rows db*32 + g4*8 + half*4 + 0..3
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = g4 * 4 + e;
+          r[e] = (o[db][v] * e0 + src[(db * 16 + v) * 64] * e1) * inv;
+        }
+        uint2 w;
+        w.x = pack_bf16x2(r[0], r[1]);
+        w.y = pack_bf16x2(r[2], r[3]);
+        *reinterpret_cast<uint2*>(Op + db * 32 + g4 * 8 + half * 4) = w;
+      }
+    return;
+  }
+
+  // split unit: group 0 writes this piece's (o relative to m, m, l) to its
+  // scratch slot as relaxed system-scope atomics (coherent between the XCDs'
+  // caches without cache-wide maintenance), then the arrival is counted
+  const int gl = gw * 64 + lane;   // lane of group 0 holding the same queries
+  float* slot_base = a.part;
+  if (grp == 0) {
+    float* dst = slot_base + static_cast<size_t>(piece) * kAttnPartFloats;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const int v = g4 * 4 + e;
+          const float x0 = o[db][v] * e0 + src[(db * 16 + v) * 64] * e1;
+          const float x1 = o[db][v + 1] * e0 + src[(db * 16 + v + 1) * 64] * e1;
+          const unsigned long long w = (static_cast<unsigned long long>(__float_as_uint(x1)) << 32) | __float_as_uint(x0);
+          __hip_atomic_store(reinterpret_cast<unsigned long long*>(dst) + ((db * 4 + g4) * 2 + e / 2) * 256 + gl, w,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    __hip_atomic_store(dst + 128 * 128 + gl, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(dst + 128 * 128 + 256 + gl, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // the stores have reached the coherence point
+  __syncthreads();
+  int* flag = reinterpret_cast<int*>(xml) + 1024;   // past the exchanged m, l
+  const int uid = piece / C + ndp;
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(&a.counters[uid], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int last = old == C - 1 ? 1 : 0;
+    if (last) __hip_atomic_store(&a.counters[uid], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    *flag = last;
+  }
+  __syncthreads();
+  if (!*flag || qrow >= rows) return;
+  // last piece: merge the C partials in key order; group g finishes dh blocks 2g, 2g+1
+  const float* first = slot_base + static_cast<size_t>(piece - c) * kAttnPartFloats;
+  float mt = -INFINITY;
+  for (int cc = 0; cc < C; ++cc)
+    mt = fmaxf(mt, __hip_atomic_load(first + static_cast<size_t>(cc) * kAttnPartFloats + 128 * 128 + gl,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
+  float acc[2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+  float lt = 0.f;
+  for (int cc = 0; cc < C; ++cc) {
+    const float* pp = first + static_cast<size_t>(cc) * kAttnPartFloats;
+    const float mc = __hip_atomic_load(pp + 128 * 128 + gl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const float lc = __hip_atomic_load(pp + 128 * 128 + 256 + gl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const float sc = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mc - mt) * scale2);
+    lt += lc * sc;
+    unsigned long long w[16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        w[i * 8 + q] = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(pp) +
+                                             (((2 * grp + i) * 4 + q / 2) * 2 + q % 2) * 256 + gl,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        acc[i][2 * q] += __uint_as_float(static_cast<unsigned>(w[i * 8 + q])) * sc;
+        acc[i][2 * q + 1] += __uint_as_float(static_cast<unsigned>(w[i * 8 + q] >> 32)) * sc;
+      }
+  }
+  const float inv = 1.0f / lt;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      // elements v = g4*4 .. g4*4+3: dh rows db*32 + g4*8 + half*4 + 0..3
-      float r[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = g4 * 4 + e;
-        r[e] = (o[db][v] * e0 + src[(db * 16 + v) * 64] * e1) * inv;
-      }
       uint2 w;
-      w.x = pack_bf16x2(r[0], r[1]);
-      w.y = pack_bf16x2(r[2], r[3]);
-      *reinterpret_cast<uint2*>(Op + db * 32 + g4 * 8 + half * 4) = w;
+      w.x = pack_bf16x2(acc[i][g4 * 4 + 0] * inv, acc[i][g4 * 4 + 1] * inv);
+      w.y = pack_bf16x2(acc[i][g4 * 4 + 2] * inv, acc[i][g4 * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(Op + (2 * grp + i) * 32 + g4 * 8 + half * 4) = w;
     }
 }
 
@@ -317,13 +465,32 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s, KernelT
   TimedLaunch t(timer, "attention", s);
   const float scale2 = kLog2e / sqrtf(static_cast<float>(a.dh));
   if (bf16) {
-    const unsigned grid = static_cast<unsigned>(((a.rows_cap + kAttnQ - 1) / kAttnQ) * a.H * a.B);
+    // one workgroup per unit at rows_cap rows; room for the pieces of split
+    // units: a full round when the units overflow one round, else the round
+    // itself (unused workgroups exit at once)
+    const long long units = static_cast<long long>((a.rows_cap + kAttnQ - 1) / kAttnQ) * a.H * a.B;
+    const long long spare = units > kAttnP ? units + kAttnP : kAttnP;
+    const unsigned grid = static_cast<unsigned>(a.part ? spare : units);
     attn_bf16_kernel<<<grid, kAttnThreads2, 0, s>>>(a, scale2);
   } else {
     const dim3 grid((a.rows_cap + 3) / 4, a.H, a.B);
     attn_f32_kernel<<<grid, 256, 0, s>>>(a, scale2);
   }
   return hipGetLastError();
+}
+
+}  // namespace wamc
+
+namespace wamc {
+
+AttnScratch attn_scratch(int B, int rows_cap, int H) {
+  AttnScratch s{};
+  if (rows_cap <= 0) return s;
+  s.slots = kAttnSlotsMax;
+  s.counters = B * ((rows_cap + kAttnQ - 1) / kAttnQ) * H;
+  s.part_bytes = static_cast<size_t>(s.slots) * kAttnPartFloats * sizeof(float);
+  s.counter_bytes = static_cast<size_t>(s.counters) * sizeof(int);
+  return s;
 }
 
 }  // namespace wamc

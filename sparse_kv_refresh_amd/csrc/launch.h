@@ -128,7 +128,20 @@ struct AttnArgs {
   void* o;              // [B*rows_cap, d] act
   int B, N, H, dh, d, rows_cap;
   const int32_t* k_eff;
+  // scratch of the key-split bf16 path (nullable: one workgroup per query tile)
+  float* part;          // [slots, kAttnPartFloats] partial (o, m, l) per piece
+  int* counters;        // per-unit arrival counters, zero between launches
+  int slots;
 };
 hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s, KernelTimer* timer);
+
+// Scratch of the key-split attention for B episodes of rows_cap rows and H heads.
+constexpr int kAttnSlotsMax = 512;
+constexpr int kAttnPartFloats = 128 * 128 + 2 * 256;   // o (128 queries x 128 dh) + m, l per lane
+struct AttnScratch {
+  size_t part_bytes, counter_bytes;
+  int slots, counters;
+};
+AttnScratch attn_scratch(int B, int rows_cap, int H);
 
 }  // namespace wamc
