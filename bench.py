@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--profile-steps", action="store_true",
                     help="only run warmup + timed refresh steps (for rocprofv3 runs)")
+    ap.add_argument("--profile-events", action="store_true",
+                    help="with --profile-steps: HIP events around every launch, as in the per-kernel pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--sweep", action="store_true",
@@ -336,7 +338,13 @@ def main():
         return a.elapsed_time(b) / steps, 1e3 * wall / steps
 
     if args.profile_steps:
+        if args.profile_events:
+            wamc.timing_enable(True)
         ms, _ = timed(refresh_step, args.steps, args.warmup)
+        if args.profile_events:
+            kt = wamc.timing_read()
+            wamc.timing_enable(False)
+            print(json.dumps({k: 1e3 * tot / max(n, 1) for k, (n, tot) in kt.items()}))
         if args.copy_calibration:
             src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
             dst = torch.empty_like(src)

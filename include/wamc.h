@@ -108,7 +108,11 @@ const char* wamc_last_error(void);
 
 /* Bytes of scratch workspace any call below needs for these sizes and a row
  * capacity of rows_cap rows per episode (the dense prefill uses rows_cap = N).
- * One workspace of this size serves every entry point. */
+ * One workspace of this size serves every entry point.  For bf16 it includes
+ * about 100 MiB for the kernels that split work across workgroups (partial
+ * tiles and arrival counters); the calls clear what must start at zero, so
+ * the workspace needs no initialisation.  Calls that share one workspace
+ * must not overlap on the device (same stream, or synchronised). */
 int wamc_workspace_bytes(const wamc_dims* dims, int32_t rows_cap, size_t* bytes);
 
 /* Token scores (WAM-Cache §1, §4.2, §4.3).

@@ -292,18 +292,27 @@ int check_layer_w(const char* fn, const wamc_layer_w* w) {
   return WAMC_OK;
 }
 
-// The GEMM arrival counters start every call at zero (the GEMMs leave them so).
-hipError_t clear_gemm_scratch(void* ws, const WsLayout& L, hipStream_t s) {
-  hipError_t e = launch_gemm_scratch_clear(at<int>(ws, L.sk_counters), L.gs.counters, s);
-  if (e == hipSuccess) e = launch_gemm_scratch_clear(at<int>(ws, L.at_counters), L.as.counters, s);
-  return e;
+// The arrival counters of the split GEMM / attention start every call at zero
+// (the kernels leave them so); the first row kernel of the call clears them.
+ZeroJob counter_clear(void* ws, const WsLayout& L) {
+  ZeroJob z;
+  if (L.gs.counters > 0) {
+    z.p0 = at<int>(ws, L.sk_counters);
+    z.n0 = L.gs.counters;
+  }
+  if (L.as.counters > 0) {
+    z.p1 = at<int>(ws, L.at_counters);
+    z.n1 = L.as.counters;
+  }
+  return z;
 }
 
 // One layer on rows [b*rows_cap, b*rows_cap + k_eff[b]): reads x_in, writes
 // x_out (may alias x_in).
 hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_in, float* x_out,
                      const int32_t* idx, const int32_t* k_eff, int32_t rows_cap, void* kc, void* vc,
-                     void* ws, const WsLayout& L, hipStream_t s, bool h1_ready = false) {
+                     void* ws, const WsLayout& L, hipStream_t s, bool h1_ready = false,
+                     const ZeroJob& zj = ZeroJob{}) {
   const bool bf16 = d->dtype == WAMC_BF16;
   const size_t es = act_size(d);
   const int D = d->d_model, F = d->d_ffn, B = d->batch;
@@ -321,7 +330,7 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
   hipError_t e;
 
   if (!h1_ready) {
-    e = launch_ln_mod(bf16, x_in, shift1, scale1, B, rows_cap, k_eff, D, d->ln_eps, hbuf, s, tm);
+    e = launch_ln_mod(bf16, x_in, shift1, scale1, B, rows_cap, k_eff, D, d->ln_eps, hbuf, zj, s, tm);
     if (e != hipSuccess) return e;
   }
 
@@ -360,7 +369,7 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
   e = launch_gemm(bf16, EPI_RESID_OUT, g, s, tm);
   if (e != hipSuccess) return e;
 
-  e = launch_ln_mod(bf16, x_out, shift2, scale2, B, rows_cap, k_eff, D, d->ln_eps, hbuf, s, tm);
+  e = launch_ln_mod(bf16, x_out, shift2, scale2, B, rows_cap, k_eff, D, d->ln_eps, hbuf, ZeroJob{}, s, tm);
   if (e != hipSuccess) return e;
 
   g.a = hbuf; g.w = w->w_1; g.bias = w->b_1; g.Nout = F; g.K = D; g.g_out = gbuf;
@@ -506,7 +515,7 @@ int wamc_gather(const wamc_dims* dims, const void* z, void* zref, const int32_t*
   if ((st = check_device(fn))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(fn, launch_gather(dims->dtype == WAMC_BF16, z, zref, idx, k_eff, dims->batch, dims->n_tokens,
-                                      dims->d_model, rows_cap, x, nullptr, s, active_timer()), s);
+                                      dims->d_model, rows_cap, x, nullptr, ZeroJob{}, s, active_timer()), s);
 }
 
 int wamc_refresh_layer(const wamc_dims* dims, int32_t layer, const wamc_layer_w* w, float* x,
@@ -530,9 +539,8 @@ int wamc_refresh_layer(const wamc_dims* dims, int32_t layer, const wamc_layer_w*
   OPT_PTR(ws);
   if ((st = check_device(fn))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = clear_gemm_scratch(ws, L, s);
-  if (e == hipSuccess) e = run_layer(dims, w, x, x, idx, k_eff, rows_cap, k_cache_l, v_cache_l, ws, L, s);
-  return hip_status(fn, e, s);
+  return hip_status(fn, run_layer(dims, w, x, x, idx, k_eff, rows_cap, k_cache_l, v_cache_l, ws, L, s, false,
+                                  counter_clear(ws, L)), s);
 }
 
 int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const void* z, void* zref,
@@ -596,16 +604,15 @@ int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const 
       e = launch_select_scored(si, age, B, N, k, dims->age_bound, rows_cap, idx_out, k_eff_out, nullptr, s);
     }
   }
-  if (e == hipSuccess) e = clear_gemm_scratch(ws, L, s);
   if (e != hipSuccess) return hip_status(fn, e, s);
   float* x = at<float>(ws, L.x);
   const size_t es = act_size(dims);
   const bool fuse_ln = D <= 4096;
   if (fuse_ln)
     e = launch_gather_ln(bf16, z, zref, idx_out, k_eff_out, B, N, D, rows_cap, x, nullptr, offset(layers[0].mod, 0, es),
-                         offset(layers[0].mod, D, es), dims->ln_eps, at<char>(ws, L.hbuf), s, tm);
+                         offset(layers[0].mod, D, es), dims->ln_eps, at<char>(ws, L.hbuf), counter_clear(ws, L), s, tm);
   else
-    e = launch_gather(bf16, z, zref, idx_out, k_eff_out, B, N, D, rows_cap, x, nullptr, s, tm);
+    e = launch_gather(bf16, z, zref, idx_out, k_eff_out, B, N, D, rows_cap, x, nullptr, counter_clear(ws, L), s, tm);
   const size_t layer_elems = static_cast<size_t>(B) * N * D;
   const size_t out_elems = static_cast<size_t>(B) * rows_cap * D;
   for (int l = 0; l < dims->n_layers && e == hipSuccess; ++l) {
@@ -647,13 +654,12 @@ int wamc_dense_prefill(const wamc_dims* dims, const wamc_layer_w* layers, const 
   float* x = at<float>(ws, L.x);
   const size_t es = act_size(dims);
   const bool fuse_ln = D <= 4096;
-  hipError_t e = clear_gemm_scratch(ws, L, s);
-  if (e != hipSuccess) return hip_status(fn, e, s);
+  hipError_t e;
   if (fuse_ln)
     e = launch_gather_ln(bf16, z, zref, nullptr, nullptr, B, N, D, N, x, age, offset(layers[0].mod, 0, es),
-                         offset(layers[0].mod, D, es), dims->ln_eps, at<char>(ws, L.hbuf), s, tm);
+                         offset(layers[0].mod, D, es), dims->ln_eps, at<char>(ws, L.hbuf), counter_clear(ws, L), s, tm);
   else
-    e = launch_gather(bf16, z, zref, nullptr, nullptr, B, N, D, N, x, age, s, tm);
+    e = launch_gather(bf16, z, zref, nullptr, nullptr, B, N, D, N, x, age, counter_clear(ws, L), s, tm);
   const size_t layer_elems = static_cast<size_t>(B) * N * D;
   for (int l = 0; l < dims->n_layers && e == hipSuccess; ++l) {
     const float* xin = (layer_out && l > 0) ? layer_out + (l - 1) * layer_elems : x;

@@ -832,11 +832,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_sk_kernel(GemmArgs 
   finish();
 }
 
-__global__ void zero_ints_kernel(int* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
-
 GemmScratch gemm_scratch(int B, int rows_cap, int d, int F) {
   GemmScratch s{};
   if (rows_cap <= 0) return s;
@@ -846,12 +841,6 @@ GemmScratch gemm_scratch(int B, int rows_cap, int d, int F) {
   s.partial_bytes = static_cast<size_t>(2) * s.slots * 128 * 128 * sizeof(float);
   s.counter_bytes = static_cast<size_t>(s.counters) * sizeof(int);
   return s;
-}
-
-hipError_t launch_gemm_scratch_clear(int* counters, int n, hipStream_t s) {
-  if (!counters || n <= 0) return hipSuccess;
-  zero_ints_kernel<<<(n + 255) / 256, 256, 0, s>>>(counters, n);
-  return hipGetLastError();
 }
 
 template <int BM, int BN, int BK, int STAGES>

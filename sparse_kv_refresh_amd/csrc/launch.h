@@ -65,20 +65,29 @@ hipError_t launch_score_finish(const float* mass_tmp, const float* surprise_tmp,
                                float* mass_out, float* surprise_out, hipStream_t s, KernelTimer* timer);
 
 // ----- row kernels (rows.hip) -----
+// Side job of the first row kernel of a call: zero two int arrays (the
+// arrival counters of the split GEMM / attention), so no extra launch is needed.
+struct ZeroJob {
+  int* p0 = nullptr;
+  int n0 = 0;
+  int* p1 = nullptr;
+  int n1 = 0;
+};
 // x[b*rows_cap + r] = float(z[b, idx[b,r]]), zref[b, idx] = z[b, idx]
 // (idx == nullptr: identity, rows = all N tokens; age (nullable) <- 0).
 hipError_t launch_gather(bool bf16, const void* z, void* zref, const int32_t* idx, const int32_t* k_eff,
-                         int B, int N, int d, int rows_cap, float* x, int32_t* age_zero, hipStream_t s,
-                         KernelTimer* timer);
+                         int B, int N, int d, int rows_cap, float* x, int32_t* age_zero, const ZeroJob& zj,
+                         hipStream_t s, KernelTimer* timer);
 // gather fused with the first modulated LayerNorm (d <= 4096): also writes
 // h = act(LN(x) * (1 + scale) + shift)
 hipError_t launch_gather_ln(bool bf16, const void* z, void* zref, const int32_t* idx, const int32_t* k_eff, int B,
                             int N, int d, int rows_cap, float* x, int32_t* age_zero, const void* shift,
-                            const void* scale, float eps, void* h, hipStream_t s, KernelTimer* timer);
+                            const void* scale, float eps, void* h, const ZeroJob& zj, hipStream_t s,
+                            KernelTimer* timer);
 // h[m] = act(LN(x_in[m]) * (1 + scale) + shift) for valid rows.
 hipError_t launch_ln_mod(bool bf16, const float* x, const void* shift, const void* scale, int B,
-                         int rows_cap, const int32_t* k_eff, int d, float eps, void* h, hipStream_t s,
-                         KernelTimer* timer);
+                         int rows_cap, const int32_t* k_eff, int d, float eps, void* h, const ZeroJob& zj,
+                         hipStream_t s, KernelTimer* timer);
 
 // ----- GEMM (gemm.hip) -----
 // EPI_RESID_OUT and EPI_RESID_DOWN share one epilogue; they are separate
@@ -117,8 +126,6 @@ struct GemmScratch {
   int slots, counters;
 };
 GemmScratch gemm_scratch(int B, int rows_cap, int d, int F);
-// zero the arrival counters (once per call that runs GEMMs; they stay zero after)
-hipError_t launch_gemm_scratch_clear(int* counters, int n, hipStream_t s);
 
 // ----- attention (attention.hip) -----
 struct AttnArgs {

@@ -15,11 +15,20 @@ namespace wamc {
 
 constexpr int kRowThreads = 256;   // 4 rows per block
 
+// every block zeroes its grid-strided share of the side job's arrays
+__device__ __forceinline__ void zero_job(const ZeroJob& zj) {
+  const int nthreads = gridDim.x * gridDim.y * kRowThreads;
+  const int i0 = (blockIdx.y * gridDim.x + blockIdx.x) * kRowThreads + threadIdx.x;
+  for (int i = i0; i < zj.n0; i += nthreads) zj.p0[i] = 0;
+  for (int i = i0; i < zj.n1; i += nthreads) zj.p1[i] = 0;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void gather_kernel(
     const T* __restrict__ z, T* __restrict__ zref, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ k_eff, int N, int d, int rows_cap, float* __restrict__ x,
-    int32_t* __restrict__ age_zero) {
+    int32_t* __restrict__ age_zero, ZeroJob zj) {
+  zero_job(zj);
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int r = blockIdx.x * (kRowThreads / kWave) + wid;
@@ -55,16 +64,16 @@ __global__ __launch_bounds__(kRowThreads) void gather_kernel(
 }
 
 hipError_t launch_gather(bool bf16, const void* z, void* zref, const int32_t* idx, const int32_t* k_eff,
-                         int B, int N, int d, int rows_cap, float* x, int32_t* age_zero, hipStream_t s,
-                         KernelTimer* timer) {
+                         int B, int N, int d, int rows_cap, float* x, int32_t* age_zero, const ZeroJob& zj,
+                         hipStream_t s, KernelTimer* timer) {
   TimedLaunch t(timer, "gather", s);
   const dim3 grid((rows_cap + 3) / 4, B);
   if (bf16)
     gather_kernel<bf16_t><<<grid, kRowThreads, 0, s>>>(static_cast<const bf16_t*>(z),
-        static_cast<bf16_t*>(zref), idx, k_eff, N, d, rows_cap, x, age_zero);
+        static_cast<bf16_t*>(zref), idx, k_eff, N, d, rows_cap, x, age_zero, zj);
   else
     gather_kernel<float><<<grid, kRowThreads, 0, s>>>(static_cast<const float*>(z),
-        static_cast<float*>(zref), idx, k_eff, N, d, rows_cap, x, age_zero);
+        static_cast<float*>(zref), idx, k_eff, N, d, rows_cap, x, age_zero, zj);
   return hipGetLastError();
 }
 
@@ -80,7 +89,8 @@ __global__ __launch_bounds__(kRowThreads) void gather_ln_kernel(
     const T* __restrict__ z, T* __restrict__ zref, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ k_eff, int N, int d, int rows_cap, float* __restrict__ x,
     int32_t* __restrict__ age_zero, const T* __restrict__ shift, const T* __restrict__ scale, float eps,
-    T* __restrict__ h) {
+    T* __restrict__ h, ZeroJob zj) {
+  zero_job(zj);
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int r = blockIdx.x * (kRowThreads / kWave) + wid;
@@ -141,18 +151,19 @@ __global__ __launch_bounds__(kRowThreads) void gather_ln_kernel(
 
 hipError_t launch_gather_ln(bool bf16, const void* z, void* zref, const int32_t* idx, const int32_t* k_eff, int B,
                             int N, int d, int rows_cap, float* x, int32_t* age_zero, const void* shift,
-                            const void* scale, float eps, void* h, hipStream_t s, KernelTimer* timer) {
+                            const void* scale, float eps, void* h, const ZeroJob& zj, hipStream_t s,
+                            KernelTimer* timer) {
   if (d > kMaxRowChunks * 256) return hipErrorInvalidValue;
   TimedLaunch t(timer, "gather_ln", s);
   const dim3 grid((rows_cap + 3) / 4, B);
   if (bf16)
     gather_ln_kernel<bf16_t><<<grid, kRowThreads, 0, s>>>(static_cast<const bf16_t*>(z), static_cast<bf16_t*>(zref),
         idx, k_eff, N, d, rows_cap, x, age_zero, static_cast<const bf16_t*>(shift),
-        static_cast<const bf16_t*>(scale), eps, static_cast<bf16_t*>(h));
+        static_cast<const bf16_t*>(scale), eps, static_cast<bf16_t*>(h), zj);
   else
     gather_ln_kernel<float><<<grid, kRowThreads, 0, s>>>(static_cast<const float*>(z), static_cast<float*>(zref),
         idx, k_eff, N, d, rows_cap, x, age_zero, static_cast<const float*>(shift),
-        static_cast<const float*>(scale), eps, static_cast<float*>(h));
+        static_cast<const float*>(scale), eps, static_cast<float*>(h), zj);
   return hipGetLastError();
 }
 
@@ -161,7 +172,8 @@ hipError_t launch_gather_ln(bool bf16, const void* z, void* zref, const int32_t*
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void ln_mod_kernel(
     const float* __restrict__ x, const T* __restrict__ shift, const T* __restrict__ scale,
-    int rows_cap, const int32_t* __restrict__ k_eff, int d, float eps, T* __restrict__ h) {
+    int rows_cap, const int32_t* __restrict__ k_eff, int d, float eps, T* __restrict__ h, ZeroJob zj) {
+  zero_job(zj);
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int r = blockIdx.x * (kRowThreads / kWave) + wid;
@@ -196,16 +208,16 @@ __global__ __launch_bounds__(kRowThreads) void ln_mod_kernel(
 }
 
 hipError_t launch_ln_mod(bool bf16, const float* x, const void* shift, const void* scale, int B,
-                         int rows_cap, const int32_t* k_eff, int d, float eps, void* h, hipStream_t s,
-                         KernelTimer* timer) {
+                         int rows_cap, const int32_t* k_eff, int d, float eps, void* h, const ZeroJob& zj,
+                         hipStream_t s, KernelTimer* timer) {
   TimedLaunch t(timer, "ln_mod", s);
   const dim3 grid((rows_cap + 3) / 4, B);
   if (bf16)
     ln_mod_kernel<bf16_t><<<grid, kRowThreads, 0, s>>>(x, static_cast<const bf16_t*>(shift),
-        static_cast<const bf16_t*>(scale), rows_cap, k_eff, d, eps, static_cast<bf16_t*>(h));
+        static_cast<const bf16_t*>(scale), rows_cap, k_eff, d, eps, static_cast<bf16_t*>(h), zj);
   else
     ln_mod_kernel<float><<<grid, kRowThreads, 0, s>>>(x, static_cast<const float*>(shift),
-        static_cast<const float*>(scale), rows_cap, k_eff, d, eps, static_cast<float*>(h));
+        static_cast<const float*>(scale), rows_cap, k_eff, d, eps, static_cast<float*>(h), zj);
   return hipGetLastError();
 }
 
