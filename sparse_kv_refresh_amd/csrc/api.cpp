@@ -341,10 +341,10 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
   g.n_tokens = d->n_tokens;
   g.d_model = D;
   g.idx = idx;
-  if (L.gs.slots > 0) {
+  if (L.gs.partial_bytes > 0) {
     g.sk_partial = at<float>(ws, L.sk_partial);
+    g.sk_partial_bytes = L.gs.partial_bytes;
     g.sk_counters = at<int>(ws, L.sk_counters);
-    g.sk_slots = L.gs.slots;
   }
 
   g.a = hbuf; g.w = w->w_qkv; g.bias = w->b_qkv; g.Nout = 3 * D; g.K = D;

@@ -26,6 +26,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace wamc {
 
 // ---------------------------------------------------------------------------
@@ -118,9 +120,9 @@ constexpr bool kForceGeneric = WAMC_GEMM_GENERIC != 0;
 // token), so the per-element work is a table read, the bias and the store.
 // ---------------------------------------------------------------------------
 
-template <int EPI, int BM>
+template <int EPI, int BM, int NT = kGemmThreads>
 __device__ __forceinline__ void fill_row_table(const GemmArgs& g, int m0, int* tab, int mend = 0x7fffffff) {
-  for (int t = threadIdx.x; t < BM; t += kGemmThreads) {
+  for (int t = threadIdx.x; t < BM; t += NT) {
     const int m = m0 + t;
     const RowInfo ri = row_info(g, m);
     int r0 = -1, r1 = -1;
@@ -144,14 +146,17 @@ __device__ __forceinline__ void fill_row_table(const GemmArgs& g, int m0, int* t
 //   n = n0 + wn*(BN/2) + j*32 + g*8 + half*4 + (0..3),
 // so each lane checks its row once and stores 4 columns with one 8-byte
 // (bf16) or 16-byte (f32) access.
-template <int EPI, int BM, int BN, int TI, int TJ>
+template <int EPI, int BM, int BN, int TI, int TJ, int WTM = BM / 2, int WTN = BN / 2>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t (&acc)[TI][TJ], int m0, int n0,
                                               int wm, int wn, int half, int col, const int* tab) {
   const bool full_n = n0 + BN <= g.Nout;   // Nout % 4 == 0: groups never straddle Nout
   const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
-    const int lr = wm * (BM / 2) + i * 32 + col;
+    // keep each row block's loads and stores together: hoisting the residual
+    // loads of every block at once costs more registers than large tiles have
+    __builtin_amdgcn_sched_barrier(0);
+    const int lr = wm * WTM + i * 32 + col;
     const int rq = tab[lr];
     if constexpr (EPI == EPI_QKV) {
       const int rkv = tab[BM + lr];
@@ -163,7 +168,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t 
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-          const int n = n0 + wn * (BN / 2) + j * 32 + gg * 8 + half * 4;
+          const int n = n0 + wn * WTN + j * 32 + gg * 8 + half * 4;
           if (!full_n && n >= g.Nout) continue;
           const int which = which0 + (n >= edge ? 1 : 0), c = n - which * d;
           const int r = which == 0 ? rq : rkv;
@@ -184,7 +189,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t 
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-          const int n = n0 + wn * (BN / 2) + j * 32 + gg * 8 + half * 4;
+          const int n = n0 + wn * WTN + j * 32 + gg * 8 + half * 4;
           if (!full_n && n >= g.Nout) continue;
           const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
           const uint2 gt = *reinterpret_cast<const uint2*>(gate + n);
@@ -204,7 +209,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t 
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-          const int n = n0 + wn * (BN / 2) + j * 32 + gg * 8 + half * 4;
+          const int n = n0 + wn * WTN + j * 32 + gg * 8 + half * 4;
           if (!full_n && n >= g.Nout) continue;
           const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
           uint2 w;
@@ -637,23 +642,40 @@ __device__ __forceinline__ SkTile sk_tile(const GemmArgs& g, int t, int tiles_m,
   return r;
 }
 
-template <int EPI, int BM, int BN, int BK, int STAGES>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_sk_kernel(GemmArgs g) {
+// Resident workgroups of a configuration: two per CU when they fit (4 waves,
+// <= 80 KiB LDS), else one.
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
+struct SkConfig {
+  static constexpr int kThreads = 64 * WGM * WGN;
+  static constexpr int kLds = STAGES * (BM + BN) * BK * 2;
+  static constexpr int kPerCu = (kThreads == 256 && kLds <= 80 * 1024) ? 2 : 1;
+  static constexpr int kP = 256 * kPerCu;
+  static constexpr size_t kTileBytes = static_cast<size_t>(BM) * BN * 4;
+};
+
+template <int EPI, int BM, int BN, int BK, int STAGES, int WGM, int WGN>
+__global__ __launch_bounds__((SkConfig<BM, BN, BK, STAGES, WGM, WGN>::kThreads),
+                             (SkConfig<BM, BN, BK, STAGES, WGM, WGN>::kPerCu))
+void gemm_bf16_sk_kernel(GemmArgs g) {
+  using Cfg = SkConfig<BM, BN, BK, STAGES, WGM, WGN>;
+  constexpr int NT = Cfg::kThreads, NW = NT / 64;
   constexpr int CPR = BK / 8;
   constexpr int CHUNKS_A = BM * CPR, CHUNKS_B = BN * CPR;
-  constexpr int LOADS_A = CHUNKS_A / kGemmThreads;
-  constexpr int LOADS_B = CHUNKS_B / kGemmThreads;
+  constexpr int LOADS_A = CHUNKS_A / NT;
+  constexpr int LOADS_B = CHUNKS_B / NT;
   constexpr int LOADS = LOADS_A + LOADS_B;
-  constexpr int TI = BM / 64, TJ = BN / 64;
-  constexpr int F4 = TI * TJ * 4;                      // float4 partials per thread
-  static_assert(LOADS_A * kGemmThreads == CHUNKS_A && LOADS_B * kGemmThreads == CHUNKS_B, "tile/threads");
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;         // wave tile
+  constexpr int TI = WTM / 32, TJ = WTN / 32;
+  static_assert(LOADS_A * NT == CHUNKS_A && LOADS_B * NT == CHUNKS_B, "tile/threads");
+  static_assert(TI * 32 == WTM && TJ * 32 == WTN, "wave tile");
 
   const int B = g.M / g.rows_cap;
   int tiles_m = 0;
   for (int b = 0; b < B; ++b) tiles_m += (rows_of(g.k_eff, b, g.rows_cap) + BM - 1) / BM;
   const int tiles_n = (g.Nout + BN - 1) / BN;
   const int tiles = tiles_m * tiles_n;
-  const int P = g.sk_slots;
+  constexpr int P = Cfg::kP;
+  const int slots = static_cast<int>(min(g.sk_partial_bytes / Cfg::kTileBytes, static_cast<size_t>(2 * P)));
   const int ndp = (tiles / P) * P;        // tiles done one per workgroup
   const int r = tiles - ndp;              // tail tiles, split along K
   const int nk = g.K / BK;
@@ -663,7 +685,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_sk_kernel(GemmArgs 
     if (r == 0) return;
     // S minimising (rounds of r*S pieces) x (piece overhead + nk/S k-tiles), with
     // the pieces within the grid and the partial slots and >= kSkMinIters k-tiles each
-    const int room = min(static_cast<int>(gridDim.x) - ndp, 2 * P);
+    const int room = min(static_cast<int>(gridDim.x) - ndp, slots);
     const int smax = max(1, min(min(kSkMaxSplit, nk / kSkMinIters), room / r));
     float best = static_cast<float>((r + P - 1) / P) * static_cast<float>(kSkPieceCost + nk);
     for (int c = 2; c <= smax; ++c) {
@@ -685,7 +707,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_sk_kernel(GemmArgs 
   int* s_last = reinterpret_cast<int*>(&lds[STAGES - 1][CHUNKS_A + CHUNKS_B - 1]);   // clear of the row table
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WGN, wn = wid % WGN;
   const int half = lane >> 5, col = lane & 31;
   const bf16_t* A = static_cast<const bf16_t*>(g.a);
   const bf16_t* Wt = static_cast<const bf16_t*>(g.w);
@@ -708,7 +730,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_sk_kernel(GemmArgs 
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int il = i < LOADS_A ? i : i - LOADS_A;
-    const int c = (il * 4 + wid) * 64 + lane;
+    const int c = (il * NW + wid) * 64 + lane;
     const int row = c / CPR;
     const int kc = swz_kc<CPR>(row, c % CPR);
     if (i < LOADS_A) goff[i] = min(tl.m0 + row, g.M - 1) * K + kc * 8 + kk0 * BK;
@@ -719,7 +741,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_sk_kernel(GemmArgs 
     for (int i = 0; i < LOADS; ++i) {
       const bf16_t* src = (i < LOADS_A ? A : Wt) + goff[i] + kt * BK;
       const int il = i < LOADS_A ? i : i - LOADS_A;
-      uint4* dst = &lds[stage][(i < LOADS_A ? 0 : CHUNKS_A) + (il * 4 + wid) * 64];
+      uint4* dst = &lds[stage][(i < LOADS_A ? 0 : CHUNKS_A) + (il * NW + wid) * 64];
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
     }
   };
@@ -730,8 +752,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_sk_kernel(GemmArgs 
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
 
-  const int ra = wm * (BM / 2) + col;
-  const int rb = wn * (BN / 2) + col;
+  const int ra = wm * WTM + col;
+  const int rb = wn * WTN + col;
   const int n = kk1 - kk0;
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
@@ -771,9 +793,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_sk_kernel(GemmArgs 
   auto finish = [&]() {
     __syncthreads();   // every wave is done with the LDS stages
     int* tab = reinterpret_cast<int*>(&lds[0][0]);
-    fill_row_table<EPI, BM>(g, tl.m0, tab, tl.mend);
+    fill_row_table<EPI, BM, NT>(g, tl.m0, tab, tl.mend);
     __syncthreads();
-    tile_epilogue<EPI, BM, BN, TI, TJ>(g, acc, tl.m0, tl.n0, wm, wn, half, col, tab);
+    tile_epilogue<EPI, BM, BN, TI, TJ, WTM, WTN>(g, acc, tl.m0, tl.n0, wm, wn, half, col, tab);
   };
   if (S == 1) {
     finish();
@@ -793,7 +815,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_sk_kernel(GemmArgs 
       for (int v2 = 0; v2 < 8; ++v2) {
         const unsigned long long x = (static_cast<unsigned long long>(__float_as_uint(acc[i][j][2 * v2 + 1])) << 32) |
                                      __float_as_uint(acc[i][j][2 * v2]);
-        __hip_atomic_store(part + own + static_cast<size_t>(((i * TJ + j) * 8 + v2) * kGemmThreads + tid), x,
+        __hip_atomic_store(part + own + static_cast<size_t>(((i * TJ + j) * 8 + v2) * NT + tid), x,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       }
   // the stores have reached the coherence point before the arrival is counted
@@ -814,47 +836,67 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_sk_kernel(GemmArgs 
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
   for (int v = 0; v < S; ++v) {
     const unsigned long long* src = part + static_cast<size_t>(tt * S + v) * (BM * BN / 2);
-    unsigned long long p[F4 * 2];
-#pragma unroll
-    for (int q = 0; q < F4 * 2; ++q)
-      p[q] = __hip_atomic_load(src + q * kGemmThreads + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+      for (int j = 0; j < TJ; ++j) {
+        // one 32x32 block at a time keeps the loads' registers few
+        unsigned long long p[8];
+#pragma unroll
+        for (int v2 = 0; v2 < 8; ++v2)
+          p[v2] = __hip_atomic_load(src + static_cast<size_t>(((i * TJ + j) * 8 + v2) * NT + tid), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_SYSTEM);
 #pragma unroll
         for (int v2 = 0; v2 < 8; ++v2) {
-          const unsigned long long x = p[(i * TJ + j) * 8 + v2];
-          acc[i][j][2 * v2] += __uint_as_float(static_cast<unsigned>(x));
-          acc[i][j][2 * v2 + 1] += __uint_as_float(static_cast<unsigned>(x >> 32));
+          acc[i][j][2 * v2] += __uint_as_float(static_cast<unsigned>(p[v2]));
+          acc[i][j][2 * v2 + 1] += __uint_as_float(static_cast<unsigned>(p[v2] >> 32));
         }
+      }
   }
   finish();
 }
+
+#ifndef WAMC_GEMM_BIG
+#define WAMC_GEMM_BIG 1
+#endif
+// 256x256 tiles (8 waves, one workgroup per CU) for the work-balanced path
+// when there are at least two full rounds of them (measured: 36-39 % of peak
+// against 33-36 % for 128x128 tiles at 16k rows; slower at 2.5-4.7k rows,
+// where the tile count leaves a large ragged round)
+constexpr bool kGemmBig = WAMC_GEMM_BIG != 0;
+using SkSmall = SkConfig<128, 128, 64, 2, 2, 2>;
+using SkBig = SkConfig<256, 256, 32, 4, 2, 4>;
 
 GemmScratch gemm_scratch(int B, int rows_cap, int d, int F) {
   GemmScratch s{};
   if (rows_cap <= 0) return s;
   const int widest = max(3 * d, F);
-  s.slots = kGemmSkSlotsMax;
+  // arrival counters: one per output tile of the smallest tile at rows_cap rows
   s.counters = B * ((rows_cap + 127) / 128) * ((widest + 127) / 128);
-  s.partial_bytes = static_cast<size_t>(2) * s.slots * 128 * 128 * sizeof(float);
   s.counter_bytes = static_cast<size_t>(s.counters) * sizeof(int);
+  // partial tiles: at most two rounds of resident workgroups' worth of pieces
+  // (fewer for small shapes: tiles x the most pieces per tile)
+  const size_t small = std::min<size_t>(2 * SkSmall::kP, static_cast<size_t>(s.counters) * kSkMaxSplit) *
+                       SkSmall::kTileBytes;
+  const size_t tiles_big = static_cast<size_t>(B) * ((rows_cap + 255) / 256) * ((widest + 255) / 256);
+  const size_t big = kGemmBig ? std::min<size_t>(2 * SkBig::kP, tiles_big * kSkMaxSplit) * SkBig::kTileBytes : 0;
+  s.partial_bytes = std::max(small, big);
   return s;
 }
 
-template <int BM, int BN, int BK, int STAGES>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
 static void launch_sk(GemmEpi epi, const GemmArgs& g, hipStream_t s) {
+  using Cfg = SkConfig<BM, BN, BK, STAGES, WGM, WGN>;
   const int B = g.M / g.rows_cap;
   const long long tiles_cap = static_cast<long long>(B) * ((g.rows_cap + BM - 1) / BM) * ((g.Nout + BN - 1) / BN);
-  const int P = g.sk_slots;
   // one workgroup per tile at the most rows; at least P so few tiles can be split
-  const unsigned grid = static_cast<unsigned>(max(tiles_cap, static_cast<long long>(P)));
+  const unsigned grid = static_cast<unsigned>(std::max<long long>(tiles_cap, Cfg::kP));
+  constexpr int NT = Cfg::kThreads;
   switch (epi) {
-    case EPI_QKV: gemm_bf16_sk_kernel<EPI_QKV, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
-    case EPI_RESID_OUT: gemm_bf16_sk_kernel<EPI_RESID_OUT, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
-    case EPI_RESID_DOWN: gemm_bf16_sk_kernel<EPI_RESID_DOWN, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
-    case EPI_GELU: gemm_bf16_sk_kernel<EPI_GELU, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
+    case EPI_QKV: gemm_bf16_sk_kernel<EPI_QKV, BM, BN, BK, STAGES, WGM, WGN><<<grid, NT, 0, s>>>(g); break;
+    case EPI_RESID_OUT: gemm_bf16_sk_kernel<EPI_RESID_OUT, BM, BN, BK, STAGES, WGM, WGN><<<grid, NT, 0, s>>>(g); break;
+    case EPI_RESID_DOWN: gemm_bf16_sk_kernel<EPI_RESID_DOWN, BM, BN, BK, STAGES, WGM, WGN><<<grid, NT, 0, s>>>(g); break;
+    case EPI_GELU: gemm_bf16_sk_kernel<EPI_GELU, BM, BN, BK, STAGES, WGM, WGN><<<grid, NT, 0, s>>>(g); break;
   }
 }
 
@@ -956,10 +998,15 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   const long long t128 = static_cast<long long>((g.M + 127) / 128) * ((g.Nout + 127) / 128);
   const bool dtl_ok = bf16 && g.K % 64 == 0 && !kForceGeneric;
   const bool use_ks2 = dtl_ok && kSplitK && t128 <= 256 && g.K >= 2 * 64 && (g.K < 4096 || t128 > 128);
-  const bool use_sk = dtl_ok && WAMC_GEMM_SK && g.sk_partial && g.sk_counters && g.sk_slots > 0 &&
-                      g.sk_slots <= kGemmSkSlotsMax;
-  if (!use_ks2 && use_sk) {
-    launch_sk<128, 128, 64, 2>(epi, g, s);
+  const bool use_sk = dtl_ok && WAMC_GEMM_SK && g.sk_partial && g.sk_counters &&
+                      g.sk_partial_bytes >= SkSmall::kTileBytes;
+  // 256-wide tiles need d >= 256 (a QKV tile crosses at most one of the Q|K|V edges)
+  const long long t256 = static_cast<long long>((g.M + 255) / 256) * ((g.Nout + 255) / 256);
+  const bool big = kGemmBig && g.d_model >= 256 && g.sk_partial_bytes >= SkBig::kTileBytes && t256 >= 2 * SkBig::kP;
+  if (!use_ks2 && use_sk && big) {
+    launch_sk<256, 256, 32, 4, 2, 4>(epi, g, s);
+  } else if (!use_ks2 && use_sk) {
+    launch_sk<128, 128, 64, 2, 2, 2>(epi, g, s);
   } else if (use_ks2) {
     const unsigned grid = static_cast<unsigned>(t128);
     switch (epi) {

@@ -113,17 +113,16 @@ struct GemmArgs {
   // EPI_GELU: g[m, c] = act(gelu(acc + bias[c]))
   void* g_out;
   // scratch of the work-balanced bf16 path (nullable: plain tiles are used)
-  float* sk_partial;    // [2 * sk_slots, 128 * 128] f32 partial tiles
-  int* sk_counters;     // per-tile arrival counters, zero between launches
-  int sk_slots;         // workgroups that share the split tiles (<= kGemmSkSlotsMax)
+  float* sk_partial;        // f32 partial tiles of split output tiles
+  size_t sk_partial_bytes;  // its size (bounds the number of pieces)
+  int* sk_counters;         // per-tile arrival counters, zero between launches
 };
 hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer);
 
 // Scratch of the work-balanced bf16 GEMM for one layer's four projections.
-constexpr int kGemmSkSlotsMax = 512;   // two 256-thread workgroups on each of 256 CUs
 struct GemmScratch {
   size_t partial_bytes, counter_bytes;
-  int slots, counters;
+  int counters;
 };
 GemmScratch gemm_scratch(int B, int rows_cap, int d, int F);
 

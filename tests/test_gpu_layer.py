@@ -76,13 +76,14 @@ def test_refresh_layer_parity(name):
 
 
 @pytest.mark.parametrize("m,spare", [(37, False), (37, True), (300, True), (1100, False), (1100, True),
-                                     (2458, False)])
+                                     (2458, False), (4096, False)])
 def test_refresh_layer_wide(m, spare):
     """The d=1536, FFN 8960 layer over N=4096 cached tokens with m refreshed
     rows, the launch sized for the rows (rows_cap = m) or for every token
     (rows_cap = N, k_eff = m read on the device): covers the GEMM schedules
-    that split K over several workgroups and the one-tile-per-workgroup
-    rounds."""
+    that split K over several workgroups, the one-tile-per-workgroup
+    rounds, and (m = N: 560 tiles of 256x256 in the MLP up projection) the
+    large-tile schedule with a split last round."""
     wl = W.preset("c2_layer")
     r = W.make_rollout(wl, chunks=1)
     prec = O.Precision(wl.dtype)
