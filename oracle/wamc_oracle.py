@@ -31,8 +31,11 @@ Readings where the pages are silent or garbled (the display equations of
 WAM-Cache §4.2-4.4 are lost in the text):
 
 * one combined score = w_a * P_i / (L*H*A) + w_s * U_i / sum(U), with a fixed
-  requested count k, instead of the page's union of two budgeted rank
-  selections (a second rule, not built here);
+  requested count k (the default rule);
+* the page's own rule, the union of two budgeted rank selections (§1, §4.3,
+  §5.3): the ceil(b_a*N) tokens of largest attention mass, the ceil(b_s*N)
+  tokens of largest surprise, and the forced tokens, each token counted once
+  (`select_union`);
 * P_i = sum over layers, heads and action queries of the row-softmax
   probability of token i, computed from the supplied queries against the
   cache as it stands before this chunk's refresh;
@@ -297,6 +300,43 @@ def select(score_f32: np.ndarray, age: np.ndarray, k: int, G: int,
     return idx, k_eff, ages_after(age, idx), n_forced
 
 
+def budget_count(b: float, N: int) -> int:
+    """ceil(b * N) computed exactly for a budget given as a decimal fraction
+    (0.4 * 4680 is 1872, not 1873 as float rounding would give)."""
+    from fractions import Fraction
+    if b < 0:
+        raise ValueError("budget must be >= 0")
+    return min(N, math.ceil(Fraction(repr(float(b))) * N))
+
+
+def top_by(values_f32: np.ndarray, n: int) -> np.ndarray:
+    """The n tokens with the largest value, ascending: larger value first,
+    equal values -> lower index first, NaN below every number, -0.0 == +0.0."""
+    N = len(values_f32)
+    n = max(0, min(n, N))
+    keys = [rank_key(False, float(values_f32[i]), i) for i in range(N)]
+    order = sorted(range(N), key=lambda i: keys[i], reverse=True)
+    return np.array(sorted(order[:n]), dtype=np.int32)
+
+
+def select_union(mass_f32: np.ndarray, surprise_f32: np.ndarray, age: np.ndarray, n_attn: int,
+                 n_surprise: int, G: int):
+    """The page's refresh rule (WAM-Cache §1 and §4.3: union of the
+    action-attention set and the latent-surprise set; §4.4: plus every token
+    whose age reached the bound; §5.3: tokens chosen by both signals are
+    counted once).  P_t = top n_attn tokens by attention mass, S_t = top
+    n_surprise by surprise, F_t = {age >= G}; the refresh set is
+    P_t | S_t | F_t in ascending token order, k_eff = its size (variable);
+    ages 0 on the set, +1 elsewhere.  Returns (idx, k_eff, new_age, n_forced)."""
+    N = len(mass_f32)
+    forced = np.flatnonzero(np.asarray(age) >= G)
+    R = set(top_by(mass_f32, n_attn).tolist()) | set(top_by(surprise_f32, n_surprise).tolist())
+    R |= set(forced.tolist())
+    idx = np.array(sorted(R), dtype=np.int32)
+    assert len(idx) <= N
+    return idx, len(idx), ages_after(age, idx), int(len(forced))
+
+
 def ages_after(age: np.ndarray, idx: np.ndarray) -> np.ndarray:
     """Age update for a refresh set: refreshed tokens restart at 0, all others
     have been reused one more chunk."""
@@ -323,13 +363,18 @@ class ChunkResult:
 def refresh_chunk(state: State, z: np.ndarray, qa: Optional[np.ndarray], weights: Sequence,
                   k: int, G: int, n_heads: int, eps: float, w_attn: float, w_surprise: float,
                   prec: Precision, idx_override: Optional[np.ndarray] = None,
-                  mass: Optional[np.ndarray] = None, cap: Optional[int] = None) -> ChunkResult:
+                  mass: Optional[np.ndarray] = None, cap: Optional[int] = None,
+                  union: Optional[tuple] = None) -> ChunkResult:
     """Score against the current cache, select, gather the refreshed rows
     (and store their reference embedding), then run every layer on them.
-    `state` is updated in place."""
+    `union` = (n_attn, n_surprise) selects with the union rule instead of the
+    fixed-k combined score (k is then ignored).  `state` is updated in place."""
     s, P, U = score(z, state.zref, qa, state.K, n_heads, w_attn, w_surprise, prec, mass,
                     n_action=None if qa is None else qa.shape[1])
-    if idx_override is None:
+    if idx_override is None and union is not None:
+        idx, k_eff, age, n_forced = select_union(np.asarray(P, dtype=np.float32), np.asarray(U, dtype=np.float32),
+                                                 state.age, union[0], union[1], G)
+    elif idx_override is None:
         idx, k_eff, age, n_forced = select(s, state.age, k, G, cap)
     else:
         idx = np.array(sorted(set(int(i) for i in idx_override)), dtype=np.int32)

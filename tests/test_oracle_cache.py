@@ -183,3 +183,28 @@ def test_supplied_mass_matches_computed_mass():
     assert np.array_equal(s, s2)
     with pytest.raises(ValueError):
         O.score(r.z[0][1], st.zref, None, st.K, wl.n_heads, wl.w_attn, wl.w_surprise, prec, mass=P)
+
+
+def test_union_rule_chunk():
+    """The union rule inside a chunk: the refresh set is the union of the
+    mass and surprise top sets and the forced tokens of the chunk's own P and
+    U; a budget covering every token equals the dense prefill bitwise."""
+    wl, r, prec = _setup()
+    N = wl.n_tokens
+    st, _ = O.dense_prefill(r.z[0][0], r.weights, wl.n_heads, wl.ln_eps, prec)
+    st.age = r.ages0[0].astype(np.int64) + 1
+    age0 = st.age.copy()
+    na, ns = O.budget_count(0.4, N), O.budget_count(0.1, N)
+    res = O.refresh_chunk(st, r.z[0][1], r.qa[0][1], r.weights, 0, wl.age_bound, wl.n_heads, wl.ln_eps,
+                          wl.w_attn, wl.w_surprise, prec, union=(na, ns))
+    want = set(O.top_by(res.mass.astype(np.float32), na).tolist()) | \
+        set(O.top_by(res.surprise.astype(np.float32), ns).tolist()) | set(np.flatnonzero(age0 >= wl.age_bound).tolist())
+    assert res.idx.tolist() == sorted(want) and res.k_eff == len(want)
+    assert (st.age <= wl.age_bound).all()
+    # budgets covering every token: the dense prefill of the new frame, bitwise
+    res = O.refresh_chunk(st, r.z[0][2], r.qa[0][2], r.weights, 0, wl.age_bound, wl.n_heads, wl.ln_eps,
+                          wl.w_attn, wl.w_surprise, prec, union=(N, 0))
+    ref, outs = O.dense_prefill(r.z[0][2], r.weights, wl.n_heads, wl.ln_eps, prec)
+    assert res.k_eff == N
+    assert np.array_equal(st.K, ref.K) and np.array_equal(st.V, ref.V)
+    assert all(np.array_equal(a, b) for a, b in zip(res.outs, outs))
