@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--plateau", action="store_true",
                     help="one-layer refresh latency vs refreshed rows, stepped every 32 rows (one JSON line)")
     ap.add_argument("--sweep-layers", type=int, default=30, help="layers of the stack used by --sweep")
+    ap.add_argument("--union", action="store_true",
+                    help="the pages' union rule on the 30-layer stack at budgets (b_a, b_s) = (0.4, 0.1) and "
+                         "(0.6, 0.1), G = 2 (one JSON line each)")
     return ap.parse_args()
 
 
@@ -216,6 +219,54 @@ def run_sweep(args):
         del eng
 
 
+def run_union(args):
+    """The union refresh rule (top ceil(b_a N) by attention mass, top
+    ceil(b_s N) by surprise, forced tokens; WAM-Cache §1, §4.3, §4.4) on the
+    30-layer stack shapes with G = 2: a dense chunk, then 15 refresh chunks;
+    ms per chunk over chunks 2..15, the recompute ratio rho = mean k_eff / N
+    (WAM-Cache §5.3) and the speedup against its bound 1/rho (§5.2)."""
+    import torch
+    from sparse_kv_refresh_amd import inputs as W
+    from sparse_kv_refresh_amd import wamc
+    base = W.preset("c3_stack", n_layers=args.sweep_layers, age_bound=2)
+    T = base.chunks
+    r = W.make_rollout(base, chunks=T)
+    dev = "cuda:0"
+    weights = wamc.Engine.upload_weights(r.weights, torch.bfloat16, dev)
+    N = base.n_tokens
+    zs = [torch.from_numpy(r.z[0][t]).to(dev, torch.bfloat16)[None].contiguous() for t in range(T)]
+    qs = [None] + [torch.from_numpy(r.qa[0][t]).to(dev, torch.bfloat16)[:, None].contiguous() for t in range(1, T)]
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * T)]
+    eng = wamc.Engine(wamc.dims_for(base), weights, N, dev)
+    for b_a, b_s in ((0.4, 0.1), (0.6, 0.1)):
+        na, ns = wamc.budget_rows(b_a, N), wamc.budget_rows(b_s, N)
+        eng.dense(zs[0])
+        keffs = []
+        for t in range(1, T):
+            ev[2 * t].record(stream)
+            eng.chunk_union(zs[t], qs[t], na, ns, stream=stream)
+            ev[2 * t + 1].record(stream)
+            keffs.append(eng.k_eff[0].clone())
+        torch.cuda.synchronize()
+        keffs = [int(k) for k in keffs]
+        ms = [ev[2 * t].elapsed_time(ev[2 * t + 1]) for t in range(2, T)]
+        dms = []
+        for _ in range(3):
+            ev[0].record(stream)
+            eng.dense(zs[T - 1], stream=stream)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            dms.append(ev[0].elapsed_time(ev[1]))
+        rho = float(np.mean(keffs[1:])) / N
+        mean_ms = float(np.mean(ms))
+        print(json.dumps({"union": {"b_a": b_a, "b_s": b_s, "n_attn": na, "n_surprise": ns}, "age_bound": 2,
+                          "layers": base.n_layers, "n_tokens": N, "k_eff_per_chunk": keffs, "rho": rho,
+                          "ms_per_chunk": mean_ms, "dense_ms": float(np.median(dms)),
+                          "speedup_vs_dense": float(np.median(dms)) / mean_ms, "speedup_bound": 1.0 / rho}),
+              flush=True)
+
+
 def run_plateau(args):
     """One d=1536 layer over N=4680 cached tokens: wamc_refresh_layer latency
     as the number of refreshed rows m grows by 32, once with the launch sized
@@ -289,6 +340,8 @@ def main():
         return run_sweep(args)
     if args.plateau:
         return run_plateau(args)
+    if args.union:
+        return run_union(args)
 
     import torch
     from sparse_kv_refresh_amd import inputs as W

@@ -193,6 +193,35 @@ int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const 
                        float* score_out, float* layer_out, int32_t rows_cap, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* The pages' own refresh rule, the union of two budgeted rank selections
+ * (WAM-Cache §1 and §4.3: the tokens the action expert attended to most in
+ * the preceding chunk and the tokens whose input embedding moved most since
+ * their last refresh; §4.4: plus every token whose age reached the bound;
+ * §5.3: a token chosen by several parts counts once):
+ *   refresh set = top n_attn tokens by mass  |  top n_surprise tokens by
+ *                 surprise  |  {i : age_i >= G},  k_eff = its size (variable)
+ * ranked as in wamc_select (larger first, equal values to the lower index,
+ * NaN below every number, -0 == +0); idx ascending, rest -1; ages as in
+ * wamc_select.  n_attn = ceil(b_a N), n_surprise = ceil(b_s N) for budget
+ * fractions (b_a, b_s), each in [0, N].  mass, surprise: [B, N] f32 (the
+ * per-token P and U of wamc_score).  The set can hold every token, so there
+ * is no row cap here. */
+int wamc_select_union(const wamc_dims* dims, const float* mass, const float* surprise, int32_t* age,
+                      int32_t n_attn, int32_t n_surprise, int32_t* idx, int32_t* k_eff, int32_t* n_forced,
+                      void* stream);
+
+/* wamc_prefill_chunk with the union rule in place of the fixed-k selection:
+ * P and U of this chunk (P from q_act, or mass_in when given), then
+ * wamc_select_union, wamc_gather and every layer on the k_eff rows.
+ * rows_cap must be N (the union can hold every token); the kernels size
+ * their work from k_eff on the device, so the spare capacity costs no time.
+ * Other arguments as in wamc_prefill_chunk. */
+int wamc_prefill_chunk_union(const wamc_dims* dims, const wamc_layer_w* layers, const void* z, void* zref,
+                             const void* q_act, const float* mass_in, void* k_cache, void* v_cache,
+                             int32_t* age, int32_t n_attn, int32_t n_surprise, int32_t* idx_out,
+                             int32_t* k_eff_out, float* layer_out, int32_t rows_cap, void* ws,
+                             size_t ws_bytes, void* stream);
+
 /* Dense prefill (WAM-Cache §4.1: the chunk at episode onset): every token
  * through every layer, K/V written for all N tokens, age <- 0, zref <- z.
  * Also the speedup baseline.  layer_out (nullable): [L,B,N,d] f32. */

@@ -412,6 +412,36 @@ hipError_t run_score(const wamc_dims* d, const void* z, const void* zref, const 
                              active_timer());
 }
 
+
+// Gather the selected rows (fused with layer 0's first LayerNorm when d fits)
+// and run every layer on them.
+hipError_t run_refresh_rows(const wamc_dims* dims, const wamc_layer_w* layers, const void* z, void* zref,
+                            void* k_cache, void* v_cache, const int32_t* idx, const int32_t* k_eff, float* layer_out,
+                            int32_t rows_cap, void* ws, const WsLayout& L, hipStream_t s) {
+  KernelTimer* tm = active_timer();
+  const bool bf16 = dims->dtype == WAMC_BF16;
+  const int B = dims->batch, N = dims->n_tokens, D = dims->d_model;
+  float* x = at<float>(ws, L.x);
+  const size_t es = act_size(dims);
+  const bool fuse_ln = D <= 4096;
+  hipError_t e;
+  if (fuse_ln)
+    e = launch_gather_ln(bf16, z, zref, idx, k_eff, B, N, D, rows_cap, x, nullptr, offset(layers[0].mod, 0, es),
+                         offset(layers[0].mod, D, es), dims->ln_eps, at<char>(ws, L.hbuf), counter_clear(ws, L), s, tm);
+  else
+    e = launch_gather(bf16, z, zref, idx, k_eff, B, N, D, rows_cap, x, nullptr, counter_clear(ws, L), s, tm);
+  const size_t layer_elems = static_cast<size_t>(B) * N * D;
+  const size_t out_elems = static_cast<size_t>(B) * rows_cap * D;
+  for (int l = 0; l < dims->n_layers && e == hipSuccess; ++l) {
+    const float* xin = (layer_out && l > 0) ? layer_out + (l - 1) * out_elems : x;
+    float* xout = layer_out ? layer_out + l * out_elems : x;
+    void* kc = static_cast<char*>(k_cache) + l * layer_elems * es;
+    void* vc = static_cast<char*>(v_cache) + l * layer_elems * es;
+    e = run_layer(dims, &layers[l], xin, xout, idx, k_eff, rows_cap, kc, vc, ws, L, s, l == 0 && fuse_ln);
+  }
+  return e;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -605,24 +635,81 @@ int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const 
     }
   }
   if (e != hipSuccess) return hip_status(fn, e, s);
-  float* x = at<float>(ws, L.x);
-  const size_t es = act_size(dims);
-  const bool fuse_ln = D <= 4096;
-  if (fuse_ln)
-    e = launch_gather_ln(bf16, z, zref, idx_out, k_eff_out, B, N, D, rows_cap, x, nullptr, offset(layers[0].mod, 0, es),
-                         offset(layers[0].mod, D, es), dims->ln_eps, at<char>(ws, L.hbuf), counter_clear(ws, L), s, tm);
-  else
-    e = launch_gather(bf16, z, zref, idx_out, k_eff_out, B, N, D, rows_cap, x, nullptr, counter_clear(ws, L), s, tm);
-  const size_t layer_elems = static_cast<size_t>(B) * N * D;
-  const size_t out_elems = static_cast<size_t>(B) * rows_cap * D;
-  for (int l = 0; l < dims->n_layers && e == hipSuccess; ++l) {
-    const float* xin = (layer_out && l > 0) ? layer_out + (l - 1) * out_elems : x;
-    float* xout = layer_out ? layer_out + l * out_elems : x;
-    void* kc = static_cast<char*>(k_cache) + l * layer_elems * es;
-    void* vc = static_cast<char*>(v_cache) + l * layer_elems * es;
-    e = run_layer(dims, &layers[l], xin, xout, idx_out, k_eff_out, rows_cap, kc, vc, ws, L, s, l == 0 && fuse_ln);
+  return hip_status(fn, run_refresh_rows(dims, layers, z, zref, k_cache, v_cache, idx_out, k_eff_out, layer_out,
+                                         rows_cap, ws, L, s), s);
+}
+
+int wamc_select_union(const wamc_dims* dims, const float* mass, const float* surprise, int32_t* age,
+                      int32_t n_attn, int32_t n_surprise, int32_t* idx, int32_t* k_eff, int32_t* n_forced,
+                      void* stream) {
+  const char* fn = "wamc_select_union";
+  g_last_error.clear();
+  int st = check_dims(fn, dims);
+  if (st) return st;
+  REQUIRE_PTR(mass);
+  REQUIRE_PTR(surprise);
+  REQUIRE_PTR(age);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(k_eff);
+  OPT_PTR(n_forced);
+  const int N = dims->n_tokens;
+  if (n_attn < 0 || n_attn > N || n_surprise < 0 || n_surprise > N)
+    return fail(WAMC_ERR_ARG, "%s: n_attn (%d) and n_surprise (%d) must be in [0, N=%d]", fn, n_attn, n_surprise, N);
+  if ((st = check_device(fn))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  {
+    TimedLaunch t(active_timer(), "select", s);
+    e = launch_select_union(mass, surprise, age, dims->batch, N, n_attn, n_surprise, dims->age_bound, idx, k_eff,
+                            n_forced, s);
   }
   return hip_status(fn, e, s);
+}
+
+int wamc_prefill_chunk_union(const wamc_dims* dims, const wamc_layer_w* layers, const void* z, void* zref,
+                             const void* q_act, const float* mass_in, void* k_cache, void* v_cache,
+                             int32_t* age, int32_t n_attn, int32_t n_surprise, int32_t* idx_out,
+                             int32_t* k_eff_out, float* layer_out, int32_t rows_cap, void* ws,
+                             size_t ws_bytes, void* stream) {
+  const char* fn = "wamc_prefill_chunk_union";
+  g_last_error.clear();
+  int st = check_dims(fn, dims);
+  if (st) return st;
+  if (!layers) return fail(WAMC_ERR_ARG, "%s: layers is NULL", fn);
+  for (int l = 0; l < dims->n_layers; ++l)
+    if ((st = check_layer_w(fn, &layers[l]))) return st;
+  REQUIRE_PTR(z);
+  REQUIRE_PTR(zref);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(age);
+  REQUIRE_PTR(idx_out);
+  REQUIRE_PTR(k_eff_out);
+  OPT_PTR(layer_out);
+  OPT_PTR(mass_in);
+  const int N = dims->n_tokens;
+  if (n_attn < 0 || n_attn > N || n_surprise < 0 || n_surprise > N)
+    return fail(WAMC_ERR_ARG, "%s: n_attn (%d) and n_surprise (%d) must be in [0, N=%d]", fn, n_attn, n_surprise, N);
+  if (rows_cap != N) return fail(WAMC_ERR_ARG, "%s: rows_cap (%d) must be N (%d)", fn, rows_cap, N);
+  if (!mass_in) {
+    REQUIRE_PTR(q_act);
+    if ((st = check_action(fn, dims))) return st;
+  }
+  const WsLayout L = ws_layout(dims, rows_cap);
+  if (!ws || ws_bytes < L.total) return fail(WAMC_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, L.total);
+  OPT_PTR(ws);
+  if ((st = check_device(fn))) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = run_score_partials(dims, z, zref, q_act, k_cache, mass_in, ws, L, s);
+  if (e == hipSuccess) {
+    TimedLaunch t(active_timer(), "select", s);
+    e = launch_select_union(at<float>(ws, L.mass_tmp), at<float>(ws, L.surp_tmp), age, dims->batch, N, n_attn,
+                            n_surprise, dims->age_bound, idx_out, k_eff_out, nullptr, s);
+  }
+  if (e != hipSuccess) return hip_status(fn, e, s);
+  return hip_status(fn, run_refresh_rows(dims, layers, z, zref, k_cache, v_cache, idx_out, k_eff_out, layer_out,
+                                         rows_cap, ws, L, s), s);
 }
 
 int wamc_dense_prefill(const wamc_dims* dims, const wamc_layer_w* layers, const void* z, void* zref,

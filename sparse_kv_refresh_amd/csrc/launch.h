@@ -43,6 +43,10 @@ struct ScoreInputs {
 };
 hipError_t launch_select_scored(const ScoreInputs& si, int32_t* age, int B, int N, int k, int G, int rows_cap,
                                 int32_t* idx, int32_t* k_eff, int32_t* n_forced, hipStream_t s);
+// union rule: top n_attn by mass, top n_surprise by surprise, forced; k_eff = union size
+hipError_t launch_select_union(const float* mass, const float* surprise, int32_t* age, int B, int N, int n_attn,
+                               int n_surprise, int G, int32_t* idx, int32_t* k_eff, int32_t* n_forced,
+                               hipStream_t s);
 hipError_t launch_ages_from_set(const int32_t* idx_in, const int32_t* k_in, int B, int N, int rows_cap,
                                 int32_t* idx_out, int32_t* k_out, int32_t* age, hipStream_t s);
 

@@ -39,147 +39,103 @@ __device__ __forceinline__ uint64_t rank_key(float s, bool forced, int i) {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 
-// KPT = keys held per thread in registers (N <= KPT * 1024); 0 = recompute
-// the keys from global memory in every pass (any N).
-// SCORED: the scores are formed here from P, U and the U partials (the last
-// scoring step fused in) and written to si.score_out; otherwise read.
-template <int KPT, bool SCORED>
-__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
-    const float* __restrict__ score, ScoreInputs si, int32_t* __restrict__ age, int N, int k, int G,
-    int rows_cap, int32_t* __restrict__ idx, int32_t* __restrict__ k_eff_out,
-    int32_t* __restrict__ n_forced_out) {
-  const int b = blockIdx.x;
+struct SelShared {
+  uint32_t hist[256];
+  int red[kSelWaves];
+  uint32_t sel, rem;
+  float red4[4];
+};
+
+// The count-th largest key (1 <= count < N) by an MSB-first radix select:
+// 8 passes of an 8-bit digit histogram in LDS, the bucket found by a
+// wave-wide suffix scan.  key_of(j, i) gives the key of token i, held in
+// register slot j when KPT > 0 (i = tid + j*1024); with KPT == 0 it is
+// recomputed for every i.  All threads of the block call it.
+template <int KPT, class KeyOf>
+__device__ uint64_t radix_threshold(KeyOf key_of, int N, uint32_t count, SelShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const size_t eoff = static_cast<size_t>(b) * N;
-  age += eoff;
-  idx += eoff;
-
-  __shared__ uint32_t hist[256];
-  __shared__ int red[kSelWaves];
-  __shared__ uint32_t s_sel, s_rem;
-  __shared__ float red4[4];
-
-  float total = 0.f;
-  if constexpr (SCORED) total = usum_total(si.usum + static_cast<size_t>(b) * si.nblocks, si.nblocks, red4);
-  auto get_score = [&](int i) -> float {
-    if constexpr (SCORED)
-      return combine_score(si.mass[eoff + i], si.surprise[eoff + i], total, si.w_attn_norm, si.w_surprise);
-    else
-      return score[eoff + i];
-  };
-
-  constexpr int NK = KPT > 0 ? KPT : 1;
-  uint64_t keys[NK];
-  int nf = 0;
-  if constexpr (KPT > 0) {
+  uint64_t prefix = 0;
+  uint32_t remaining = count;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    const uint64_t hi_mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
+    if (tid < 256) sh.hist[tid] = 0;
+    __syncthreads();
+    if constexpr (KPT > 0) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int i = tid + j * kSelThreads;
-      keys[j] = 0;
-      if (i < N) {
-        const bool f = age[i] >= G;
-        nf += f;
-        const float sc = get_score(i);
-        if constexpr (SCORED) si.score_out[eoff + i] = sc;
-        keys[j] = rank_key(sc, f, i);
-      }
-    }
-  } else {
-    keys[0] = 0;
-    for (int i = tid; i < N; i += kSelThreads) {
-      nf += age[i] >= G;
-      if constexpr (SCORED) si.score_out[eoff + i] = get_score(i);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) nf += __shfl_xor(nf, o, kWave);
-  if (lane == 0) red[wid] = nf;
-  __syncthreads();
-  int n_forced = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) n_forced += red[w];
-  __syncthreads();
-
-  int ke = k > n_forced ? k : n_forced;
-  if (ke > rows_cap) ke = rows_cap;
-  const bool take_all = ke >= N, take_none = ke <= 0;
-
-  uint64_t thr = 0;
-  if (!take_all && !take_none) {
-    uint64_t prefix = 0;
-    uint32_t remaining = static_cast<uint32_t>(ke);
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      const uint64_t hi_mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      if constexpr (KPT > 0) {
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-          const int i = tid + j * kSelThreads;
-          if (i < N && (keys[j] & hi_mask) == prefix)
-            atomicAdd(&hist[(keys[j] >> shift) & 255u], 1u);
-        }
-      } else {
-        for (int i = tid; i < N; i += kSelThreads) {
-          const uint64_t key = rank_key(get_score(i), age[i] >= G, i);
-          if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      for (int j = 0; j < KPT; ++j) {
+        const int i = tid + j * kSelThreads;
+        if (i < N) {
+          const uint64_t key = key_of(j, i);
+          if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
         }
       }
-      __syncthreads();
-      if (wid == 0) {
-        // lane l owns bins 4l..4l+3; suffix sums find the bucket that holds
-        // the remaining-th largest key
-        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
-        const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-        const uint32_t s = h0 + h1 + h2 + h3;
-        uint32_t suf = s;
+    } else {
+      for (int i = tid; i < N; i += kSelThreads) {
+        const uint64_t key = key_of(0, i);
+        if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    if (wid == 0) {
+      // lane l owns bins 4l..4l+3; suffix sums find the bucket that holds
+      // the remaining-th largest key
+      const uint32_t h0 = sh.hist[4 * lane], h1 = sh.hist[4 * lane + 1];
+      const uint32_t h2 = sh.hist[4 * lane + 2], h3 = sh.hist[4 * lane + 3];
+      const uint32_t s = h0 + h1 + h2 + h3;
+      uint32_t suf = s;
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const uint32_t v = __shfl_down(suf, o, kWave);
-          if (lane + o < kWave) suf += v;
-        }
-        const uint32_t above = suf - s;
-        if (above < remaining && remaining <= suf) {
-          uint32_t c = above;
-          uint32_t sel;
-          if (c + h3 >= remaining) {
-            sel = 4 * lane + 3;
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t v = __shfl_down(suf, o, kWave);
+        if (lane + o < kWave) suf += v;
+      }
+      const uint32_t above = suf - s;
+      if (above < remaining && remaining <= suf) {
+        uint32_t c = above;
+        uint32_t sel;
+        if (c + h3 >= remaining) {
+          sel = 4 * lane + 3;
+        } else {
+          c += h3;
+          if (c + h2 >= remaining) {
+            sel = 4 * lane + 2;
           } else {
-            c += h3;
-            if (c + h2 >= remaining) {
-              sel = 4 * lane + 2;
+            c += h2;
+            if (c + h1 >= remaining) {
+              sel = 4 * lane + 1;
             } else {
-              c += h2;
-              if (c + h1 >= remaining) {
-                sel = 4 * lane + 1;
-              } else {
-                c += h1;
-                sel = 4 * lane;
-              }
+              c += h1;
+              sel = 4 * lane;
             }
           }
-          s_sel = sel;
-          s_rem = remaining - c;
         }
+        sh.sel = sel;
+        sh.rem = remaining - c;
       }
-      __syncthreads();
-      prefix |= static_cast<uint64_t>(s_sel) << shift;
-      remaining = s_rem;
     }
-    thr = prefix;
+    __syncthreads();
+    prefix |= static_cast<uint64_t>(sh.sel) << shift;
+    remaining = sh.rem;
   }
+  return prefix;
+}
 
-  // ascending-order compaction and age update, one 1024-token tile at a time
+// Ascending-order compaction of the tokens with flag_of(j, i) set into idx,
+// ages reset on the set and +1 elsewhere; returns the set size.  One
+// 1024-token tile at a time with a block-wide ballot/popcount scan.
+template <int KPT, class FlagOf>
+__device__ int compact_set(FlagOf flag_of, int N, int32_t* __restrict__ idx, int32_t* __restrict__ age,
+                           SelShared& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   int base = 0;
-  auto compact = [&](int i, bool flag) {
+  auto tile = [&](int i, bool flag) {
     const uint64_t ball = __ballot(flag);
     const int wpre = __popcll(ball & ((1ull << lane) - 1ull));
-    if (lane == 0) red[wid] = __popcll(ball);
+    if (lane == 0) sh.red[wid] = __popcll(ball);
     __syncthreads();
     int off = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) {
-      const int c = red[w];
+      const int c = sh.red[w];
       off += w < wid ? c : 0;
       tot += c;
     }
@@ -193,17 +149,145 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     for (int j = 0; j < KPT; ++j) {
       if (j * kSelThreads >= N) break;
       const int i = tid + j * kSelThreads;
-      const bool flag = i < N && (take_all || (!take_none && keys[j] >= thr));
-      compact(i, flag);
+      tile(i, i < N && flag_of(j, i));
     }
   } else {
     for (int t0 = 0; t0 < N; t0 += kSelThreads) {
       const int i = t0 + tid;
-      const bool flag = i < N && (take_all || (!take_none && rank_key(get_score(i), age[i] >= G, i) >= thr));
-      compact(i, flag);
+      tile(i, i < N && flag_of(0, i));
     }
   }
-  for (int i = ke + tid; i < N; i += kSelThreads) idx[i] = -1;
+  for (int i = base + tid; i < N; i += kSelThreads) idx[i] = -1;
+  return base;
+}
+
+// block-wide count of forced tokens (age >= G)
+__device__ int count_forced(const int32_t* __restrict__ age, int N, int G, SelShared& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  int nf = 0;
+  for (int i = tid; i < N; i += kSelThreads) nf += age[i] >= G;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) nf += __shfl_xor(nf, o, kWave);
+  if (lane == 0) sh.red[wid] = nf;
+  __syncthreads();
+  int n = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) n += sh.red[w];
+  __syncthreads();
+  return n;
+}
+
+// KPT = keys held per thread in registers (N <= KPT * 1024); 0 = recompute
+// the keys from global memory in every pass (any N).
+// SCORED: the scores are formed here from P, U and the U partials (the last
+// scoring step fused in) and written to si.score_out; otherwise read.
+template <int KPT, bool SCORED>
+__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
+    const float* __restrict__ score, ScoreInputs si, int32_t* __restrict__ age, int N, int k, int G,
+    int rows_cap, int32_t* __restrict__ idx, int32_t* __restrict__ k_eff_out,
+    int32_t* __restrict__ n_forced_out) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const size_t eoff = static_cast<size_t>(b) * N;
+  age += eoff;
+  idx += eoff;
+  __shared__ SelShared sh;
+
+  float total = 0.f;
+  if constexpr (SCORED) total = usum_total(si.usum + static_cast<size_t>(b) * si.nblocks, si.nblocks, sh.red4);
+  auto get_score = [&](int i) -> float {
+    if constexpr (SCORED)
+      return combine_score(si.mass[eoff + i], si.surprise[eoff + i], total, si.w_attn_norm, si.w_surprise);
+    else
+      return score[eoff + i];
+  };
+
+  constexpr int NK = KPT > 0 ? KPT : 1;
+  uint64_t keys[NK];
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int i = tid + j * kSelThreads;
+      keys[j] = 0;
+      if (i < N) {
+        const float sc = get_score(i);
+        if constexpr (SCORED) si.score_out[eoff + i] = sc;
+        keys[j] = rank_key(sc, age[i] >= G, i);
+      }
+    }
+  } else {
+    if constexpr (SCORED)
+      for (int i = tid; i < N; i += kSelThreads) si.score_out[eoff + i] = get_score(i);
+  }
+  const int n_forced = count_forced(age, N, G, sh);
+
+  int ke = k > n_forced ? k : n_forced;
+  if (ke > rows_cap) ke = rows_cap;
+  const bool take_all = ke >= N, take_none = ke <= 0;
+  auto key_of = [&](int j, int i) -> uint64_t {
+    if constexpr (KPT > 0) return keys[j];
+    else return rank_key(get_score(i), age[i] >= G, i);
+  };
+  uint64_t thr = 0;
+  if (!take_all && !take_none) thr = radix_threshold<KPT>(key_of, N, static_cast<uint32_t>(ke), sh);
+  compact_set<KPT>([&](int j, int i) { return take_all || (!take_none && key_of(j, i) >= thr); }, N, idx, age,
+                   sh);
+  if (tid == 0) {
+    k_eff_out[b] = ke;
+    if (n_forced_out) n_forced_out[b] = n_forced;
+  }
+}
+
+// The union rule (WAM-Cache §1, §4.3, §4.4): the n_attn tokens of largest
+// attention mass, the n_surprise tokens of largest surprise and the forced
+// tokens, each once; k_eff = the size of the union (at most N).  Two radix
+// selects on the keys  mass(32) | ~index(31)  and  surprise(32) | ~index(31)
+// (same order conventions as above), then one compaction of the union.
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void select_union_kernel(
+    const float* __restrict__ mass, const float* __restrict__ surprise, int32_t* __restrict__ age, int N,
+    int n_attn, int n_surprise, int G, int32_t* __restrict__ idx, int32_t* __restrict__ k_eff_out,
+    int32_t* __restrict__ n_forced_out) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const size_t eoff = static_cast<size_t>(b) * N;
+  age += eoff;
+  idx += eoff;
+  mass += eoff;
+  surprise += eoff;
+  __shared__ SelShared sh;
+
+  constexpr int NK = KPT > 0 ? KPT : 1;
+  uint64_t kp[NK], ku[NK];
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int i = tid + j * kSelThreads;
+      kp[j] = i < N ? rank_key(mass[i], false, i) : 0;
+      ku[j] = i < N ? rank_key(surprise[i], false, i) : 0;
+    }
+  }
+  const int n_forced = count_forced(age, N, G, sh);
+  auto kp_of = [&](int j, int i) -> uint64_t {
+    if constexpr (KPT > 0) return kp[j];
+    else return rank_key(mass[i], false, i);
+  };
+  auto ku_of = [&](int j, int i) -> uint64_t {
+    if constexpr (KPT > 0) return ku[j];
+    else return rank_key(surprise[i], false, i);
+  };
+  // thresholds: ~0 selects nothing (keys never reach it), 0 selects everything
+  const uint64_t kNone = ~0ull;
+  uint64_t tp = kNone, tu = kNone;
+  if (n_attn >= N) tp = 0;
+  else if (n_attn > 0) tp = radix_threshold<KPT>(kp_of, N, static_cast<uint32_t>(n_attn), sh);
+  if (n_surprise >= N) tu = 0;
+  else if (n_surprise > 0) tu = radix_threshold<KPT>(ku_of, N, static_cast<uint32_t>(n_surprise), sh);
+  const int ke = compact_set<KPT>(
+      [&](int j, int i) {
+        return age[i] >= G || (tp != kNone && kp_of(j, i) >= tp) || (tu != kNone && ku_of(j, i) >= tu);
+      },
+      N, idx, age, sh);
   if (tid == 0) {
     k_eff_out[b] = ke;
     if (n_forced_out) n_forced_out[b] = n_forced;
@@ -235,6 +319,23 @@ hipError_t launch_select(const float* score, int32_t* age, int B, int N, int k, 
 hipError_t launch_select_scored(const ScoreInputs& si, int32_t* age, int B, int N, int k, int G, int rows_cap,
                                 int32_t* idx, int32_t* k_eff, int32_t* n_forced, hipStream_t s) {
   launch_select_impl<true>(nullptr, si, age, B, N, k, G, rows_cap, idx, k_eff, n_forced, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_union(const float* mass, const float* surprise, int32_t* age, int B, int N, int n_attn,
+                               int n_surprise, int G, int32_t* idx, int32_t* k_eff, int32_t* n_forced,
+                               hipStream_t s) {
+  const dim3 grid(B), block(kSelThreads);
+  if (N <= 1024)
+    select_union_kernel<1><<<grid, block, 0, s>>>(mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
+  else if (N <= 2048)
+    select_union_kernel<2><<<grid, block, 0, s>>>(mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
+  else if (N <= 4096)
+    select_union_kernel<4><<<grid, block, 0, s>>>(mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
+  else if (N <= 8192)
+    select_union_kernel<8><<<grid, block, 0, s>>>(mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
+  else
+    select_union_kernel<0><<<grid, block, 0, s>>>(mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
   return hipGetLastError();
 }
 

@@ -59,6 +59,9 @@ _SIGNATURES = {
     "wamc_refresh_layer": ([_DP, _I, _LP, _P, _P, _P, _I, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "wamc_prefill_chunk": ([_DP, _LP, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P],
                            ctypes.c_int),
+    "wamc_select_union": ([_DP, _P, _P, _P, _I, _I, _P, _P, _P, _P], ctypes.c_int),
+    "wamc_prefill_chunk_union": ([_DP, _LP, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _SZ, _P],
+                                 ctypes.c_int),
     "wamc_dense_prefill": ([_DP, _LP, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "wamc_timing_enable": ([ctypes.c_int], ctypes.c_int),
     "wamc_timing_count": ([], ctypes.c_int),
@@ -192,6 +195,28 @@ def prefill_chunk(dims, layers: Sequence[dict], z, zref, q_act, k_cache, v_cache
                                     _ptr(layer_out), rows_cap, _ptr(ws), ws.numel(), _stream(stream)))
 
 
+def budget_rows(fraction: float, n_tokens: int) -> int:
+    """Token count of a refresh budget given as a fraction of the tokens:
+    ceil(fraction * n_tokens), taken on the decimal value (0.1 of 30 is 3)."""
+    from fractions import Fraction
+    return min(n_tokens, -(-Fraction(repr(float(fraction))) * n_tokens // 1))
+
+
+def select_union(dims, mass, surprise, age, n_attn, n_surprise, idx, k_eff, n_forced=None, stream=None):
+    _check(lib().wamc_select_union(ctypes.byref(dims), _ptr(mass), _ptr(surprise), _ptr(age), n_attn, n_surprise,
+                                   _ptr(idx), _ptr(k_eff), _ptr(n_forced), _stream(stream)))
+
+
+def prefill_chunk_union(dims, layers: Sequence[dict], z, zref, q_act, k_cache, v_cache, age, n_attn, n_surprise,
+                        idx_out, k_eff_out, rows_cap, ws, mass_in=None, layer_out=None, stream=None,
+                        _layer_array=None):
+    arr = _layer_array if _layer_array is not None else _layers(layers)
+    _check(lib().wamc_prefill_chunk_union(ctypes.byref(dims), arr, _ptr(z), _ptr(zref), _ptr(q_act), _ptr(mass_in),
+                                          _ptr(k_cache), _ptr(v_cache), _ptr(age), n_attn, n_surprise, _ptr(idx_out),
+                                          _ptr(k_eff_out), _ptr(layer_out), rows_cap, _ptr(ws), ws.numel(),
+                                          _stream(stream)))
+
+
 def dense_prefill(dims, layers: Sequence[dict], z, zref, k_cache, v_cache, age, ws, layer_out=None, stream=None,
                   _layer_array=None):
     arr = _layer_array if _layer_array is not None else _layers(layers)
@@ -259,6 +284,12 @@ class Engine:
                       self.idx, self.k_eff, self.rows_cap, self.ws, mass_in=mass_in, idx_override=idx_override,
                       k_eff_override=k_eff_override, score_out=self.score, layer_out=layer_out, stream=stream,
                       _layer_array=self.layer_array)
+
+    def chunk_union(self, z, q_act, n_attn, n_surprise, mass_in=None, layer_out=None, stream=None):
+        """A refresh chunk with the union rule (needs rows_cap == N)."""
+        prefill_chunk_union(self.dims, self.weights, z, self.zref, q_act, self.k_cache, self.v_cache, self.age,
+                            n_attn, n_surprise, self.idx, self.k_eff, self.rows_cap, self.ws, mass_in=mass_in,
+                            layer_out=layer_out, stream=stream, _layer_array=self.layer_array)
 
     def snapshot(self):
         return {n: getattr(self, n).clone() for n in ("k_cache", "v_cache", "zref", "age")}

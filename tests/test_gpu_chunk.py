@@ -196,3 +196,44 @@ def test_replay_is_bitwise(name):
         outs.append([lo.clone(), eng.k_cache.clone(), eng.v_cache.clone(), eng.score.clone(), eng.idx.clone()])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["c1_tiny", "t_bf16_small", "t_bf16_batch"])
+def test_union_rule_rollout(name):
+    """Chunks with the union rule (WAM-Cache §1, §4.3, §4.4) at the pages'
+    default budgets (b_a, b_s) = (0.4, 0.1): the library's set is exactly the
+    oracle's union on the library's own mass and surprise, k_eff varies from
+    chunk to chunk, and the rows, K/V cache and ages match the oracle run on
+    the same sets."""
+    wl = W.preset(name)
+    r = W.make_rollout(wl)
+    prec = O.Precision(wl.dtype)
+    N, B = wl.n_tokens, wl.batch
+    na, ns = O.budget_count(0.4, N), O.budget_count(0.1, N)
+    eng = engine(wl, r)
+    eng.dense(batch_z(wl, r, 0))
+    states = [O.dense_prefill(r.z[e][0], r.weights, wl.n_heads, wl.ln_eps, prec)[0] for e in range(B)]
+    lo = torch.zeros((wl.n_layers, B, N, wl.d_model), dtype=torch.float32, device=DEV)
+    P = torch.empty((B, N), dtype=torch.float32, device=DEV)
+    U = torch.empty_like(P)
+    sc = torch.empty_like(P)
+    keffs = []
+    for t in range(1, wl.chunks):
+        z, qa = batch_z(wl, r, t), batch_q(wl, r, t)
+        age_before = to_np(eng.age).copy()
+        wamc.score(eng.dims, z, eng.zref, qa, eng.k_cache, sc, eng.ws, mass_out=P, surprise_out=U)
+        eng.chunk_union(z, qa, na, ns, layer_out=lo)
+        torch.cuda.synchronize()
+        res = []
+        for b in range(B):
+            idx, k_eff, age, _ = O.select_union(to_np(P[b]), to_np(U[b]), age_before[b], na, ns, wl.age_bound)
+            assert int(eng.k_eff[b]) == k_eff
+            assert np.array_equal(to_np(eng.idx[b])[:k_eff], idx)
+            assert (to_np(eng.idx[b])[k_eff:] == -1).all()
+            assert np.array_equal(to_np(eng.age[b]), age)
+            keffs.append(k_eff)
+            res.append(O.refresh_chunk(states[b], r.z[b][t], r.qa[b][t], r.weights, 0, wl.age_bound, wl.n_heads,
+                                       wl.ln_eps, wl.w_attn, wl.w_surprise, prec, idx_override=idx))
+        _compare_chunk(wl, eng, states, res, lo, t)
+        assert int(eng.age.max()) <= wl.age_bound
+    assert min(keffs) >= max(na, ns)

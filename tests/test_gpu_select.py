@@ -87,3 +87,45 @@ def test_select_repeatable():
         wamc.select(dims, score, a, 1200, N, idx, keff)
         outs.append((idx.cpu(), keff.cpu(), a.cpu()))
     assert all(torch.equal(x, y) for x, y in zip(outs[0], outs[1]))
+
+
+UNION_CASES = [
+    # B, N, n_attn, n_surprise, G, value kind
+    (1, 1, 0, 0, 0, "normal"),
+    (1, 7, 3, 2, 2, "ties"),
+    (2, 256, 100, 30, 2, "ties"),
+    (3, 1000, 400, 100, 2, "mixed"),
+    (1, 4680, 1872, 468, 2, "normal"),
+    (2, 8192, 3277, 820, 4, "mixed"),
+    (1, 9000, 3600, 900, 2, "ties"),       # recompute-from-global path
+    (2, 20000, 8000, 2000, 3, "mixed"),
+    (1, 3000, 3000, 0, 2, "normal"),       # attention budget covers every token
+    (1, 3000, 0, 0, 2, "normal"),          # forced tokens only
+    (1, 3000, 0, 3000, 9, "ties"),         # surprise budget covers every token
+]
+
+
+@pytest.mark.parametrize("B,N,na,ns,G,kind", UNION_CASES)
+def test_select_union_bit_exact(B, N, na, ns, G, kind):
+    """The union rule (WAM-Cache §1, §4.3, §4.4) against the oracle on the
+    same mass and surprise values: idx, k_eff, forced counts and ages."""
+    rng = np.random.default_rng(N * 17 + na + 3 * ns)
+    mass = _scores(rng, B, N, kind)
+    surp = _scores(rng, B, N, kind)
+    age = rng.integers(0, G + 2, size=(B, N)).astype(np.int32)
+    dims = _dims(B, N, G)
+    a_d = torch.from_numpy(age).to(DEV)
+    idx = torch.full((B, N), -7, dtype=torch.int32, device=DEV)
+    keff = torch.zeros(B, dtype=torch.int32, device=DEV)
+    nf = torch.zeros(B, dtype=torch.int32, device=DEV)
+    wamc.select_union(dims, torch.from_numpy(mass).to(DEV), torch.from_numpy(surp).to(DEV), a_d, na, ns, idx, keff,
+                      nf)
+    torch.cuda.synchronize()
+    for b in range(B):
+        want_idx, want_k, want_age, want_nf = O.select_union(mass[b], surp[b], age[b], na, ns, G)
+        assert int(keff[b]) == want_k
+        assert int(nf[b]) == want_nf
+        got = idx[b].cpu().numpy()
+        assert np.array_equal(got[:want_k], want_idx)
+        assert (got[want_k:] == -1).all()
+        assert np.array_equal(a_d[b].cpu().numpy(), want_age)

@@ -122,3 +122,23 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         wamc._ptr(torch.zeros(4))
+
+
+def test_union_entry_points_validate():
+    L = wamc.lib()
+    d = _dims()
+    N = d.n_tokens
+    assert L.wamc_select_union(ctypes.byref(d), FAKE, FAKE, FAKE, N + 1, 0, FAKE, FAKE, None, None) == 1
+    assert L.wamc_select_union(ctypes.byref(d), FAKE, FAKE, FAKE, 3, -1, FAKE, FAKE, None, None) == 1
+    assert L.wamc_select_union(ctypes.byref(d), None, FAKE, FAKE, 3, 3, FAKE, FAKE, None, None) == 1
+    assert L.wamc_select_union(ctypes.byref(d), FAKE, MISALIGNED, FAKE, 3, 3, FAKE, FAKE, None, None) == 4
+    lw = wamc.LayerW(*([FAKE] * 9))
+    arr = (wamc.LayerW * d.n_layers)(*([lw] * d.n_layers))
+    ws = wamc.workspace_bytes(d, N)
+    # the union can hold every token: rows_cap must be N
+    st = L.wamc_prefill_chunk_union(ctypes.byref(d), arr, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, 5, FAKE,
+                                    FAKE, None, N - 1, FAKE, ws, None)
+    assert st == 1 and b"rows_cap" in L.wamc_last_error()
+    st = L.wamc_prefill_chunk_union(ctypes.byref(d), arr, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, 5, FAKE,
+                                    FAKE, None, N, FAKE, ws - 1, None)
+    assert st == 3
