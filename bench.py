@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--plateau", action="store_true",
                     help="one-layer refresh latency vs refreshed rows, stepped every 32 rows (one JSON line)")
     ap.add_argument("--sweep-layers", type=int, default=30, help="layers of the stack used by --sweep")
+    ap.add_argument("--small-n", action="store_true",
+                    help="30-layer d=1536 stack at 120 / 480 / 1080 tokens with k = 0.584 N, eager and HIP-graph "
+                         "replay (one JSON line each)")
     ap.add_argument("--union", action="store_true",
                     help="the pages' union rule on the 30-layer stack at budgets (b_a, b_s) = (0.4, 0.1) and "
                          "(0.6, 0.1), G = 2 (one JSON line each)")
@@ -267,6 +270,85 @@ def run_union(args):
               flush=True)
 
 
+def run_small_n(args):
+    """The pages' latency experiment (WAM-Cache §5.2, Figure 3): the refresh
+    ratio measured at the native 120 tokens (0.584) replayed at 120, 480 and
+    1080 tokens (a 12x10 grid and 4x / 9x larger ones) on the 30-layer d=1536
+    stack; refresh and dense chunks timed eagerly and as HIP-graph replays
+    (the pages use CUDA-graph replay)."""
+    import torch
+    from sparse_kv_refresh_amd import inputs as W
+    from sparse_kv_refresh_amd import wamc
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    weights = None
+    for rows, cols in ((12, 10), (24, 20), (36, 30)):
+        N = rows * cols
+        k = int(round(0.584 * N))
+        wl = W.preset("c3_stack", n_layers=args.sweep_layers, views=1, rows=rows, cols=cols, k=k, age_bound=2)
+        r = W.make_rollout(wl, chunks=2)
+        if weights is None:
+            weights = wamc.Engine.upload_weights(r.weights, torch.bfloat16, dev)
+        eng = wamc.Engine(wamc.dims_for(wl), weights, k, dev)
+        z0 = torch.from_numpy(r.z[0][0]).to(dev, torch.bfloat16)[None].contiguous()
+        z1 = torch.from_numpy(r.z[0][1]).to(dev, torch.bfloat16)[None].contiguous()
+        q1 = torch.from_numpy(r.qa[0][1]).to(dev, torch.bfloat16)[:, None].contiguous()
+        eng.dense(z0)
+        torch.cuda.synchronize()
+        snap = eng.snapshot()
+
+        def refresh():
+            eng.chunk(z1, q1, k)
+
+        def dense():
+            eng.dense(z1)
+
+        def eager(fn, reps=20):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+
+        def graphed(fn, reps=20):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+
+        # k >= N/2, so k_eff = k in every chunk and repeated chunks do equal work
+        out = {"small_n": N, "grid": [rows, cols], "layers": wl.n_layers, "k": k, "rho": k / N}
+        out["refresh_ms_eager"] = eager(refresh)
+        eng.restore(snap)
+        out["refresh_ms_graph"] = graphed(refresh)
+        out["dense_ms_eager"] = eager(dense)
+        out["dense_ms_graph"] = graphed(dense)
+        out["speedup_eager"] = out["dense_ms_eager"] / out["refresh_ms_eager"]
+        out["speedup_graph"] = out["dense_ms_graph"] / out["refresh_ms_graph"]
+        out["speedup_bound"] = N / k
+        print(json.dumps(out), flush=True)
+        del eng
+
+
 def run_plateau(args):
     """One d=1536 layer over N=4680 cached tokens: wamc_refresh_layer latency
     as the number of refreshed rows m grows by 32, once with the launch sized
@@ -342,6 +424,8 @@ def main():
         return run_plateau(args)
     if args.union:
         return run_union(args)
+    if args.small_n:
+        return run_small_n(args)
 
     import torch
     from sparse_kv_refresh_amd import inputs as W
