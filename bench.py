@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--small-n", action="store_true",
                     help="30-layer d=1536 stack at 120 / 480 / 1080 tokens with k = 0.584 N, eager and HIP-graph "
                          "replay (one JSON line each)")
+    ap.add_argument("--capacity", action="store_true",
+                    help="capacity filling on the 30-layer stack: measured per-layer plateau, then chunks at k and "
+                         "at the plateau's upper end (one JSON line per k)")
     ap.add_argument("--union", action="store_true",
                     help="the pages' union rule on the 30-layer stack at budgets (b_a, b_s) = (0.4, 0.1) and "
                          "(0.6, 0.1), G = 2 (one JSON line each)")
@@ -349,6 +352,76 @@ def run_small_n(args):
         del eng
 
 
+def run_capacity(args):
+    """Capacity filling (RealtimeWAM §3): the per-layer latency of the d=1536
+    layer over N=4680 tokens is measured every 32 rows with launches sized for
+    the rows; for each requested k the plateau's upper end k_fill (2 %
+    tolerance) is taken, and whole 30-layer chunks are timed at k and k_fill
+    (ages reset before each chunk, so exactly k resp. k_fill rows refresh)."""
+    import torch
+    from sparse_kv_refresh_amd import inputs as W
+    from sparse_kv_refresh_amd import wamc
+    from sparse_kv_refresh_amd.capacity import plateau_capacity
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # per-layer curve
+    wl1 = W.preset("c3_stack", n_layers=1)
+    r1 = W.make_rollout(wl1, chunks=1)
+    dims1 = wamc.dims_for(wl1)
+    w1 = wamc.Engine.upload_weights(r1.weights, torch.bfloat16, dev)[0]
+    N, d = wl1.n_tokens, wl1.d_model
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    kc = torch.randn((1, N, d), device=dev, generator=g).to(torch.bfloat16)
+    vc = torch.randn((1, N, d), device=dev, generator=g).to(torch.bfloat16)
+    x0 = torch.randn((1, N, d), device=dev, generator=g)
+    idx = torch.arange(N, dtype=torch.int32, device=dev)[None].contiguous()
+    ws = torch.empty(wamc.workspace_bytes(dims1, N), dtype=torch.uint8, device=dev)
+    rows = list(range(32, N + 1, 32)) + ([N] if N % 32 else [])
+    curve = []
+    for m in rows:
+        keff = torch.tensor([m], dtype=torch.int32, device=dev)
+        x = x0[:, :m].contiguous()
+        for _ in range(2):
+            wamc.refresh_layer(dims1, 0, w1, x, idx, keff, m, kc, vc, ws, stream=stream)
+        a.record(stream)
+        for _ in range(5):
+            wamc.refresh_layer(dims1, 0, w1, x, idx, keff, m, kc, vc, ws, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        curve.append(a.elapsed_time(b) / 5)
+    del kc, vc, x0, ws
+    # whole chunks at k and at the capacity
+    wl = W.preset("c3_stack", n_layers=args.sweep_layers)
+    r = W.make_rollout(wl, chunks=2)
+    weights = wamc.Engine.upload_weights(r.weights, torch.bfloat16, dev)
+    z0 = torch.from_numpy(r.z[0][0]).to(dev, torch.bfloat16)[None].contiguous()
+    z1 = torch.from_numpy(r.z[0][1]).to(dev, torch.bfloat16)[None].contiguous()
+    q1 = torch.from_numpy(r.qa[0][1]).to(dev, torch.bfloat16)[:, None].contiguous()
+    for k in (468, 1170, 2340, 2458, 2808):
+        k_fill = plateau_capacity(rows, curve, k, tol=0.02)
+        res = {}
+        for name, kk in (("k", k), ("fill", k_fill)):
+            eng = wamc.Engine(wamc.dims_for(wl), weights, kk, dev)
+            eng.dense(z0)
+            ts = []
+            for _ in range(6):
+                eng.age.zero_()
+                a.record(stream)
+                eng.chunk(z1, q1, kk, stream=stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            res[name] = float(np.median(ts[1:]))
+            del eng
+        print(json.dumps({"capacity": {"k": k, "k_fill": k_fill, "extra_tokens": k_fill - k},
+                          "layers": wl.n_layers, "n_tokens": N, "ms_at_k": res["k"], "ms_at_fill": res["fill"],
+                          "latency_change": res["fill"] / res["k"] - 1.0,
+                          "layer_ms_at_k": float(np.interp(k, rows, curve)),
+                          "layer_ms_at_fill": float(np.interp(k_fill, rows, curve))}), flush=True)
+
+
 def run_plateau(args):
     """One d=1536 layer over N=4680 cached tokens: wamc_refresh_layer latency
     as the number of refreshed rows m grows by 32, once with the launch sized
@@ -424,6 +497,8 @@ def main():
         return run_plateau(args)
     if args.union:
         return run_union(args)
+    if args.capacity:
+        return run_capacity(args)
     if args.small_n:
         return run_small_n(args)
 
