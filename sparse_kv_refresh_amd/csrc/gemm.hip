@@ -330,6 +330,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// s_waitcnt vmcnt(ahead * LOADS) for a run-time ahead in [0, MAXA]
+template <int LOADS, int MAXA>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  if constexpr (MAXA <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= MAXA) wait_vmcnt<MAXA * LOADS>();
+    else wait_tiles_ahead<LOADS, MAXA - 1>(ahead);
+  }
+}
+
 // Column key of element chunk (row, kc) in a tile with CPR 16-byte chunks per
 // row.  gfx950 LDS has 64 banks (a 256-byte window) and serves ds_read_b128
 // 16 lanes at a time; an MFMA fragment read has 16 consecutive rows at the
@@ -759,17 +770,8 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   for (int p = 0; p < STAGES - 1; ++p)
     if (p < n) issue(p, p);
   for (int q = 0; q < n; ++q) {
-    const int ahead = min(STAGES - 2, n - 1 - q);
-    if constexpr (STAGES >= 4) {
-      if (ahead >= 2) wait_vmcnt<2 * LOADS>();
-      else if (ahead == 1) wait_vmcnt<LOADS>();
-      else wait_vmcnt<0>();
-    } else if constexpr (STAGES == 3) {
-      if (ahead >= 1) wait_vmcnt<LOADS>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // tile q has landed once at most (tiles issued after it) x LOADS loads remain
+    wait_tiles_ahead<LOADS, STAGES - 2>(min(STAGES - 2, n - 1 - q));
     __builtin_amdgcn_s_barrier();
     if (q + STAGES - 1 < n) issue(q + STAGES - 1, (q + STAGES - 1) % STAGES);
     const uint4* as = lds[q % STAGES];
@@ -864,7 +866,23 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
 // against 33-36 % for 128x128 tiles at 16k rows; slower at 2.5-4.7k rows,
 // where the tile count leaves a large ragged round)
 constexpr bool kGemmBig = WAMC_GEMM_BIG != 0;
-using SkSmall = SkConfig<128, 128, 64, 2, 2, 2>;
+#ifndef WAMC_SK_BK
+#define WAMC_SK_BK 64
+#endif
+#ifndef WAMC_SK_STAGES
+#define WAMC_SK_STAGES 2
+#endif
+#ifndef WAMC_SK_BM
+#define WAMC_SK_BM 128
+#endif
+
+#ifndef WAMC_SK_BN
+#define WAMC_SK_BN 128
+#endif
+// (measured on the d=1536 shapes: 128x256 / 256x128 wave tiles, BK 32 with
+// 4 or 6 stages, BK 64 with 3 stages, and raised wave priority around the
+// MFMAs were all slower than 128x128, BK 64, 2 stages, 2 workgroups per CU)
+using SkSmall = SkConfig<WAMC_SK_BM, WAMC_SK_BN, WAMC_SK_BK, WAMC_SK_STAGES, 2, 2>;
 using SkBig = SkConfig<256, 256, 32, 4, 2, 4>;
 
 GemmScratch gemm_scratch(int B, int rows_cap, int d, int F) {
@@ -975,6 +993,9 @@ static void launch_dtl(GemmEpi epi, const GemmArgs& g, hipStream_t s) {
 #ifndef WAMC_GEMM_SPLITK
 #define WAMC_GEMM_SPLITK 1
 #endif
+#ifndef WAMC_GEMM_KS2
+#define WAMC_GEMM_KS2 1
+#endif
 constexpr bool kSplitK = WAMC_GEMM_SPLITK != 0;
 
 // Tile shape per GEMM.  128x256 / 256x128 tiles stage a third fewer bytes per
@@ -997,7 +1018,8 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   // Otherwise the work-balanced kernel sizes its work from k_eff on the device.
   const long long t128 = static_cast<long long>((g.M + 127) / 128) * ((g.Nout + 127) / 128);
   const bool dtl_ok = bf16 && g.K % 64 == 0 && !kForceGeneric;
-  const bool use_ks2 = dtl_ok && kSplitK && t128 <= 256 && g.K >= 2 * 64 && (g.K < 4096 || t128 > 128);
+  const bool use_ks2 = dtl_ok && kSplitK && WAMC_GEMM_KS2 && t128 <= 256 && g.K >= 2 * 64 &&
+                       (g.K < 4096 || t128 > 128);
   const bool use_sk = dtl_ok && WAMC_GEMM_SK && g.sk_partial && g.sk_counters &&
                       g.sk_partial_bytes >= SkSmall::kTileBytes;
   // 256-wide tiles need d >= 256 (a QKV tile crosses at most one of the Q|K|V edges)
@@ -1006,7 +1028,7 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   if (!use_ks2 && use_sk && big) {
     launch_sk<256, 256, 32, 4, 2, 4>(epi, g, s);
   } else if (!use_ks2 && use_sk) {
-    launch_sk<128, 128, 64, 2, 2, 2>(epi, g, s);
+    launch_sk<WAMC_SK_BM, WAMC_SK_BN, WAMC_SK_BK, WAMC_SK_STAGES, 2, 2>(epi, g, s);
   } else if (use_ks2) {
     const unsigned grid = static_cast<unsigned>(t128);
     switch (epi) {
