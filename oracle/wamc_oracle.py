@@ -52,6 +52,10 @@ WAM-Cache §4.2-4.4 are lost in the text):
   *before* attention, softmax(Q K^T / sqrt(dh)) V over all N cached keys,
   gated residual out-projection, a second modulated LN, GELU (erf form) MLP
   with a gated residual;
+* optional text cross-attention between the two (§3: SA, CA, MLP): queries
+  from an unmodulated LN of the rows with bias, keys/values projected from
+  the instruction's embeddings once per episode, per-head softmax over the T
+  text tokens, ungated residual out-projection;
 * precision: fp32 workloads run here in float64 with no rounding; bf16
   workloads run in float32 arithmetic with round-to-nearest-even bf16 at the
   storage points (weights, z, zref, Qa, H1, Q, K/V cache, attention output,
@@ -150,14 +154,30 @@ def attention(Q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, n_heads: int) -> np
     return O
 
 
+def text_kv(E: np.ndarray, w, prec: Precision):
+    """Keys and values of the text cross-attention of one layer (WAM-Cache §3:
+    the cross-attention layer attends to keys and values projected from the
+    text embeddings): [K_t | V_t] = E W_kvc^T + b_kvc, rows of W_kvc K then
+    V.  They depend on the instruction only, so they are computed once per
+    episode and kept."""
+    d = E.shape[1]
+    ld = prec.load
+    KV = ld(E) @ ld(w.w_kvc).T + ld(w.b_kvc)
+    return prec.store(KV[:, :d]), prec.store(KV[:, d:])
+
+
 def block(X: np.ndarray, I: np.ndarray, w, Kc: np.ndarray, Vc: np.ndarray,
-          n_heads: int, eps: float, prec: Precision) -> np.ndarray:
+          n_heads: int, eps: float, prec: Precision, text=None) -> np.ndarray:
     """One DiT layer applied to the rows X (token ids I, ascending).
 
     Kc, Vc are this layer's cache [N, d]; rows I are overwritten with the
     fresh keys/values before attention, so refreshed queries see their own
-    fresh keys and every other token's retained ones.  Returns the layer's
-    output rows (the residual stream, arithmetic precision).
+    fresh keys and every other token's retained ones.  With `text` = (K_t,
+    V_t) the module also runs its text cross-attention between self-attention
+    and the MLP (WAM-Cache §3: SA, CA, MLP, each with a residual): the
+    queries come from an unmodulated LayerNorm of the rows, the residual is
+    ungated.  Returns the layer's output rows (the residual stream,
+    arithmetic precision).
     """
     d = X.shape[1]
     ld = prec.load
@@ -170,6 +190,12 @@ def block(X: np.ndarray, I: np.ndarray, w, Kc: np.ndarray, Vc: np.ndarray,
     Vc[I] = prec.store(QKV[:, 2 * d:])
     O = prec.store(attention(Q, Kc, Vc, n_heads))
     X = X + gate1 * (O @ ld(w.w_o).T + ld(w.b_o))
+    if text is not None:
+        Kt, Vt = text
+        H3 = prec.store(layer_norm(X, eps))
+        Qc = prec.store(H3 @ ld(w.w_qc).T + ld(w.b_qc))
+        Oc = prec.store(attention(Qc, Kt, Vt, n_heads))
+        X = X + (Oc @ ld(w.w_oc).T + ld(w.b_oc))
     H2 = prec.store(layer_norm(X, eps) * (1 + scale2) + shift2)
     G = prec.store(gelu(H2 @ ld(w.w_1).T + ld(w.b_1)))
     X = X + gate2 * (G @ ld(w.w_2).T + ld(w.b_2))
@@ -182,32 +208,38 @@ def block(X: np.ndarray, I: np.ndarray, w, Kc: np.ndarray, Vc: np.ndarray,
 
 @dataclass
 class State:
-    """Per-episode cache state: K, V [L, N, d]; age [N] int; zref [N, d]."""
+    """Per-episode cache state: K, V [L, N, d]; age [N] int; zref [N, d];
+    text: per layer (K_t, V_t) of the instruction, or None (no text
+    cross-attention)."""
     K: np.ndarray
     V: np.ndarray
     age: np.ndarray
     zref: np.ndarray
+    text: Optional[list] = None
 
     def copy(self) -> "State":
-        return State(self.K.copy(), self.V.copy(), self.age.copy(), self.zref.copy())
+        return State(self.K.copy(), self.V.copy(), self.age.copy(), self.zref.copy(), self.text)
 
 
 def dense_prefill(z: np.ndarray, weights: Sequence, n_heads: int, eps: float,
-                  prec: Precision):
-    """Chunk 0: every token through every layer; ages 0 and zref = z.
+                  prec: Precision, text_emb: Optional[np.ndarray] = None):
+    """Chunk 0: every token through every layer; ages 0 and zref = z.  With
+    text embeddings E [T, d] every layer also runs its text cross-attention
+    (its text keys/values, computed here, are kept in the state).
 
     Returns (state, [X_l for each layer])."""
     N, d = z.shape
     L = len(weights)
     K = np.zeros((L, N, d), dtype=prec.acc)
     V = np.zeros((L, N, d), dtype=prec.acc)
+    text = None if text_emb is None else [text_kv(text_emb, weights[l], prec) for l in range(L)]
     X = prec.load(z)
     I = np.arange(N)
     outs = []
     for l in range(L):
-        X = block(X, I, weights[l], K[l], V[l], n_heads, eps, prec)
+        X = block(X, I, weights[l], K[l], V[l], n_heads, eps, prec, None if text is None else text[l])
         outs.append(X.copy())
-    return State(K, V, np.zeros(N, dtype=np.int64), prec.load(z).copy()), outs
+    return State(K, V, np.zeros(N, dtype=np.int64), prec.load(z).copy(), text), outs
 
 
 # --------------------------------------------------------------------------
@@ -386,7 +418,8 @@ def refresh_chunk(state: State, z: np.ndarray, qa: Optional[np.ndarray], weights
     state.zref[idx] = zl[idx]
     outs = []
     for l in range(len(weights)):
-        X = block(X, idx, weights[l], state.K[l], state.V[l], n_heads, eps, prec)
+        X = block(X, idx, weights[l], state.K[l], state.V[l], n_heads, eps, prec,
+                  None if state.text is None else state.text[l])
         outs.append(X.copy())
     return ChunkResult(s, P, U, idx, k_eff, n_forced, outs)
 

@@ -33,6 +33,8 @@ SEED_PATCH = 1
 SEED_LATENT = 100
 SEED_QUERY = 200
 SEED_AGES = 300
+SEED_TEXT = 400
+SEED_TEXT_WEIGHTS = 7
 
 
 @dataclass(frozen=True)
@@ -57,6 +59,7 @@ class Workload:
     w_surprise: float = 0.1
     ln_eps: float = 1e-6
     random_initial_ages: bool = False   # ages ~ U{0..G} after the dense chunk
+    n_text: int = 0                     # instruction tokens of the text cross-attention (0: none)
 
     @property
     def n_tokens(self) -> int:
@@ -95,6 +98,12 @@ PRESETS: Dict[str, Workload] = {
                              batch=3, chunks=4, latent="episodes"),
     "t_bf16_stack": Workload("t_bf16_stack", 4, 1536, 12, 8960, 3, 30, 52, 64, 2808, 3, "bf16",
                              chunks=3, latent="stack"),
+    # with the text cross-attention: 77 instruction tokens (ragged against
+    # the 64-key tiles)
+    "t_bf16_text": Workload("t_bf16_text", 2, 256, 2, 640, 1, 20, 35, 40, 300, 2, "bf16",
+                            chunks=4, latent="blob", n_text=77),
+    "t_fp32_text": Workload("t_fp32_text", 2, 128, 4, 512, 1, 16, 16, 32, 64, 4, "fp32",
+                            chunks=4, latent="blob", n_text=23),
 }
 
 
@@ -134,6 +143,13 @@ class LayerWeights:
     w_2: np.ndarray     # [d, F]
     b_2: np.ndarray     # [d]
     mod: np.ndarray     # [6, d]: shift1, scale1, gate1, shift2, scale2, gate2
+    # text cross-attention (present when the workload has instruction tokens)
+    w_qc: Optional[np.ndarray] = None    # [d, d]
+    b_qc: Optional[np.ndarray] = None    # [d]
+    w_kvc: Optional[np.ndarray] = None   # [2d, d]  rows: K, V
+    b_kvc: Optional[np.ndarray] = None   # [2d]
+    w_oc: Optional[np.ndarray] = None    # [d, d]
+    b_oc: Optional[np.ndarray] = None    # [d]
 
 
 def make_weights(wl: Workload, seed: int = SEED_WEIGHTS) -> List[LayerWeights]:
@@ -156,6 +172,17 @@ def make_weights(wl: Workload, seed: int = SEED_WEIGHTS) -> List[LayerWeights]:
         mod[5] += 1.0
         out.append(LayerWeights(*[_store(wl, a) for a in
                                   (w_qkv, b_qkv, w_o, b_o, w_1, b_1, w_2, b_2, mod)]))
+    if wl.n_text > 0:
+        # a generator of its own, so the self-attention / MLP weights above do
+        # not depend on whether the workload has a text cross-attention
+        rc = np.random.default_rng([seed, SEED_TEXT_WEIGHTS])
+        for lw in out:
+            lw.w_qc = _store(wl, _normal(rc, (d, d), 0.02))
+            lw.b_qc = _store(wl, _normal(rc, (d,), 0.02))
+            lw.w_kvc = _store(wl, _normal(rc, (2 * d, d), 0.02))
+            lw.b_kvc = _store(wl, _normal(rc, (2 * d,), 0.02))
+            lw.w_oc = _store(wl, _normal(rc, (d, d), 0.02))
+            lw.b_oc = _store(wl, _normal(rc, (d,), 0.02))
     return out
 
 
@@ -282,6 +309,14 @@ class Rollout:
     z: List[List[np.ndarray]]            # [episode][chunk] -> [N, d]
     qa: List[List[Optional[np.ndarray]]]  # [episode][chunk] -> [L, A, d] (None at t=0)
     ages0: List[np.ndarray]              # [episode] -> [N] int32
+    text: Optional[List[np.ndarray]] = None   # [episode] -> [T, d] instruction embeddings
+
+
+def make_text(wl: Workload, episode: int = 0) -> np.ndarray:
+    """Instruction embeddings E [T, d] ~ N(0, 1) (a stand-in for the text
+    encoder's output), fixed for the episode."""
+    rng = np.random.default_rng([SEED_TEXT, episode])
+    return _store(wl, _normal(rng, (wl.n_text, wl.d_model)))
 
 
 def make_rollout(wl: Workload, chunks: Optional[int] = None) -> Rollout:
@@ -294,4 +329,5 @@ def make_rollout(wl: Workload, chunks: Optional[int] = None) -> Rollout:
         zs.append([tokens_from_latent(wl, src.latent(t), w_pe) for t in range(T)])
         qs.append([None] + [make_queries(wl, t, e) for t in range(1, T)])
         ages.append(make_initial_ages(wl, e))
-    return Rollout(wl, weights, zs, qs, ages)
+    text = [make_text(wl, e) for e in range(wl.batch)] if wl.n_text > 0 else None
+    return Rollout(wl, weights, zs, qs, ages, text)

@@ -121,9 +121,18 @@ def _scalar_bf16(v):
     return struct.unpack("<f", struct.pack("<I", b & 0xFFFFFFFF))[0]
 
 
-def scalar_block(X, I, w, Kc, Vc, H, eps, rnd=lambda v: v):
+def scalar_text_kv(E, w, rnd=lambda v: v):
+    """Text keys/values of one layer as scalar loops."""
+    d = len(E[0])
+    kv = [[rnd(w.b_kvc[o] + sum(E[j][c] * w.w_kvc[o][c] for c in range(d))) for o in range(2 * d)]
+          for j in range(len(E))]
+    return [r[:d] for r in kv], [r[d:] for r in kv]
+
+
+def scalar_block(X, I, w, Kc, Vc, H, eps, rnd=lambda v: v, text=None):
     """The block written as plain scalar loops (float64), rounding through
-    `rnd` at the storage points."""
+    `rnd` at the storage points; `text` = (K_t, V_t) adds the cross-attention
+    between self-attention and MLP."""
     m, d = len(X), len(X[0])
     N = len(Kc)
     dh = d // H
@@ -165,6 +174,23 @@ def scalar_block(X, I, w, Kc, Vc, H, eps, rnd=lambda v: v):
     for r in range(m):
         proj = [w.b_o[o] + sum(out[r][c] * w.w_o[o][c] for c in range(d)) for o in range(d)]
         X[r] = [X[r][o] + w.mod[2][o] * proj[o] for o in range(d)]
+    if text is not None:
+        Kt, Vt = text
+        T = len(Kt)
+        zero = [0.0] * d
+        h3 = [ln_mod(X[r], zero, zero) for r in range(m)]
+        qc = [[rnd(w.b_qc[o] + sum(h3[r][c] * w.w_qc[o][c] for c in range(d))) for o in range(d)] for r in range(m)]
+        oc = [[0.0] * d for _ in range(m)]
+        for r in range(m):
+            for h in range(H):
+                s = [sum(qc[r][h * dh + c] * Kt[j][h * dh + c] for c in range(dh)) / math.sqrt(dh) for j in range(T)]
+                mx = max(s)
+                e = [math.exp(v - mx) for v in s]
+                tot = sum(e)
+                for c in range(dh):
+                    oc[r][h * dh + c] = rnd(sum(e[j] / tot * Vt[j][h * dh + c] for j in range(T)))
+        for r in range(m):
+            X[r] = [X[r][o] + w.b_oc[o] + sum(oc[r][c] * w.w_oc[o][c] for c in range(d)) for o in range(d)]
     h2 = [ln_mod(X[r], w.mod[3], w.mod[4]) for r in range(m)]
     for r in range(m):
         g = []
@@ -191,6 +217,60 @@ def test_block_against_scalar_formulation(m, N, d, H, F):
     assert np.allclose(Vo, Vw, rtol=1e-12, atol=1e-12)
     untouched = np.setdiff1d(np.arange(N), I)
     assert np.array_equal(Ko[untouched], Kc[untouched])
+
+
+def _text_weights(rng, w, d, std=0.3):
+    w.w_qc, w.b_qc = rng.standard_normal((d, d)) * std, rng.standard_normal(d) * std
+    w.w_kvc, w.b_kvc = rng.standard_normal((2 * d, d)) * std, rng.standard_normal(2 * d) * std
+    w.w_oc, w.b_oc = rng.standard_normal((d, d)) * std, rng.standard_normal(d) * std
+    return w
+
+
+@pytest.mark.parametrize("m,N,T,d,H,F", [(3, 7, 1, 8, 2, 12), (2, 5, 3, 16, 4, 20), (4, 8, 5, 12, 3, 9)])
+def test_block_with_text_against_scalar_formulation(m, N, T, d, H, F):
+    """The text cross-attention (WAM-Cache §3: SA, CA, MLP, each with a
+    residual) against the scalar loops, text keys/values included."""
+    rng = np.random.default_rng(m * 1000 + N * 10 + T)
+    w = _text_weights(rng, _rand_weights(rng, d, F), d)
+    E = rng.standard_normal((T, d))
+    X = rng.standard_normal((m, d))
+    I = np.sort(rng.choice(N, size=m, replace=False))
+    Kc, Vc = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    Kt, Vt = O.text_kv(E, w, F64)
+    Kts, Vts = scalar_text_kv(E.tolist(), w)
+    assert np.allclose(Kt, Kts, rtol=1e-12, atol=1e-12) and np.allclose(Vt, Vts, rtol=1e-12, atol=1e-12)
+    Ko, Vo = Kc.copy(), Vc.copy()
+    got = O.block(X.copy(), I, w, Ko, Vo, H, 1e-6, F64, text=(Kt, Vt))
+    want, Kw, Vw = scalar_block(X, I, w, Kc, Vc, H, 1e-6, text=(Kts, Vts))
+    assert np.allclose(got, want, rtol=1e-11, atol=1e-11)
+    assert np.allclose(Ko, Kw, rtol=1e-12, atol=1e-12)
+
+
+def test_text_cross_attention_special_cases():
+    """A zero output projection leaves the block bitwise as without text; a
+    single text token gives every row the same cross-attention output
+    V_t W_oc^T + b_oc (its softmax weight is 1)."""
+    rng = np.random.default_rng(3)
+    m, N, d, H, F = 4, 9, 12, 3, 10
+    w = _text_weights(rng, _rand_weights(rng, d, F), d)
+    X = rng.standard_normal((m, d))
+    I = np.array([0, 3, 4, 8])
+    Kc, Vc = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    E = rng.standard_normal((3, d))
+    w0 = SimpleNamespace(**vars(w))
+    w0.w_oc, w0.b_oc = np.zeros((d, d)), np.zeros(d)
+    a = O.block(X.copy(), I, w0, Kc.copy(), Vc.copy(), H, 1e-6, F64, text=O.text_kv(E, w0, F64))
+    b = O.block(X.copy(), I, w0, Kc.copy(), Vc.copy(), H, 1e-6, F64)
+    assert np.array_equal(a, b)
+    # single token; MLP switched off (zero weights and biases) so the output
+    # is the post-attention stream plus the cross-attention branch
+    w1 = SimpleNamespace(**vars(w))
+    w1.w_1, w1.b_1, w1.w_2, w1.b_2 = np.zeros_like(w.w_1), np.zeros_like(w.b_1), np.zeros_like(w.w_2), np.zeros_like(w.b_2)
+    Kt, Vt = O.text_kv(E[:1], w1, F64)
+    with_t = O.block(X.copy(), I, w1, Kc.copy(), Vc.copy(), H, 1e-6, F64, text=(Kt, Vt))
+    without = O.block(X.copy(), I, w1, Kc.copy(), Vc.copy(), H, 1e-6, F64)
+    branch = Vt[0] @ w1.w_oc.T + w1.b_oc
+    assert np.allclose(with_t - without, np.repeat(branch[None], m, axis=0), rtol=1e-12, atol=1e-12)
 
 
 def test_block_bf16_storage_points():

@@ -208,3 +208,23 @@ def test_union_rule_chunk():
     assert res.k_eff == N
     assert np.array_equal(st.K, ref.K) and np.array_equal(st.V, ref.V)
     assert all(np.array_equal(a, b) for a, b in zip(res.outs, outs))
+
+
+@pytest.mark.parametrize("name", ["t_fp32_text", "t_bf16_text"])
+def test_text_cross_attention_chunks(name):
+    """With the text cross-attention: k = N from a stale state equals the
+    dense prefill bitwise, and k = 0 leaves the cache untouched (the text
+    keys/values are the episode's, computed once at the dense chunk)."""
+    wl, r, prec = _setup(name)
+    st, _ = O.dense_prefill(r.z[0][0], r.weights, wl.n_heads, wl.ln_eps, prec, text_emb=r.text[0])
+    assert st.text is not None and len(st.text) == wl.n_layers
+    _chunk(wl, st, r, 1, prec)
+    st.age[:] = 0
+    before = st.copy()
+    res = _chunk(wl, st, r, 2, prec, k=0)
+    assert res.k_eff == 0 and np.array_equal(st.K, before.K) and np.array_equal(st.V, before.V)
+    st.age[:] = 0
+    res = _chunk(wl, st, r, 2, prec, k=wl.n_tokens)
+    ref, outs = O.dense_prefill(r.z[0][2], r.weights, wl.n_heads, wl.ln_eps, prec, text_emb=r.text[0])
+    assert np.array_equal(st.K, ref.K) and np.array_equal(st.V, ref.V)
+    assert all(np.array_equal(a, b) for a, b in zip(res.outs, outs))
