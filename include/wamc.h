@@ -85,16 +85,28 @@ typedef struct {
   float ln_eps;         /* LayerNorm epsilon (1e-6) */
   float w_attn;         /* weight of the attention-mass term of the score */
   float w_surprise;     /* weight of the latent-surprise term of the score */
+  int32_t n_text;       /* T instruction tokens of the text cross-attention; 0 = the module has none */
 } wamc_dims;
 
 /* One layer's weights (act dtype), in the [out, in] layout of a linear map.
- * mod rows: shift1, scale1, gate1, shift2, scale2, gate2. */
+ * mod rows: shift1, scale1, gate1, shift2, scale2, gate2.
+ * Text cross-attention (used when dims.n_text > 0, else may be NULL;
+ * WAM-Cache §3: a module is self-attention, a cross-attention to keys and
+ * values projected from the text embeddings, and an MLP, each with a
+ * residual): its queries come from an unmodulated LayerNorm of the rows,
+ * its residual is ungated.  text_k / text_v are this layer's keys and values
+ * of the instruction, [B, T, d] act, caller-owned state written by
+ * wamc_text_kv once per episode (they depend on the instruction only). */
 typedef struct {
   const void *w_qkv, *b_qkv;   /* [3d, d], [3d]; output rows ordered Q, K, V; head h = cols [h*dh,(h+1)*dh) */
   const void *w_o, *b_o;       /* [d, d], [d] */
   const void *w_1, *b_1;       /* [F, d], [F] */
   const void *w_2, *b_2;       /* [d, F], [d] */
   const void *mod;             /* [6, d] */
+  const void *w_qc, *b_qc;     /* [d, d], [d]   cross-attention queries */
+  const void *w_kvc, *b_kvc;   /* [2d, d], [2d] cross-attention keys (rows 0..d-1) and values */
+  const void *w_oc, *b_oc;     /* [d, d], [d]   cross-attention output projection */
+  void *text_k, *text_v;       /* [B, T, d] keys / values of the instruction */
 } wamc_layer_w;
 
 /* Library version (WAMC_VERSION). */
@@ -160,6 +172,8 @@ int wamc_gather(const wamc_dims* dims, const void* z, void* zref, const int32_t*
  *   K[idx[r]] <- Kn[r], V[idx[r]] <- Vn[r]   (before attention);
  *   O = per-head softmax(Q K^T / sqrt(dh)) V over all N cache rows;
  *   x += gate1 * (O W_o^T + b_o);
+ *   with text (dims.n_text = T > 0): Qc = LN(x) W_qc^T + b_qc,
+ *   x += softmax(Qc K_t^T / sqrt(dh)) V_t W_oc^T + b_oc over the T text keys;
  *   x += gate2 * (GELU(H2 W_1^T + b_1) W_2^T + b_2),  H2 = LN(x)*(1+scale2)+shift2
  * LN: no affine, biased variance, eps = dims.ln_eps; GELU: erf form.
  * layer: in [0, L) (bookkeeping only: w and the cache pointers are this layer's).
@@ -221,6 +235,14 @@ int wamc_prefill_chunk_union(const wamc_dims* dims, const wamc_layer_w* layers, 
                              int32_t* age, int32_t n_attn, int32_t n_surprise, int32_t* idx_out,
                              int32_t* k_eff_out, float* layer_out, int32_t rows_cap, void* ws,
                              size_t ws_bytes, void* stream);
+
+/* Text keys and values of every layer from the instruction embeddings
+ * (WAM-Cache §3): layers[l].text_k / text_v <- text W_kvc^T + b_kvc (K then
+ * V halves), rounded to act.  text: [B, T, d] act.  Call once per episode,
+ * before the dense prefill; needs dims.n_text > 0 and every layer's w_kvc,
+ * b_kvc, text_k, text_v.  ws as for rows_cap = T. */
+int wamc_text_kv(const wamc_dims* dims, const wamc_layer_w* layers, const void* text, void* ws, size_t ws_bytes,
+                 void* stream);
 
 /* Dense prefill (WAM-Cache §4.1: the chunk at episode onset): every token
  * through every layer, K/V written for all N tokens, age <- 0, zref <- z.

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -177,6 +178,7 @@ int check_dims(const char* fn, const wamc_dims* d) {
     return fail(WAMC_ERR_UNSUPPORTED, "%s: the bf16 path is built for head_dim 128 (got %d)", fn, d->head_dim);
   if (d->dtype == WAMC_FP32 && d->head_dim > 128)
     return fail(WAMC_ERR_UNSUPPORTED, "%s: the fp32 path supports head_dim <= 128 (got %d)", fn, d->head_dim);
+  if (d->n_text < 0 || d->n_text > (1 << 20)) return fail(WAMC_ERR_ARG, "%s: n_text must be in [0, 2^20]", fn);
   return WAMC_OK;
 }
 
@@ -278,8 +280,18 @@ int hip_status(const char* fn, hipError_t e, hipStream_t s) {
   return WAMC_OK;
 }
 
-int check_layer_w(const char* fn, const wamc_layer_w* w) {
+int check_layer_w(const char* fn, const wamc_layer_w* w, int n_text = 0) {
   if (!w) return fail(WAMC_ERR_ARG, "%s: layer weights are NULL", fn);
+  if (n_text > 0) {
+    REQUIRE_PTR(w->w_qc);
+    REQUIRE_PTR(w->b_qc);
+    REQUIRE_PTR(w->w_kvc);
+    REQUIRE_PTR(w->b_kvc);
+    REQUIRE_PTR(w->w_oc);
+    REQUIRE_PTR(w->b_oc);
+    REQUIRE_PTR(w->text_k);
+    REQUIRE_PTR(w->text_v);
+  }
   REQUIRE_PTR(w->w_qkv);
   REQUIRE_PTR(w->b_qkv);
   REQUIRE_PTR(w->w_o);
@@ -368,6 +380,23 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
   g.resid_in = x_in; g.resid_out = x_out; g.gate = gate1;
   e = launch_gemm(bf16, EPI_RESID_OUT, g, s, tm);
   if (e != hipSuccess) return e;
+
+  if (d->n_text > 0) {
+    // text cross-attention: Qc = LN(x) W_qc^T + b_qc; x += attn(Qc, K_t, V_t) W_oc^T + b_oc
+    e = launch_ln_mod(bf16, x_out, nullptr, nullptr, B, rows_cap, k_eff, D, d->ln_eps, hbuf, ZeroJob{}, s, tm);
+    if (e != hipSuccess) return e;
+    g.a = hbuf; g.w = w->w_qc; g.bias = w->b_qc; g.Nout = D; g.K = D; g.g_out = qbuf;
+    e = launch_gemm(bf16, EPI_STORE, g, s, tm);
+    if (e != hipSuccess) return e;
+    AttnArgs ca = at_;
+    ca.k_cache = w->text_k; ca.v_cache = w->text_v; ca.N = d->n_text;
+    e = launch_attention(bf16, ca, s, tm);
+    if (e != hipSuccess) return e;
+    g.a = hbuf; g.w = w->w_oc; g.bias = w->b_oc; g.Nout = D; g.K = D;
+    g.resid_in = x_out; g.resid_out = x_out; g.gate = nullptr;
+    e = launch_gemm(bf16, EPI_RESID_PLAIN, g, s, tm);
+    if (e != hipSuccess) return e;
+  }
 
   e = launch_ln_mod(bf16, x_out, shift2, scale2, B, rows_cap, k_eff, D, d->ln_eps, hbuf, ZeroJob{}, s, tm);
   if (e != hipSuccess) return e;
@@ -557,7 +586,7 @@ int wamc_refresh_layer(const wamc_dims* dims, int32_t layer, const wamc_layer_w*
   if (st) return st;
   if (layer < 0 || layer >= dims->n_layers)
     return fail(WAMC_ERR_ARG, "%s: layer %d out of range [0, %d)", fn, layer, dims->n_layers);
-  if ((st = check_layer_w(fn, w))) return st;
+  if ((st = check_layer_w(fn, w, dims->n_text))) return st;
   REQUIRE_PTR(x);
   REQUIRE_PTR(k_cache_l);
   REQUIRE_PTR(v_cache_l);
@@ -584,7 +613,7 @@ int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const 
   if (st) return st;
   if (!layers) return fail(WAMC_ERR_ARG, "%s: layers is NULL", fn);
   for (int l = 0; l < dims->n_layers; ++l)
-    if ((st = check_layer_w(fn, &layers[l]))) return st;
+    if ((st = check_layer_w(fn, &layers[l], dims->n_text))) return st;
   REQUIRE_PTR(z);
   REQUIRE_PTR(zref);
   REQUIRE_PTR(k_cache);
@@ -677,7 +706,7 @@ int wamc_prefill_chunk_union(const wamc_dims* dims, const wamc_layer_w* layers, 
   if (st) return st;
   if (!layers) return fail(WAMC_ERR_ARG, "%s: layers is NULL", fn);
   for (int l = 0; l < dims->n_layers; ++l)
-    if ((st = check_layer_w(fn, &layers[l]))) return st;
+    if ((st = check_layer_w(fn, &layers[l], dims->n_text))) return st;
   REQUIRE_PTR(z);
   REQUIRE_PTR(zref);
   REQUIRE_PTR(k_cache);
@@ -712,6 +741,39 @@ int wamc_prefill_chunk_union(const wamc_dims* dims, const wamc_layer_w* layers, 
                                          rows_cap, ws, L, s), s);
 }
 
+int wamc_text_kv(const wamc_dims* dims, const wamc_layer_w* layers, const void* text, void* ws, size_t ws_bytes,
+                 void* stream) {
+  const char* fn = "wamc_text_kv";
+  g_last_error.clear();
+  int st = check_dims(fn, dims);
+  if (st) return st;
+  if (dims->n_text <= 0) return fail(WAMC_ERR_ARG, "%s: dims.n_text must be > 0", fn);
+  if (!layers) return fail(WAMC_ERR_ARG, "%s: layers is NULL", fn);
+  for (int l = 0; l < dims->n_layers; ++l)
+    if ((st = check_layer_w(fn, &layers[l], dims->n_text))) return st;
+  REQUIRE_PTR(text);
+  const int T = dims->n_text;
+  const WsLayout L = ws_layout(dims, std::min(T, dims->n_tokens));
+  if (!ws || ws_bytes < L.total) return fail(WAMC_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, L.total);
+  OPT_PTR(ws);
+  if ((st = check_device(fn))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dims->dtype == WAMC_BF16;
+  hipError_t e = hipSuccess;
+  for (int l = 0; l < dims->n_layers && e == hipSuccess; ++l) {
+    // one GEMM per layer: [B*T, d] x [2d, d]^T, K half -> text_k, V half -> text_v
+    // (plain tiles: no split scratch, so the arrival counters are not needed)
+    GemmArgs g{};
+    g.a = text; g.w = layers[l].w_kvc; g.bias = layers[l].b_kvc;
+    g.M = dims->batch * T; g.Nout = 2 * dims->d_model; g.K = dims->d_model;
+    g.rows_cap = T; g.k_eff = nullptr; g.idx = nullptr;
+    g.n_tokens = T; g.d_model = dims->d_model;
+    g.k_cache = layers[l].text_k; g.v_cache = layers[l].text_v;
+    e = launch_gemm(bf16, EPI_KV, g, s, active_timer());
+  }
+  return hip_status(fn, e, s);
+}
+
 int wamc_dense_prefill(const wamc_dims* dims, const wamc_layer_w* layers, const void* z, void* zref,
                        void* k_cache, void* v_cache, int32_t* age, float* layer_out, void* ws, size_t ws_bytes,
                        void* stream) {
@@ -721,7 +783,7 @@ int wamc_dense_prefill(const wamc_dims* dims, const wamc_layer_w* layers, const 
   if (st) return st;
   if (!layers) return fail(WAMC_ERR_ARG, "%s: layers is NULL", fn);
   for (int l = 0; l < dims->n_layers; ++l)
-    if ((st = check_layer_w(fn, &layers[l]))) return st;
+    if ((st = check_layer_w(fn, &layers[l], dims->n_text))) return st;
   REQUIRE_PTR(z);
   REQUIRE_PTR(zref);
   REQUIRE_PTR(k_cache);

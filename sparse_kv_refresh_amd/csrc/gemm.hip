@@ -10,7 +10,10 @@
 //   EPI_QKV   : Q -> q_out (act), K/V -> written straight into this layer's
 //               cache at the row's token index (the scatter is fused here);
 //   EPI_RESID_OUT / EPI_RESID_DOWN : out = in + gate * v   (gated residual, f32 stream);
-//   EPI_GELU  : g = act(GELU_erf(v)).
+//   EPI_GELU  : g = act(GELU_erf(v));
+//   EPI_KV    : text keys/values of the cross-attention (K -> k_cache, V -> v_cache rows);
+//   EPI_STORE : g = act(v)  (the cross-attention queries);
+//   EPI_RESID_PLAIN : out = in + v  (the ungated cross-attention residual).
 //
 // bf16 path (K % 64 == 0): BM x BN tiles (128x128, 128x256 or 256x128,
 // picked per GEMM shape), 4 waves in a 2x2 layout, each wave (BM/2) x (BN/2)
@@ -34,6 +37,18 @@ namespace wamc {
 // shared epilogue
 // ---------------------------------------------------------------------------
 
+// Runs CALL with the compile-time epilogue E of the run-time kind epi.
+#define WAMC_EPI_DISPATCH(epi, CALL)                                      \
+  switch (epi) {                                                          \
+    case EPI_QKV: { constexpr int E = EPI_QKV; CALL; } break;             \
+    case EPI_RESID_OUT: { constexpr int E = EPI_RESID_OUT; CALL; } break; \
+    case EPI_GELU: { constexpr int E = EPI_GELU; CALL; } break;           \
+    case EPI_RESID_DOWN: { constexpr int E = EPI_RESID_DOWN; CALL; } break; \
+    case EPI_KV: { constexpr int E = EPI_KV; CALL; } break;               \
+    case EPI_STORE: { constexpr int E = EPI_STORE; CALL; } break;         \
+    case EPI_RESID_PLAIN: { constexpr int E = EPI_RESID_PLAIN; CALL; } break; \
+  }
+
 struct RowInfo {
   bool valid;
   int b, r;
@@ -51,9 +66,10 @@ template <int EPI, typename T>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, const RowInfo& ri, int m, int n, float acc) {
   if (!ri.valid || n >= g.Nout) return;
   const float v = acc + Elem<T>::load(static_cast<const T*>(g.bias), n);
-  if constexpr (EPI == EPI_QKV) {
+  if constexpr (EPI == EPI_QKV || EPI == EPI_KV) {
     const int d = g.d_model;
-    const int which = n / d, c = n - which * d;
+    const int wr = n / d, c = n - wr * d;
+    const int which = wr + (EPI == EPI_KV ? 1 : 0);
     if (which == 0) {
       Elem<T>::store(static_cast<T*>(g.q_out), static_cast<size_t>(m) * d + c, v);
     } else {
@@ -65,6 +81,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const RowInfo& ri, i
   } else if constexpr (EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN) {
     const size_t o = static_cast<size_t>(m) * g.Nout + n;
     g.resid_out[o] = g.resid_in[o] + Elem<T>::load(static_cast<const T*>(g.gate), n) * v;
+  } else if constexpr (EPI == EPI_RESID_PLAIN) {
+    const size_t o = static_cast<size_t>(m) * g.Nout + n;
+    g.resid_out[o] = g.resid_in[o] + v;
+  } else if constexpr (EPI == EPI_STORE) {
+    Elem<T>::store(static_cast<T*>(g.g_out), static_cast<size_t>(m) * g.Nout + n, v);
   } else {
     Elem<T>::store(static_cast<T*>(g.g_out), static_cast<size_t>(m) * g.Nout + n, gelu_erf(v));
   }
@@ -128,7 +149,7 @@ __device__ __forceinline__ void fill_row_table(const GemmArgs& g, int m0, int* t
     int r0 = -1, r1 = -1;
     if (ri.valid && m < mend) {
       r0 = m;
-      if constexpr (EPI == EPI_QKV) {
+      if constexpr (EPI == EPI_QKV || EPI == EPI_KV) {
         const int tok = g.idx ? g.idx[static_cast<size_t>(ri.b) * g.n_tokens + ri.r] : ri.r;
         r1 = (tok >= 0 && tok < g.n_tokens) ? ri.b * g.n_tokens + tok : -1;
       }
@@ -158,19 +179,21 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t 
     __builtin_amdgcn_sched_barrier(0);
     const int lr = wm * WTM + i * 32 + col;
     const int rq = tab[lr];
-    if constexpr (EPI == EPI_QKV) {
+    if constexpr (EPI == EPI_QKV || EPI == EPI_KV) {
       const int rkv = tab[BM + lr];
       const int d = g.d_model;
       // a tile crosses at most one of the Q|K|V boundaries (d >= BN / 2... and
       // d >= 128 in the bf16 path; BN <= 256 <= 2d)
       const int which0 = n0 / d, edge = (which0 + 1) * d;
+      constexpr int kOff = EPI == EPI_KV ? 1 : 0;   // EPI_KV has no Q columns
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
           const int n = n0 + wn * WTN + j * 32 + gg * 8 + half * 4;
           if (!full_n && n >= g.Nout) continue;
-          const int which = which0 + (n >= edge ? 1 : 0), c = n - which * d;
+          const int wr = which0 + (n >= edge ? 1 : 0), c = n - wr * d;
+          const int which = wr + kOff;
           const int r = which == 0 ? rq : rkv;
           if (r < 0) continue;
           const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
@@ -182,7 +205,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t 
           bf16_t* dst = static_cast<bf16_t*>(which == 0 ? g.q_out : (which == 1 ? g.k_cache : g.v_cache));
           *reinterpret_cast<uint2*>(dst + static_cast<size_t>(r) * d + c) = w;
         }
-    } else if constexpr (EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN) {
+    } else if constexpr (EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN || EPI == EPI_RESID_PLAIN) {
       if (rq < 0) continue;
       const bf16_t* gate = static_cast<const bf16_t*>(g.gate);
 #pragma unroll
@@ -192,7 +215,9 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t 
           const int n = n0 + wn * WTN + j * 32 + gg * 8 + half * 4;
           if (!full_n && n >= g.Nout) continue;
           const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
-          const uint2 gt = *reinterpret_cast<const uint2*>(gate + n);
+          // EPI_RESID_PLAIN: ungated (gate 1.0 = 0x3f80 in bf16)
+          const uint2 gt = EPI == EPI_RESID_PLAIN ? make_uint2(0x3f803f80u, 0x3f803f80u)
+                                                  : *reinterpret_cast<const uint2*>(gate + n);
           const size_t o = static_cast<size_t>(rq) * g.Nout + n;
           const float4 xin = *reinterpret_cast<const float4*>(g.resid_in + o);
           float4 xo;
@@ -213,10 +238,18 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t 
           if (!full_n && n >= g.Nout) continue;
           const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
           uint2 w;
-          w.x = pack_bf16x2(gelu_erf_fast(acc[i][j][4 * gg + 0] + __uint_as_float(bb.x << 16)),
-                            gelu_erf_fast(acc[i][j][4 * gg + 1] + __uint_as_float(bb.x & 0xffff0000u)));
-          w.y = pack_bf16x2(gelu_erf_fast(acc[i][j][4 * gg + 2] + __uint_as_float(bb.y << 16)),
-                            gelu_erf_fast(acc[i][j][4 * gg + 3] + __uint_as_float(bb.y & 0xffff0000u)));
+          float v0 = acc[i][j][4 * gg + 0] + __uint_as_float(bb.x << 16);
+          float v1 = acc[i][j][4 * gg + 1] + __uint_as_float(bb.x & 0xffff0000u);
+          float v2 = acc[i][j][4 * gg + 2] + __uint_as_float(bb.y << 16);
+          float v3 = acc[i][j][4 * gg + 3] + __uint_as_float(bb.y & 0xffff0000u);
+          if constexpr (EPI == EPI_GELU) {
+            v0 = gelu_erf_fast(v0);
+            v1 = gelu_erf_fast(v1);
+            v2 = gelu_erf_fast(v2);
+            v3 = gelu_erf_fast(v3);
+          }
+          w.x = pack_bf16x2(v0, v1);
+          w.y = pack_bf16x2(v2, v3);
           *reinterpret_cast<uint2*>(out + static_cast<size_t>(rq) * g.Nout + n) = w;
         }
     }
@@ -910,12 +943,7 @@ static void launch_sk(GemmEpi epi, const GemmArgs& g, hipStream_t s) {
   // one workgroup per tile at the most rows; at least P so few tiles can be split
   const unsigned grid = static_cast<unsigned>(std::max<long long>(tiles_cap, Cfg::kP));
   constexpr int NT = Cfg::kThreads;
-  switch (epi) {
-    case EPI_QKV: gemm_bf16_sk_kernel<EPI_QKV, BM, BN, BK, STAGES, WGM, WGN><<<grid, NT, 0, s>>>(g); break;
-    case EPI_RESID_OUT: gemm_bf16_sk_kernel<EPI_RESID_OUT, BM, BN, BK, STAGES, WGM, WGN><<<grid, NT, 0, s>>>(g); break;
-    case EPI_RESID_DOWN: gemm_bf16_sk_kernel<EPI_RESID_DOWN, BM, BN, BK, STAGES, WGM, WGN><<<grid, NT, 0, s>>>(g); break;
-    case EPI_GELU: gemm_bf16_sk_kernel<EPI_GELU, BM, BN, BK, STAGES, WGM, WGN><<<grid, NT, 0, s>>>(g); break;
-  }
+  WAMC_EPI_DISPATCH(epi, (gemm_bf16_sk_kernel<E, BM, BN, BK, STAGES, WGM, WGN><<<grid, NT, 0, s>>>(g)));
 }
 
 // ---------------------------------------------------------------------------
@@ -971,20 +999,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 
 static const char* gemm_name(const GemmArgs& g, GemmEpi e) {
-  if (e == EPI_QKV) return "gemm_qkv";
-  if (e == EPI_GELU) return "gemm_up_gelu";
-  return e == EPI_RESID_OUT ? "gemm_out_resid" : "gemm_down_resid";
+  switch (e) {
+    case EPI_QKV: return "gemm_qkv";
+    case EPI_GELU: return "gemm_up_gelu";
+    case EPI_RESID_OUT: return "gemm_out_resid";
+    case EPI_RESID_DOWN: return "gemm_down_resid";
+    case EPI_KV: return "gemm_text_kv";
+    case EPI_STORE: return "gemm_ca_q";
+    default: return "gemm_ca_out";
+  }
 }
 
 template <int BM, int BN, int BK, int STAGES>
 static void launch_dtl(GemmEpi epi, const GemmArgs& g, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(((g.M + BM - 1) / BM) * ((g.Nout + BN - 1) / BN));
-  switch (epi) {
-    case EPI_QKV: gemm_bf16_dtl_kernel<EPI_QKV, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
-    case EPI_RESID_OUT: gemm_bf16_dtl_kernel<EPI_RESID_OUT, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
-    case EPI_RESID_DOWN: gemm_bf16_dtl_kernel<EPI_RESID_DOWN, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
-    case EPI_GELU: gemm_bf16_dtl_kernel<EPI_GELU, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g); break;
-  }
+  WAMC_EPI_DISPATCH(epi, (gemm_bf16_dtl_kernel<E, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g)));
 }
 
 #ifndef WAMC_GEMM_TILE
@@ -1031,12 +1060,7 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
     launch_sk<WAMC_SK_BM, WAMC_SK_BN, WAMC_SK_BK, WAMC_SK_STAGES, 2, 2>(epi, g, s);
   } else if (use_ks2) {
     const unsigned grid = static_cast<unsigned>(t128);
-    switch (epi) {
-      case EPI_QKV: gemm_bf16_dtl_ks2_kernel<EPI_QKV, 64, 2><<<grid, kKs2Threads, 0, s>>>(g); break;
-      case EPI_RESID_OUT: gemm_bf16_dtl_ks2_kernel<EPI_RESID_OUT, 64, 2><<<grid, kKs2Threads, 0, s>>>(g); break;
-      case EPI_RESID_DOWN: gemm_bf16_dtl_ks2_kernel<EPI_RESID_DOWN, 64, 2><<<grid, kKs2Threads, 0, s>>>(g); break;
-      case EPI_GELU: gemm_bf16_dtl_ks2_kernel<EPI_GELU, 64, 2><<<grid, kKs2Threads, 0, s>>>(g); break;
-    }
+    WAMC_EPI_DISPATCH(epi, (gemm_bf16_dtl_ks2_kernel<E, 64, 2><<<grid, kKs2Threads, 0, s>>>(g)));
   } else if (dtl_ok) {
     switch (pick_tile(g)) {
       case 2: launch_dtl<128, 256, 32, 3>(epi, g, s); break;
@@ -1047,20 +1071,10 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
     }
   } else if (bf16) {
     const unsigned grid = static_cast<unsigned>(((g.M + kBM - 1) / kBM) * ((g.Nout + kBN - 1) / kBN));
-    switch (epi) {
-      case EPI_QKV: gemm_bf16_kernel<EPI_QKV><<<grid, kGemmThreads, 0, s>>>(g); break;
-      case EPI_RESID_OUT: gemm_bf16_kernel<EPI_RESID_OUT><<<grid, kGemmThreads, 0, s>>>(g); break;
-      case EPI_RESID_DOWN: gemm_bf16_kernel<EPI_RESID_DOWN><<<grid, kGemmThreads, 0, s>>>(g); break;
-      case EPI_GELU: gemm_bf16_kernel<EPI_GELU><<<grid, kGemmThreads, 0, s>>>(g); break;
-    }
+    WAMC_EPI_DISPATCH(epi, (gemm_bf16_kernel<E><<<grid, kGemmThreads, 0, s>>>(g)));
   } else {
     const unsigned grid = static_cast<unsigned>(((g.M + kFBM - 1) / kFBM) * ((g.Nout + kFBN - 1) / kFBN));
-    switch (epi) {
-      case EPI_QKV: gemm_f32_kernel<EPI_QKV><<<grid, 256, 0, s>>>(g); break;
-      case EPI_RESID_OUT: gemm_f32_kernel<EPI_RESID_OUT><<<grid, 256, 0, s>>>(g); break;
-      case EPI_RESID_DOWN: gemm_f32_kernel<EPI_RESID_DOWN><<<grid, 256, 0, s>>>(g); break;
-      case EPI_GELU: gemm_f32_kernel<EPI_GELU><<<grid, 256, 0, s>>>(g); break;
-    }
+    WAMC_EPI_DISPATCH(epi, (gemm_f32_kernel<E><<<grid, 256, 0, s>>>(g)));
   }
   return hipGetLastError();
 }

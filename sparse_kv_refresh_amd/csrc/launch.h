@@ -88,7 +88,8 @@ hipError_t launch_gather_ln(bool bf16, const void* z, void* zref, const int32_t*
                             int N, int d, int rows_cap, float* x, int32_t* age_zero, const void* shift,
                             const void* scale, float eps, void* h, const ZeroJob& zj, hipStream_t s,
                             KernelTimer* timer);
-// h[m] = act(LN(x_in[m]) * (1 + scale) + shift) for valid rows.
+// h[m] = act(LN(x_in[m]) * (1 + scale) + shift) for valid rows (shift == scale
+// == nullptr: act(LN(x_in[m]))).
 hipError_t launch_ln_mod(bool bf16, const float* x, const void* shift, const void* scale, int B,
                          int rows_cap, const int32_t* k_eff, int d, float eps, void* h, const ZeroJob& zj,
                          hipStream_t s, KernelTimer* timer);
@@ -96,7 +97,11 @@ hipError_t launch_ln_mod(bool bf16, const float* x, const void* shift, const voi
 // ----- GEMM (gemm.hip) -----
 // EPI_RESID_OUT and EPI_RESID_DOWN share one epilogue; they are separate
 // instances so profilers tell the two projections apart.
-enum GemmEpi { EPI_QKV = 0, EPI_RESID_OUT = 1, EPI_GELU = 2, EPI_RESID_DOWN = 3 };
+// EPI_KV: the text keys/values (cols [0,d) -> k_cache row, [d,2d) -> v_cache row);
+// EPI_STORE: act(acc + bias) to g_out; EPI_RESID_PLAIN: out = in + (acc + bias).
+enum GemmEpi {
+  EPI_QKV = 0, EPI_RESID_OUT = 1, EPI_GELU = 2, EPI_RESID_DOWN = 3, EPI_KV = 4, EPI_STORE = 5, EPI_RESID_PLAIN = 6
+};
 struct GemmArgs {
   const void* a;        // [M, K] act, row-major
   const void* w;        // [Nout, K] act, row-major (linear-layer layout)

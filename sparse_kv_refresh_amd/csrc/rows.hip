@@ -167,9 +167,10 @@ hipError_t launch_gather_ln(bool bf16, const void* z, void* zref, const int32_t*
   return hipGetLastError();
 }
 
-// LayerNorm without affine (biased variance), then *(1 + scale) + shift,
-// rounded to the activation type.
-template <typename T>
+// LayerNorm without affine (biased variance), then *(1 + scale) + shift
+// (MOD; without: the plain normalisation, as the cross-attention queries
+// use), rounded to the activation type.
+template <typename T, bool MOD>
 __global__ __launch_bounds__(kRowThreads) void ln_mod_kernel(
     const float* __restrict__ x, const T* __restrict__ shift, const T* __restrict__ scale,
     int rows_cap, const int32_t* __restrict__ k_eff, int d, float eps, T* __restrict__ h, ZeroJob zj) {
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(kRowThreads) void ln_mod_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float n = (vv[i] - mean) * rstd;
-      const float y = n * (1.0f + Elem<T>::load(scale, c + i)) + Elem<T>::load(shift, c + i);
+      const float y = MOD ? n * (1.0f + Elem<T>::load(scale, c + i)) + Elem<T>::load(shift, c + i) : n;
       Elem<T>::store(hr, c + i, y);
     }
   }
@@ -212,12 +213,19 @@ hipError_t launch_ln_mod(bool bf16, const float* x, const void* shift, const voi
                          hipStream_t s, KernelTimer* timer) {
   TimedLaunch t(timer, "ln_mod", s);
   const dim3 grid((rows_cap + 3) / 4, B);
-  if (bf16)
-    ln_mod_kernel<bf16_t><<<grid, kRowThreads, 0, s>>>(x, static_cast<const bf16_t*>(shift),
+  const bool mod = shift != nullptr;
+  if (bf16 && mod)
+    ln_mod_kernel<bf16_t, true><<<grid, kRowThreads, 0, s>>>(x, static_cast<const bf16_t*>(shift),
         static_cast<const bf16_t*>(scale), rows_cap, k_eff, d, eps, static_cast<bf16_t*>(h), zj);
-  else
-    ln_mod_kernel<float><<<grid, kRowThreads, 0, s>>>(x, static_cast<const float*>(shift),
+  else if (bf16)
+    ln_mod_kernel<bf16_t, false><<<grid, kRowThreads, 0, s>>>(x, nullptr, nullptr, rows_cap, k_eff, d, eps,
+        static_cast<bf16_t*>(h), zj);
+  else if (mod)
+    ln_mod_kernel<float, true><<<grid, kRowThreads, 0, s>>>(x, static_cast<const float*>(shift),
         static_cast<const float*>(scale), rows_cap, k_eff, d, eps, static_cast<float*>(h), zj);
+  else
+    ln_mod_kernel<float, false><<<grid, kRowThreads, 0, s>>>(x, nullptr, nullptr, rows_cap, k_eff, d, eps,
+        static_cast<float*>(h), zj);
   return hipGetLastError();
 }
 

@@ -34,12 +34,15 @@ class Dims(ctypes.Structure):
                 ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("d_ffn", ctypes.c_int32),
                 ("n_tokens", ctypes.c_int32), ("n_action", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("age_bound", ctypes.c_int32), ("ln_eps", ctypes.c_float), ("w_attn", ctypes.c_float),
-                ("w_surprise", ctypes.c_float)]
+                ("w_surprise", ctypes.c_float), ("n_text", ctypes.c_int32)]
+
+
+LAYER_FIELDS = ("w_qkv", "b_qkv", "w_o", "b_o", "w_1", "b_1", "w_2", "b_2", "mod",
+                "w_qc", "b_qc", "w_kvc", "b_kvc", "w_oc", "b_oc", "text_k", "text_v")
 
 
 class LayerW(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_qkv", "b_qkv", "w_o", "b_o", "w_1", "b_1", "w_2", "b_2", "mod")]
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_FIELDS]
 
 
 _P = ctypes.c_void_p
@@ -62,6 +65,7 @@ _SIGNATURES = {
     "wamc_select_union": ([_DP, _P, _P, _P, _I, _I, _P, _P, _P, _P], ctypes.c_int),
     "wamc_prefill_chunk_union": ([_DP, _LP, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _SZ, _P],
                                  ctypes.c_int),
+    "wamc_text_kv": ([_DP, _LP, _P, _P, _SZ, _P], ctypes.c_int),
     "wamc_dense_prefill": ([_DP, _LP, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "wamc_timing_enable": ([ctypes.c_int], ctypes.c_int),
     "wamc_timing_count": ([], ctypes.c_int),
@@ -126,20 +130,22 @@ def act_dtype(dims: Dims) -> torch.dtype:
 
 
 def make_dims(batch, n_layers, d_model, n_heads, d_ffn, n_tokens, n_action, dtype, age_bound,
-              ln_eps=1e-6, w_attn=0.4, w_surprise=0.1) -> Dims:
+              ln_eps=1e-6, w_attn=0.4, w_surprise=0.1, n_text=0) -> Dims:
     dt = {"fp32": WAMC_FP32, "bf16": WAMC_BF16}.get(dtype, dtype)
     return Dims(batch, n_layers, d_model, n_heads, d_model // n_heads, d_ffn, n_tokens, n_action, dt,
-                age_bound, ln_eps, w_attn, w_surprise)
+                age_bound, ln_eps, w_attn, w_surprise, n_text)
 
 
 def dims_for(wl) -> Dims:
     """Dims of a workload description (sparse_kv_refresh_amd.inputs.Workload)."""
     return make_dims(wl.batch, wl.n_layers, wl.d_model, wl.n_heads, wl.d_ffn, wl.n_tokens, wl.n_action,
-                     wl.dtype, wl.age_bound, wl.ln_eps, wl.w_attn, wl.w_surprise)
+                     wl.dtype, wl.age_bound, wl.ln_eps, wl.w_attn, wl.w_surprise, getattr(wl, "n_text", 0))
 
 
 def layer_struct(w: dict) -> LayerW:
-    return LayerW(*[_ptr(w[n]) for n in ("w_qkv", "b_qkv", "w_o", "b_o", "w_1", "b_1", "w_2", "b_2", "mod")])
+    """One layer's pointers; the text cross-attention fields stay NULL when
+    the dict has none."""
+    return LayerW(*[_ptr(w.get(n)) for n in LAYER_FIELDS])
 
 
 def _layers(layers: Sequence[dict]):
@@ -217,6 +223,11 @@ def prefill_chunk_union(dims, layers: Sequence[dict], z, zref, q_act, k_cache, v
                                           _stream(stream)))
 
 
+def text_kv(dims, layers: Sequence[dict], text, ws, stream=None, _layer_array=None):
+    arr = _layer_array if _layer_array is not None else _layers(layers)
+    _check(lib().wamc_text_kv(ctypes.byref(dims), arr, _ptr(text), _ptr(ws), ws.numel(), _stream(stream)))
+
+
 def dense_prefill(dims, layers: Sequence[dict], z, zref, k_cache, v_cache, age, ws, layer_out=None, stream=None,
                   _layer_array=None):
     arr = _layer_array if _layer_array is not None else _layers(layers)
@@ -256,7 +267,14 @@ class Engine:
         self.rows_cap = rows_cap
         B, L, N, d = dims.batch, dims.n_layers, dims.n_tokens, dims.d_model
         adt = act_dtype(dims)
-        self.weights = list(weights)
+        self.weights = [dict(w) for w in weights]
+        T = dims.n_text
+        if T > 0:
+            # per-layer keys/values of the instruction, written by text_kv()
+            self.text_k = torch.zeros((L, B, T, d), dtype=adt, device=self.device)
+            self.text_v = torch.zeros((L, B, T, d), dtype=adt, device=self.device)
+            for l, w in enumerate(self.weights):
+                w["text_k"], w["text_v"] = self.text_k[l], self.text_v[l]
         self.layer_array = _layers(self.weights)
         self.k_cache = torch.zeros((L, B, N, d), dtype=adt, device=self.device)
         self.v_cache = torch.zeros((L, B, N, d), dtype=adt, device=self.device)
@@ -270,9 +288,14 @@ class Engine:
 
     @staticmethod
     def upload_weights(np_layers, dtype: torch.dtype, device="cuda") -> List[dict]:
-        names = ("w_qkv", "b_qkv", "w_o", "b_o", "w_1", "b_1", "w_2", "b_2", "mod")
-        return [{n: torch.from_numpy(getattr(w, n)).to(device=device, dtype=dtype).contiguous() for n in names}
-                for w in np_layers]
+        names = LAYER_FIELDS[:15]
+        return [{n: torch.from_numpy(getattr(w, n)).to(device=device, dtype=dtype).contiguous() for n in names
+                 if getattr(w, n, None) is not None} for w in np_layers]
+
+    def text_kv(self, text, stream=None):
+        """The instruction's keys/values for every layer (once per episode,
+        before the dense chunk).  text: [B, T, d]."""
+        text_kv(self.dims, self.weights, text, self.ws, stream=stream, _layer_array=self.layer_array)
 
     def dense(self, z, layer_out=None, stream=None):
         dense_prefill(self.dims, self.weights, z, self.zref, self.k_cache, self.v_cache, self.age, self.ws,

@@ -43,9 +43,14 @@ def close(wl, g, o):
 
 
 def engine(wl, rollout, rows_cap=None):
+    """An engine for the workload; with instruction tokens, the text
+    keys/values are computed right away (as at episode onset)."""
     dims = wamc.dims_for(wl)
     weights = wamc.Engine.upload_weights(rollout.weights, act(wl), DEV)
-    return wamc.Engine(dims, weights, rows_cap or wl.n_tokens, DEV)
+    eng = wamc.Engine(dims, weights, rows_cap or wl.n_tokens, DEV)
+    if getattr(rollout, "text", None) is not None:
+        eng.text_kv(to_dev(np.stack(rollout.text), act(wl)))
+    return eng
 
 
 def batch_z(wl, rollout, t):

@@ -27,7 +27,8 @@ pytestmark = pytest.mark.gpu
 def _oracle_states(wl, r, prec):
     out = []
     for e in range(wl.batch):
-        st, _ = O.dense_prefill(r.z[e][0], r.weights, wl.n_heads, wl.ln_eps, prec)
+        st, _ = O.dense_prefill(r.z[e][0], r.weights, wl.n_heads, wl.ln_eps, prec,
+                                text_emb=None if r.text is None else r.text[e])
         st.age = r.ages0[e].astype(np.int64)
         out.append(st)
     return out
@@ -71,7 +72,8 @@ def _run_override_rollout(wl, chunks):
         _compare_chunk(wl, eng, states, res, lo, t)
 
 
-@pytest.mark.parametrize("name", ["c1_tiny", "t_fp32_ragged", "t_bf16_small", "t_bf16_batch"])
+@pytest.mark.parametrize("name", ["c1_tiny", "t_fp32_ragged", "t_bf16_small", "t_bf16_batch", "t_bf16_text",
+                                  "t_fp32_text"])
 def test_rollout_oracle_refresh_set(name):
     wl = W.preset(name)
     _run_override_rollout(wl, wl.chunks)
@@ -145,7 +147,7 @@ def test_own_selection_rollout(name):
         assert int(eng.age.max()) <= wl.age_bound
 
 
-@pytest.mark.parametrize("name", ["c1_tiny", "t_bf16_small"])
+@pytest.mark.parametrize("name", ["c1_tiny", "t_bf16_small", "t_bf16_text"])
 def test_full_refresh_equals_dense_on_gpu(name):
     wl = W.preset(name)
     r = W.make_rollout(wl, chunks=3)

@@ -14,7 +14,8 @@ from gpu_util import DEV, act, batch_z, close, engine, to_dev, to_np
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["c1_tiny", "t_fp32_ragged", "t_bf16_small", "t_bf16_batch"])
+@pytest.mark.parametrize("name", ["c1_tiny", "t_fp32_ragged", "t_bf16_small", "t_bf16_batch", "t_bf16_text",
+                                  "t_fp32_text"])
 def test_dense_parity(name):
     wl = W.preset(name)
     r = W.make_rollout(wl, chunks=1)
@@ -29,7 +30,8 @@ def test_dense_parity(name):
     assert (eng.age == 0).all()
     assert torch.equal(eng.zref, z0)
     for b in range(B):
-        st, outs = O.dense_prefill(r.z[b][0], r.weights, wl.n_heads, wl.ln_eps, prec)
+        st, outs = O.dense_prefill(r.z[b][0], r.weights, wl.n_heads, wl.ln_eps, prec,
+                                   text_emb=None if r.text is None else r.text[b])
         for l in range(L):
             for name_, g, o in (("K", eng.k_cache[l, b], st.K[l]), ("V", eng.v_cache[l, b], st.V[l]),
                                 ("X", lo[l, b], outs[l])):

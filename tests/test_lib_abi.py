@@ -142,3 +142,22 @@ def test_union_entry_points_validate():
     st = L.wamc_prefill_chunk_union(ctypes.byref(d), arr, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, 5, FAKE,
                                     FAKE, None, N, FAKE, ws - 1, None)
     assert st == 3
+
+
+def test_text_cross_attention_validates():
+    """With instruction tokens every layer needs its cross-attention weights
+    and text caches; wamc_text_kv needs n_text > 0."""
+    L = wamc.lib()
+    d = _dims(n_text=12)
+    lw = wamc.LayerW(*([FAKE] * 9 + [None] * 8))
+    ws = wamc.workspace_bytes(d, 100)
+    assert L.wamc_refresh_layer(ctypes.byref(d), 0, ctypes.byref(lw), FAKE, FAKE, FAKE, 100, FAKE, FAKE,
+                                FAKE, ws, None) == 1
+    assert b"w_qc" in L.wamc_last_error()
+    full = wamc.LayerW(*([FAKE] * 17))
+    arr = (wamc.LayerW * d.n_layers)(*([full] * d.n_layers))
+    d0 = _dims()
+    assert L.wamc_text_kv(ctypes.byref(d0), arr, FAKE, FAKE, ws, None) == 1
+    assert L.wamc_text_kv(ctypes.byref(d), arr, None, FAKE, ws, None) == 1
+    d.n_text = -1
+    assert L.wamc_workspace_bytes(ctypes.byref(d), 10, ctypes.byref(ctypes.c_size_t())) == 1
