@@ -69,16 +69,22 @@ def parse():
 
 def kernel_work(wl, k_eff_total: int):
     """Algorithmic work per launch of each kernel kind: FLOPs for the MFMA
-    kernels, HBM bytes for the memory-bound ones (act = 2 bytes in bf16)."""
+    kernels, HBM bytes for the memory-bound ones (act = 2 bytes in bf16).
+    With a text cross-attention the attention kind holds two launches per
+    layer (over N keys and over T text keys); its figure is their mean."""
     L, B, N, d, F, H, A = wl.n_layers, wl.batch, wl.n_tokens, wl.d_model, wl.d_ffn, wl.n_heads, wl.n_action
+    T = getattr(wl, "n_text", 0)
     M = k_eff_total
     es = 2 if wl.dtype == "bf16" else 4
+    attn = 4.0 * M * N * d if T == 0 else 0.5 * (4.0 * M * N * d + 4.0 * M * T * d)
     return {
+        "gemm_ca_q": ("flop", 2.0 * M * d * d),
+        "gemm_ca_out": ("flop", 2.0 * M * d * d),
         "gemm_qkv": ("flop", 2.0 * M * 3 * d * d),
         "gemm_out_resid": ("flop", 2.0 * M * d * d),
         "gemm_up_gelu": ("flop", 2.0 * M * F * d),
         "gemm_down_resid": ("flop", 2.0 * M * d * F),
-        "attention": ("flop", 4.0 * M * N * d),
+        "attention": ("flop", attn),
         # K cache once (+ queries) per pass
         "score_pass1": ("byte", float(L * B * N * d * es + L * B * A * d * es)),
         "score_pass2": ("byte", float(L * B * N * d * es + L * B * A * d * es + L * H * B * N * 4)),
@@ -131,7 +137,8 @@ def cpu_baseline(wl, seconds: float):
     r = W.make_rollout(swl, chunks=2)
     prec = O.Precision(wl.dtype)
     t0 = time.perf_counter()
-    st, _ = O.dense_prefill(r.z[0][0], r.weights, wl.n_heads, wl.ln_eps, prec)
+    st, _ = O.dense_prefill(r.z[0][0], r.weights, wl.n_heads, wl.ln_eps, prec,
+                            text_emb=None if r.text is None else r.text[0])
     dense_s = time.perf_counter() - t0
     st.age = r.ages0[0].astype(np.int64)
     times = []
@@ -515,6 +522,9 @@ def main():
     weights = wamc.Engine.upload_weights(r.weights, adt, dev)
     rows_cap = wl.k if wl.k >= (wl.n_tokens + 1) // 2 else wl.n_tokens
     eng = wamc.Engine(dims, weights, rows_cap, dev)
+    if r.text is not None:
+        # the instruction's keys/values, once per episode (outside the timed steps)
+        eng.text_kv(torch.from_numpy(np.stack(r.text)).to(dev, adt).contiguous())
 
     def bz(t):
         return torch.from_numpy(np.stack([r.z[e][t] for e in range(wl.batch)])).to(dev, adt).contiguous()

@@ -86,6 +86,10 @@ PRESETS: Dict[str, Workload] = {
     # 30-layer bf16 stack, 3 views x 30x52 = 4680 tokens, k = 60 %.
     "c3_stack": Workload("c3_stack", 30, 1536, 12, 8960, 3, 30, 52, 64, 2808, 3, "bf16",
                          chunks=16, latent="stack"),
+    # the 30-layer stack with the module's text cross-attention over 128
+    # instruction tokens
+    "c3_text": Workload("c3_text", 30, 1536, 12, 8960, 3, 30, 52, 64, 2808, 3, "bf16",
+                        chunks=16, latent="stack", n_text=128),
     # 20-layer d=3072 bf16, 2 views x 64x64 = 8192 tokens, 4 episodes, k = 50 %.
     "c5_large": Workload("c5_large", 20, 3072, 24, 12288, 2, 64, 64, 128, 4096, 4, "bf16",
                          batch=4, chunks=8, latent="episodes"),
