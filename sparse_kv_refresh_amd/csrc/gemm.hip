@@ -170,88 +170,91 @@ __device__ __forceinline__ void fill_row_table(const GemmArgs& g, int m0, int* t
 template <int EPI, int BM, int BN, int TI, int TJ, int WTM = BM / 2, int WTN = BN / 2>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t (&acc)[TI][TJ], int m0, int n0,
                                               int wm, int wn, int half, int col, const int* tab) {
-  const bool full_n = n0 + BN <= g.Nout;   // Nout % 4 == 0: groups never straddle Nout
+  (void)m0;
+  // The lane's TJ*4 column groups.  Nout % 4 == 0, so a group lies wholly
+  // inside or outside [0, Nout); groups outside read column 0 (valid memory)
+  // and store nothing.  Every load is unconditional, so all of a row block's
+  // loads are in flight together instead of one round trip per group.
+  constexpr int NG = TJ * 4;
   const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
+  int ncol[NG];
+  bool nok[NG];
+  uint2 bb[NG];
+#pragma unroll
+  for (int jg = 0; jg < NG; ++jg) {
+    const int n = n0 + wn * WTN + (jg / 4) * 32 + (jg % 4) * 8 + half * 4;
+    nok[jg] = n < g.Nout;
+    ncol[jg] = nok[jg] ? n : 0;
+    bb[jg] = *reinterpret_cast<const uint2*>(bias + ncol[jg]);
+  }
+  // gate of the gated residuals (EPI_RESID_PLAIN: 1.0 = 0x3f80 in bf16)
+  uint2 gt[NG];
+#pragma unroll
+  for (int jg = 0; jg < NG; ++jg) {
+    if constexpr (EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN)
+      gt[jg] = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(g.gate) + ncol[jg]);
+    else
+      gt[jg] = make_uint2(0x3f803f80u, 0x3f803f80u);
+  }
+  auto biased = [&](int i, int jg, int e) {
+    const uint32_t w = e < 2 ? bb[jg].x : bb[jg].y;
+    const float b = (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+    return acc[i][jg / 4][4 * (jg % 4) + e] + b;
+  };
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
-    // keep each row block's loads and stores together: hoisting the residual
-    // loads of every block at once costs more registers than large tiles have
+    // one row block at a time: hoisting the residual loads of every block
+    // at once costs more registers than the large tiles have
     __builtin_amdgcn_sched_barrier(0);
     const int lr = wm * WTM + i * 32 + col;
     const int rq = tab[lr];
     if constexpr (EPI == EPI_QKV || EPI == EPI_KV) {
       const int rkv = tab[BM + lr];
       const int d = g.d_model;
-      // a tile crosses at most one of the Q|K|V boundaries (d >= BN / 2... and
-      // d >= 128 in the bf16 path; BN <= 256 <= 2d)
+      // a tile crosses at most one of the Q|K|V boundaries (BN <= 256 <= 2d)
       const int which0 = n0 / d, edge = (which0 + 1) * d;
       constexpr int kOff = EPI == EPI_KV ? 1 : 0;   // EPI_KV has no Q columns
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const int n = n0 + wn * WTN + j * 32 + gg * 8 + half * 4;
-          if (!full_n && n >= g.Nout) continue;
-          const int wr = which0 + (n >= edge ? 1 : 0), c = n - wr * d;
-          const int which = wr + kOff;
-          const int r = which == 0 ? rq : rkv;
-          if (r < 0) continue;
-          const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
-          uint2 w;
-          w.x = pack_bf16x2(acc[i][j][4 * gg + 0] + __uint_as_float(bb.x << 16),
-                            acc[i][j][4 * gg + 1] + __uint_as_float(bb.x & 0xffff0000u));
-          w.y = pack_bf16x2(acc[i][j][4 * gg + 2] + __uint_as_float(bb.y << 16),
-                            acc[i][j][4 * gg + 3] + __uint_as_float(bb.y & 0xffff0000u));
-          bf16_t* dst = static_cast<bf16_t*>(which == 0 ? g.q_out : (which == 1 ? g.k_cache : g.v_cache));
-          *reinterpret_cast<uint2*>(dst + static_cast<size_t>(r) * d + c) = w;
-        }
+      for (int jg = 0; jg < NG; ++jg) {
+        const int n = ncol[jg];
+        const int wr = which0 + (n >= edge ? 1 : 0), c = n - wr * d;
+        const int which = wr + kOff;
+        const int r = which == 0 ? rq : rkv;
+        uint2 w;
+        w.x = pack_bf16x2(biased(i, jg, 0), biased(i, jg, 1));
+        w.y = pack_bf16x2(biased(i, jg, 2), biased(i, jg, 3));
+        bf16_t* dst = static_cast<bf16_t*>(which == 0 ? g.q_out : (which == 1 ? g.k_cache : g.v_cache));
+        if (r >= 0 && nok[jg]) *reinterpret_cast<uint2*>(dst + static_cast<size_t>(r) * d + c) = w;
+      }
     } else if constexpr (EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN || EPI == EPI_RESID_PLAIN) {
-      if (rq < 0) continue;
-      const bf16_t* gate = static_cast<const bf16_t*>(g.gate);
+      const size_t rbase = static_cast<size_t>(rq < 0 ? 0 : rq) * g.Nout;
+      float4 xin[NG];
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+      for (int jg = 0; jg < NG; ++jg) xin[jg] = *reinterpret_cast<const float4*>(g.resid_in + rbase + ncol[jg]);
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const int n = n0 + wn * WTN + j * 32 + gg * 8 + half * 4;
-          if (!full_n && n >= g.Nout) continue;
-          const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
-          // EPI_RESID_PLAIN: ungated (gate 1.0 = 0x3f80 in bf16)
-          const uint2 gt = EPI == EPI_RESID_PLAIN ? make_uint2(0x3f803f80u, 0x3f803f80u)
-                                                  : *reinterpret_cast<const uint2*>(gate + n);
-          const size_t o = static_cast<size_t>(rq) * g.Nout + n;
-          const float4 xin = *reinterpret_cast<const float4*>(g.resid_in + o);
-          float4 xo;
-          xo.x = fmaf(__uint_as_float(gt.x << 16), acc[i][j][4 * gg + 0] + __uint_as_float(bb.x << 16), xin.x);
-          xo.y = fmaf(__uint_as_float(gt.x & 0xffff0000u), acc[i][j][4 * gg + 1] + __uint_as_float(bb.x & 0xffff0000u), xin.y);
-          xo.z = fmaf(__uint_as_float(gt.y << 16), acc[i][j][4 * gg + 2] + __uint_as_float(bb.y << 16), xin.z);
-          xo.w = fmaf(__uint_as_float(gt.y & 0xffff0000u), acc[i][j][4 * gg + 3] + __uint_as_float(bb.y & 0xffff0000u), xin.w);
-          *reinterpret_cast<float4*>(g.resid_out + o) = xo;
-        }
+      for (int jg = 0; jg < NG; ++jg) {
+        float4 xo;
+        xo.x = fmaf(__uint_as_float(gt[jg].x << 16), biased(i, jg, 0), xin[jg].x);
+        xo.y = fmaf(__uint_as_float(gt[jg].x & 0xffff0000u), biased(i, jg, 1), xin[jg].y);
+        xo.z = fmaf(__uint_as_float(gt[jg].y << 16), biased(i, jg, 2), xin[jg].z);
+        xo.w = fmaf(__uint_as_float(gt[jg].y & 0xffff0000u), biased(i, jg, 3), xin[jg].w);
+        if (rq >= 0 && nok[jg]) *reinterpret_cast<float4*>(g.resid_out + rbase + ncol[jg]) = xo;
+      }
     } else {
-      if (rq < 0) continue;
-      bf16_t* out = static_cast<bf16_t*>(g.g_out);
+      bf16_t* out = static_cast<bf16_t*>(g.g_out) + static_cast<size_t>(rq < 0 ? 0 : rq) * g.Nout;
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+      for (int jg = 0; jg < NG; ++jg) {
+        float v[4];
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const int n = n0 + wn * WTN + j * 32 + gg * 8 + half * 4;
-          if (!full_n && n >= g.Nout) continue;
-          const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
-          uint2 w;
-          float v0 = acc[i][j][4 * gg + 0] + __uint_as_float(bb.x << 16);
-          float v1 = acc[i][j][4 * gg + 1] + __uint_as_float(bb.x & 0xffff0000u);
-          float v2 = acc[i][j][4 * gg + 2] + __uint_as_float(bb.y << 16);
-          float v3 = acc[i][j][4 * gg + 3] + __uint_as_float(bb.y & 0xffff0000u);
-          if constexpr (EPI == EPI_GELU) {
-            v0 = gelu_erf_fast(v0);
-            v1 = gelu_erf_fast(v1);
-            v2 = gelu_erf_fast(v2);
-            v3 = gelu_erf_fast(v3);
-          }
-          w.x = pack_bf16x2(v0, v1);
-          w.y = pack_bf16x2(v2, v3);
-          *reinterpret_cast<uint2*>(out + static_cast<size_t>(rq) * g.Nout + n) = w;
+        for (int e = 0; e < 4; ++e) {
+          v[e] = biased(i, jg, e);
+          if constexpr (EPI == EPI_GELU) v[e] = gelu_erf_fast(v[e]);
         }
+        uint2 w;
+        w.x = pack_bf16x2(v[0], v[1]);
+        w.y = pack_bf16x2(v[2], v[3]);
+        if (rq >= 0 && nok[jg]) *reinterpret_cast<uint2*>(out + ncol[jg]) = w;
+      }
     }
   }
 }
