@@ -37,26 +37,36 @@ __global__ __launch_bounds__(kRowThreads) void gather_kernel(
   if (t < 0 || t >= N) return;
   const size_t src = (static_cast<size_t>(b) * N + t) * d;
   float* xr = x + (static_cast<size_t>(b) * rows_cap + r) * d;
-  for (int c = lane * 8; c < d; c += kWave * 8) {
-    if constexpr (sizeof(T) == 2) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(z + src + c);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  // 16-byte chunks lane*8 + 512*j, four in flight at a time
+  constexpr int kPer = 16 / sizeof(T);   // elements per 16-byte load
+  for (int c0 = lane * 8; c0 < d; c0 += 4 * kWave * 8) {
+    uint4 raw[4][8 / kPer];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = c0 + q * kWave * 8 < d ? c0 + q * kWave * 8 : c0;
+#pragma unroll
+      for (int u = 0; u < 8 / kPer; ++u) raw[q][u] = *reinterpret_cast<const uint4*>(z + src + c + u * kPer);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = c0 + q * kWave * 8;
+      if (c >= d) continue;
       float4 lo, hi;
-      lo.x = __uint_as_float(w[0] << 16); lo.y = __uint_as_float(w[0] & 0xffff0000u);
-      lo.z = __uint_as_float(w[1] << 16); lo.w = __uint_as_float(w[1] & 0xffff0000u);
-      hi.x = __uint_as_float(w[2] << 16); hi.y = __uint_as_float(w[2] & 0xffff0000u);
-      hi.z = __uint_as_float(w[3] << 16); hi.w = __uint_as_float(w[3] & 0xffff0000u);
-      *reinterpret_cast<float4*>(xr + c) = lo;
-      *reinterpret_cast<float4*>(xr + c + 4) = hi;
-      if (zref) *reinterpret_cast<uint4*>(zref + src + c) = raw;
-    } else {
-      const float4 lo = *reinterpret_cast<const float4*>(z + src + c);
-      const float4 hi = *reinterpret_cast<const float4*>(z + src + c + 4);
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t w[4] = {raw[q][0].x, raw[q][0].y, raw[q][0].z, raw[q][0].w};
+        lo.x = __uint_as_float(w[0] << 16); lo.y = __uint_as_float(w[0] & 0xffff0000u);
+        lo.z = __uint_as_float(w[1] << 16); lo.w = __uint_as_float(w[1] & 0xffff0000u);
+        hi.x = __uint_as_float(w[2] << 16); hi.y = __uint_as_float(w[2] & 0xffff0000u);
+        hi.z = __uint_as_float(w[3] << 16); hi.w = __uint_as_float(w[3] & 0xffff0000u);
+      } else {
+        lo = __builtin_bit_cast(float4, raw[q][0]);
+        hi = __builtin_bit_cast(float4, raw[q][8 / kPer - 1]);
+      }
       *reinterpret_cast<float4*>(xr + c) = lo;
       *reinterpret_cast<float4*>(xr + c + 4) = hi;
       if (zref) {
-        *reinterpret_cast<float4*>(zref + src + c) = lo;
-        *reinterpret_cast<float4*>(zref + src + c + 4) = hi;
+#pragma unroll
+        for (int u = 0; u < 8 / kPer; ++u) *reinterpret_cast<uint4*>(zref + src + c + u * kPer) = raw[q][u];
       }
     }
   }
@@ -84,7 +94,119 @@ hipError_t launch_gather(bool bf16, const void* z, void* zref, const int32_t* id
 // kernel below, so both give the same bits.
 constexpr int kMaxRowChunks = 16;   // d <= 4096
 
-template <typename T>
+// Chunks per lane that the row kernels hold in registers: the smallest of
+// 1, 2, 4, 6, 8, 12, 16 covering d (fewer registers, more waves resident);
+// 0 = d > 4096 (streaming).
+static int row_chunks(int d) {
+  const int need = (d + 255) / 256;
+  constexpr int kSizes[] = {1, 2, 4, 6, 8, 12, 16};
+  for (int c : kSizes)
+    if (need <= c) return c;
+  return 0;
+}
+
+#define WAMC_ROW_NC_DISPATCH(nc, ...)                 \
+  switch (nc) {                                       \
+    case 1: { constexpr int NC = 1; __VA_ARGS__; } break;    \
+    case 2: { constexpr int NC = 2; __VA_ARGS__; } break;    \
+    case 4: { constexpr int NC = 4; __VA_ARGS__; } break;    \
+    case 6: { constexpr int NC = 6; __VA_ARGS__; } break;    \
+    case 8: { constexpr int NC = 8; __VA_ARGS__; } break;    \
+    case 12: { constexpr int NC = 12; __VA_ARGS__; } break;  \
+    case 16: { constexpr int NC = 16; __VA_ARGS__; } break;  \
+    default: { constexpr int NC = 0; __VA_ARGS__; } break;   \
+  }
+
+// Row chunk j of a lane = elements lane*4 + 256*j + 0..3.  Every chunk load of
+// a row is issued before the first use (one memory round trip per row); the
+// chunk loop stops at the first chunk wholly past d (a uniform branch), lanes
+// past d inside the last chunk re-read element 0 and are masked later.
+template <int NC, typename T>
+__device__ __forceinline__ void load_row(const T* __restrict__ p, int d, int lane, float (&v)[NC][4]) {
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    if (j * 256 >= d) break;
+    const int c = lane * 4 + j * 256;
+    const int cc = c < d ? c : 0;
+    if constexpr (sizeof(T) == 2) {
+      const uint2 raw = *reinterpret_cast<const uint2*>(p + cc);
+      v[j][0] = __uint_as_float(raw.x << 16);
+      v[j][1] = __uint_as_float(raw.x & 0xffff0000u);
+      v[j][2] = __uint_as_float(raw.y << 16);
+      v[j][3] = __uint_as_float(raw.y & 0xffff0000u);
+    } else {
+      const float4 f = *reinterpret_cast<const float4*>(p + cc);
+      v[j][0] = f.x; v[j][1] = f.y; v[j][2] = f.z; v[j][3] = f.w;
+    }
+  }
+}
+
+// mean and 1/sqrt(var + eps) of a row held by one wavefront (biased variance,
+// two passes over the registers; the summation order is fixed by the chunk
+// assignment)
+template <int NC>
+__device__ __forceinline__ void row_stats(const float (&v)[NC][4], int d, int lane, float eps, float& mean,
+                                          float& rstd) {
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    if (j * 256 >= d) break;
+    if (lane * 4 + j * 256 < d) sum += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
+  }
+  mean = wave_sum(sum) / static_cast<float>(d);
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    if (j * 256 >= d) break;
+    if (lane * 4 + j * 256 < d) {
+      const float a0 = v[j][0] - mean, a1 = v[j][1] - mean, a2 = v[j][2] - mean, a3 = v[j][3] - mean;
+      q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+    }
+  }
+  const float var = wave_sum(q) / static_cast<float>(d);
+  rstd = 1.0f / sqrtf(var + eps);
+}
+
+// h = (v - mean) * rstd, times (1 + scale) plus shift when MOD, rounded to T;
+// the shift/scale chunks are loaded as one batch first
+template <int NC, typename T, bool MOD>
+__device__ __forceinline__ void row_norm_store(const float (&v)[NC][4], int d, int lane, float mean, float rstd,
+                                               const T* __restrict__ shift, const T* __restrict__ scale,
+                                               T* __restrict__ hr) {
+  float sh[NC][4], sc[NC][4];
+  if constexpr (MOD) {
+    load_row<NC>(shift, d, lane, sh);
+    load_row<NC>(scale, d, lane, sc);
+  }
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    if (j * 256 >= d) break;
+    const int c = lane * 4 + j * 256;
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float n = (v[j][i] - mean) * rstd;
+      y[i] = MOD ? n * (1.0f + sc[j][i]) + sh[j][i] : n;
+    }
+    if (c < d) {
+      if constexpr (sizeof(T) == 2) {
+        uint2 w;
+        w.x = pack_bf16x2(y[0], y[1]);
+        w.y = pack_bf16x2(y[2], y[3]);
+        *reinterpret_cast<uint2*>(hr + c) = w;
+      } else {
+        *reinterpret_cast<float4*>(hr + c) = make_float4(y[0], y[1], y[2], y[3]);
+      }
+    }
+  }
+}
+
+// Gather fused with the first modulated LayerNorm of layer 0: the row is
+// held in registers, x and zref are written, and h = LN(x)(1+scale)+shift is
+// produced in the same pass.  Each lane owns elements lane*4 + 256*j + 0..3,
+// the assignment (and so the summation order) of the stand-alone LayerNorm
+// kernel below, so both give the same bits.
+template <int NC, typename T>
 __global__ __launch_bounds__(kRowThreads) void gather_ln_kernel(
     const T* __restrict__ z, T* __restrict__ zref, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ k_eff, int N, int d, int rows_cap, float* __restrict__ x,
@@ -100,53 +222,29 @@ __global__ __launch_bounds__(kRowThreads) void gather_ln_kernel(
   const size_t src = (static_cast<size_t>(b) * N + t) * d;
   const size_t row = static_cast<size_t>(b) * rows_cap + r;
   float* xr = x + row * d;
-  T* hr = h + row * d;
-  float v[kMaxRowChunks][4];
-  float sum = 0.f;
+  float v[NC][4];
+  load_row<NC>(z + src, d, lane, v);
 #pragma unroll
-  for (int j = 0; j < kMaxRowChunks; ++j) {
+  for (int j = 0; j < NC; ++j) {
+    if (j * 256 >= d) break;
     const int c = lane * 4 + j * 256;
     if (c < d) {
       if constexpr (sizeof(T) == 2) {
-        const uint2 raw = *reinterpret_cast<const uint2*>(z + src + c);
-        v[j][0] = __uint_as_float(raw.x << 16);
-        v[j][1] = __uint_as_float(raw.x & 0xffff0000u);
-        v[j][2] = __uint_as_float(raw.y << 16);
-        v[j][3] = __uint_as_float(raw.y & 0xffff0000u);
+        // the values are bf16, so their upper halves are the original bits
+        uint2 raw;
+        raw.x = (__float_as_uint(v[j][0]) >> 16) | (__float_as_uint(v[j][1]) & 0xffff0000u);
+        raw.y = (__float_as_uint(v[j][2]) >> 16) | (__float_as_uint(v[j][3]) & 0xffff0000u);
         *reinterpret_cast<uint2*>(zref + src + c) = raw;
       } else {
-        const float4 f = *reinterpret_cast<const float4*>(z + src + c);
-        v[j][0] = f.x; v[j][1] = f.y; v[j][2] = f.z; v[j][3] = f.w;
-        *reinterpret_cast<float4*>(zref + src + c) = f;
+        *reinterpret_cast<float4*>(zref + src + c) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
       }
       *reinterpret_cast<float4*>(xr + c) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
-      sum += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
     }
   }
   if (age_zero && lane == 0) age_zero[static_cast<size_t>(b) * N + t] = 0;
-  const float mean = wave_sum(sum) / static_cast<float>(d);
-  float q = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxRowChunks; ++j) {
-    if (lane * 4 + j * 256 < d) {
-      const float a0 = v[j][0] - mean, a1 = v[j][1] - mean, a2 = v[j][2] - mean, a3 = v[j][3] - mean;
-      q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
-    }
-  }
-  const float var = wave_sum(q) / static_cast<float>(d);
-  const float rstd = 1.0f / sqrtf(var + eps);
-#pragma unroll
-  for (int j = 0; j < kMaxRowChunks; ++j) {
-    const int c = lane * 4 + j * 256;
-    if (c < d) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float n = (v[j][i] - mean) * rstd;
-        const float y = n * (1.0f + Elem<T>::load(scale, c + i)) + Elem<T>::load(shift, c + i);
-        Elem<T>::store(hr, c + i, y);
-      }
-    }
-  }
+  float mean, rstd;
+  row_stats(v, d, lane, eps, mean, rstd);
+  row_norm_store<NC, T, true>(v, d, lane, mean, rstd, shift, scale, h + row * d);
 }
 
 hipError_t launch_gather_ln(bool bf16, const void* z, void* zref, const int32_t* idx, const int32_t* k_eff, int B,
@@ -156,21 +254,23 @@ hipError_t launch_gather_ln(bool bf16, const void* z, void* zref, const int32_t*
   if (d > kMaxRowChunks * 256) return hipErrorInvalidValue;
   TimedLaunch t(timer, "gather_ln", s);
   const dim3 grid((rows_cap + 3) / 4, B);
-  if (bf16)
-    gather_ln_kernel<bf16_t><<<grid, kRowThreads, 0, s>>>(static_cast<const bf16_t*>(z), static_cast<bf16_t*>(zref),
-        idx, k_eff, N, d, rows_cap, x, age_zero, static_cast<const bf16_t*>(shift),
-        static_cast<const bf16_t*>(scale), eps, static_cast<bf16_t*>(h), zj);
-  else
-    gather_ln_kernel<float><<<grid, kRowThreads, 0, s>>>(static_cast<const float*>(z), static_cast<float*>(zref),
-        idx, k_eff, N, d, rows_cap, x, age_zero, static_cast<const float*>(shift),
-        static_cast<const float*>(scale), eps, static_cast<float*>(h), zj);
+  const int nc = row_chunks(d);
+  if (bf16) {
+    WAMC_ROW_NC_DISPATCH(nc, if constexpr (NC > 0) gather_ln_kernel<NC, bf16_t><<<grid, kRowThreads, 0, s>>>(
+        static_cast<const bf16_t*>(z), static_cast<bf16_t*>(zref), idx, k_eff, N, d, rows_cap, x, age_zero,
+        static_cast<const bf16_t*>(shift), static_cast<const bf16_t*>(scale), eps, static_cast<bf16_t*>(h), zj))
+  } else {
+    WAMC_ROW_NC_DISPATCH(nc, if constexpr (NC > 0) gather_ln_kernel<NC, float><<<grid, kRowThreads, 0, s>>>(
+        static_cast<const float*>(z), static_cast<float*>(zref), idx, k_eff, N, d, rows_cap, x, age_zero,
+        static_cast<const float*>(shift), static_cast<const float*>(scale), eps, static_cast<float*>(h), zj))
+  }
   return hipGetLastError();
 }
 
 // LayerNorm without affine (biased variance), then *(1 + scale) + shift
 // (MOD; without: the plain normalisation, as the cross-attention queries
 // use), rounded to the activation type.
-template <typename T, bool MOD>
+template <int NC, typename T, bool MOD>
 __global__ __launch_bounds__(kRowThreads) void ln_mod_kernel(
     const float* __restrict__ x, const T* __restrict__ shift, const T* __restrict__ scale,
     int rows_cap, const int32_t* __restrict__ k_eff, int d, float eps, T* __restrict__ h, ZeroJob zj) {
@@ -180,30 +280,40 @@ __global__ __launch_bounds__(kRowThreads) void ln_mod_kernel(
   const int r = blockIdx.x * (kRowThreads / kWave) + wid;
   if (r >= rows_of(k_eff, b, rows_cap)) return;
   const size_t row = static_cast<size_t>(b) * rows_cap + r;
-  const float* xr = x + row * d;
-  T* hr = h + row * d;
-  float s = 0.f;
-  for (int c = lane * 4; c < d; c += kWave * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + c);
-    s += (v.x + v.y) + (v.z + v.w);
-  }
-  const float mean = wave_sum(s) / static_cast<float>(d);
-  float q = 0.f;
-  for (int c = lane * 4; c < d; c += kWave * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + c);
-    const float a = v.x - mean, bb = v.y - mean, cc = v.z - mean, dd = v.w - mean;
-    q += (a * a + bb * bb) + (cc * cc + dd * dd);
-  }
-  const float var = wave_sum(q) / static_cast<float>(d);
-  const float rstd = 1.0f / sqrtf(var + eps);
-  for (int c = lane * 4; c < d; c += kWave * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + c);
-    const float vv[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (NC > 0) {
+    float v[NC][4];
+    load_row<NC>(x + row * d, d, lane, v);
+    float mean, rstd;
+    row_stats(v, d, lane, eps, mean, rstd);
+    row_norm_store<NC, T, MOD>(v, d, lane, mean, rstd, shift, scale, h + row * d);
+  } else {
+    // rows too long for registers: three streaming passes, same chunk
+    // assignment and summation order
+    const float* xr = x + row * d;
+    T* hr = h + row * d;
+    float s = 0.f;
+    for (int c = lane * 4; c < d; c += kWave * 4) {
+      const float4 v = *reinterpret_cast<const float4*>(xr + c);
+      s += (v.x + v.y) + (v.z + v.w);
+    }
+    const float mean = wave_sum(s) / static_cast<float>(d);
+    float q = 0.f;
+    for (int c = lane * 4; c < d; c += kWave * 4) {
+      const float4 v = *reinterpret_cast<const float4*>(xr + c);
+      const float a = v.x - mean, bb = v.y - mean, cc = v.z - mean, dd = v.w - mean;
+      q += (a * a + bb * bb) + (cc * cc + dd * dd);
+    }
+    const float var = wave_sum(q) / static_cast<float>(d);
+    const float rstd = 1.0f / sqrtf(var + eps);
+    for (int c = lane * 4; c < d; c += kWave * 4) {
+      const float4 v = *reinterpret_cast<const float4*>(xr + c);
+      const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float n = (vv[i] - mean) * rstd;
-      const float y = MOD ? n * (1.0f + Elem<T>::load(scale, c + i)) + Elem<T>::load(shift, c + i) : n;
-      Elem<T>::store(hr, c + i, y);
+      for (int i = 0; i < 4; ++i) {
+        const float n = (vv[i] - mean) * rstd;
+        const float y = MOD ? n * (1.0f + Elem<T>::load(scale, c + i)) + Elem<T>::load(shift, c + i) : n;
+        Elem<T>::store(hr, c + i, y);
+      }
     }
   }
 }
@@ -214,18 +324,22 @@ hipError_t launch_ln_mod(bool bf16, const float* x, const void* shift, const voi
   TimedLaunch t(timer, "ln_mod", s);
   const dim3 grid((rows_cap + 3) / 4, B);
   const bool mod = shift != nullptr;
-  if (bf16 && mod)
-    ln_mod_kernel<bf16_t, true><<<grid, kRowThreads, 0, s>>>(x, static_cast<const bf16_t*>(shift),
-        static_cast<const bf16_t*>(scale), rows_cap, k_eff, d, eps, static_cast<bf16_t*>(h), zj);
-  else if (bf16)
-    ln_mod_kernel<bf16_t, false><<<grid, kRowThreads, 0, s>>>(x, nullptr, nullptr, rows_cap, k_eff, d, eps,
-        static_cast<bf16_t*>(h), zj);
-  else if (mod)
-    ln_mod_kernel<float, true><<<grid, kRowThreads, 0, s>>>(x, static_cast<const float*>(shift),
-        static_cast<const float*>(scale), rows_cap, k_eff, d, eps, static_cast<float*>(h), zj);
-  else
-    ln_mod_kernel<float, false><<<grid, kRowThreads, 0, s>>>(x, nullptr, nullptr, rows_cap, k_eff, d, eps,
-        static_cast<float*>(h), zj);
+  const int nc = row_chunks(d);
+  if (bf16 && mod) {
+    WAMC_ROW_NC_DISPATCH(nc, ln_mod_kernel<NC, bf16_t, true><<<grid, kRowThreads, 0, s>>>(x,
+        static_cast<const bf16_t*>(shift), static_cast<const bf16_t*>(scale), rows_cap, k_eff, d, eps,
+        static_cast<bf16_t*>(h), zj))
+  } else if (bf16) {
+    WAMC_ROW_NC_DISPATCH(nc, ln_mod_kernel<NC, bf16_t, false><<<grid, kRowThreads, 0, s>>>(x, nullptr, nullptr,
+        rows_cap, k_eff, d, eps, static_cast<bf16_t*>(h), zj))
+  } else if (mod) {
+    WAMC_ROW_NC_DISPATCH(nc, ln_mod_kernel<NC, float, true><<<grid, kRowThreads, 0, s>>>(x,
+        static_cast<const float*>(shift), static_cast<const float*>(scale), rows_cap, k_eff, d, eps,
+        static_cast<float*>(h), zj))
+  } else {
+    WAMC_ROW_NC_DISPATCH(nc, ln_mod_kernel<NC, float, false><<<grid, kRowThreads, 0, s>>>(x, nullptr, nullptr,
+        rows_cap, k_eff, d, eps, static_cast<float*>(h), zj))
+  }
   return hipGetLastError();
 }
 

@@ -65,15 +65,59 @@ __device__ __forceinline__ void load_k_frags(const bf16_t* __restrict__ krow, bo
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // Stage Qa[l, b, :, h*dh:(h+1)*dh] (A x 128 bf16) into LDS, zero-padding
-// rows A..QB*32.
+// rows A..QB*32.  All of a thread's loads are issued before the first LDS
+// write, so they are in flight together.
 __device__ __forceinline__ void stage_queries(const bf16_t* __restrict__ qa, int A, int QB, int d,
                                               bf16_t* sq) {
+  constexpr int kPer = kMaxQB * 32 * (kScoreDh / 8) / kScoreThreads;
   const int chunks = QB * 32 * (kScoreDh / 8);
-  for (int c = threadIdx.x; c < chunks; c += kScoreThreads) {
+  uint4 v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = threadIdx.x + i * kScoreThreads;
     const int row = c / (kScoreDh / 8), col = (c % (kScoreDh / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < A) v = *reinterpret_cast<const uint4*>(qa + static_cast<size_t>(row) * d + col);
-    *reinterpret_cast<uint4*>(sq + row * kQaStride + col) = v;
+    // rows past A read row 0 (valid memory) and are replaced by zeros
+    const uint4 x = *reinterpret_cast<const uint4*>(qa + static_cast<size_t>(row < A ? row : 0) * d + col);
+    v[i] = row < A ? x : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = threadIdx.x + i * kScoreThreads;
+    const int row = c / (kScoreDh / 8), col = (c % (kScoreDh / 8)) * 8;
+    if (c < chunks) *reinterpret_cast<uint4*>(sq + row * kQaStride + col) = v[i];
+  }
+}
+
+// Each query's softmax (max, sum) over all N keys, from the per-chunk
+// partials of pass 1: the QB*32 query slots split the threads into groups
+// that take interleaved chunks (8 independent loads per round), then the
+// groups' results are merged in group order.  The order is fixed by
+// (nchunks, QB), so the result is reproducible.
+__device__ __forceinline__ void merge_chunk_stats(const float2* __restrict__ p, int A, int QB, int nchunks,
+                                                  float2 (*sg)[kMaxQB * 32], float* smax, float* sinv) {
+  const int QS = QB * 32, G = kScoreThreads / QS;
+  const int a = threadIdx.x % QS, gi = threadIdx.x / QS;
+  float mm = -INFINITY, zz = 0.f;
+  if (gi < G && a < A) {
+    for (int c0 = gi; c0 < nchunks; c0 += 8 * G) {
+      float2 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int cc = c0 + i * G;
+        v[i] = cc < nchunks ? p[static_cast<size_t>(cc) * A + a] : make_float2(-INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) merge_ms(mm, zz, v[i].x, v[i].y);
+    }
+  }
+  if (gi < G) sg[gi][a] = make_float2(mm, zz);
+  __syncthreads();
+  if (threadIdx.x < QS) {
+    float m = -INFINITY, z = 0.f;
+    for (int g = 0; g < G; ++g) merge_ms(m, z, sg[g][threadIdx.x].x, sg[g][threadIdx.x].y);
+    const bool real = static_cast<int>(threadIdx.x) < A;
+    smax[threadIdx.x] = real ? m : INFINITY;   // padded queries contribute exp2(-inf) = 0
+    sinv[threadIdx.x] = real ? 1.f / z : 0.f;
   }
 }
 
@@ -165,6 +209,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_pass2_bf16(
   const int QB = (A + 31) / 32;
   __shared__ bf16_t sq[kMaxQB * 32 * kQaStride];
   __shared__ float smax[kMaxQB * 32], sinv[kMaxQB * 32];
+  __shared__ float2 sg[kScoreThreads / 32][kMaxQB * 32];
 
   const bf16_t* kbase = kc + (static_cast<size_t>(l) * B + b) * N * d + h * kScoreDh;
   float* prow = part + (static_cast<size_t>(b) * LH + lh) * N;
@@ -175,16 +220,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_pass2_bf16(
     load_k_frags(kbase + static_cast<size_t>(key) * d, key < k1, half, kf);
   }
   stage_queries(qa + (static_cast<size_t>(l) * B + b) * A * d + h * kScoreDh, A, QB, d, sq);
-  for (int a = threadIdx.x; a < QB * 32; a += kScoreThreads) {
-    float mm = -INFINITY, zz = 0.f;
-    if (a < A) {
-      const float2* p = ms_in + (static_cast<size_t>(b) * LH + lh) * nchunks * A + a;
-      for (int cc = 0; cc < nchunks; ++cc) merge_ms(mm, zz, p[static_cast<size_t>(cc) * A].x,
-                                                    p[static_cast<size_t>(cc) * A].y);
-    }
-    smax[a] = a < A ? mm : INFINITY;   // padded queries contribute exp2(-inf) = 0
-    sinv[a] = a < A ? 1.f / zz : 0.f;
-  }
+  merge_chunk_stats(ms_in + (static_cast<size_t>(b) * LH + lh) * nchunks * A, A, QB, nchunks, sg, smax, sinv);
   lds_barrier();
 
   for (int kb = k0 + wid * 32; kb < k1; kb += 4 * 32) {
@@ -280,10 +316,9 @@ __global__ __launch_bounds__(256) void score_pass2_f32(
 constexpr int kCombTokens = 16;     // tokens per combine-1 block (4 per wavefront)
 constexpr int kCombThreads = 256;
 
-// sum over one 16-byte chunk of (z - zref)^2
-__device__ __forceinline__ float sq_diff16(const bf16_t* z, const bf16_t* r) {
-  const uint4 a = *reinterpret_cast<const uint4*>(z);
-  const uint4 b = *reinterpret_cast<const uint4*>(r);
+// sum over one 16-byte chunk of (z - zref)^2 (the chunk's bits in a, b; the
+// last argument picks the element type)
+__device__ __forceinline__ float sq_diff16(uint4 a, uint4 b, bf16_t) {
   const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
   float acc = 0.f;
 #pragma unroll
@@ -295,9 +330,9 @@ __device__ __forceinline__ float sq_diff16(const bf16_t* z, const bf16_t* r) {
   }
   return acc;
 }
-__device__ __forceinline__ float sq_diff16(const float* z, const float* r) {
-  const float4 a = *reinterpret_cast<const float4*>(z);
-  const float4 b = *reinterpret_cast<const float4*>(r);
+__device__ __forceinline__ float sq_diff16(uint4 ua, uint4 ub, float) {
+  const float4 a = __builtin_bit_cast(float4, ua);
+  const float4 b = __builtin_bit_cast(float4, ub);
   const float d0 = a.x - b.x, d1 = a.y - b.y, d2 = a.z - b.z, d3 = a.w - b.w;
   return fmaf(d0, d0, fmaf(d1, d1, fmaf(d2, d2, d3 * d3)));
 }
@@ -323,7 +358,17 @@ __global__ __launch_bounds__(kCombThreads) void score_combine1(
       if (mass_in) {
         if (grp == 0) acc = mass_in[static_cast<size_t>(b) * N + tok];
       } else {
-        for (int r = grp; r < LH; r += 16) acc += part[(static_cast<size_t>(b) * LH + r) * N + tok];
+        // rows grp, grp+16, ... summed in that order; 8 loads in flight at a time
+        for (int r0 = grp; r0 < LH; r0 += 16 * 8) {
+          float v[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int r = r0 + 16 * q;
+            v[q] = r < LH ? part[(static_cast<size_t>(b) * LH + r) * N + tok] : 0.f;
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc += v[q];
+        }
       }
     }
     sp[grp][tk] = acc;
@@ -338,7 +383,19 @@ __global__ __launch_bounds__(kCombThreads) void score_combine1(
     if (tok < N) {
       const T* zr = z + (static_cast<size_t>(b) * N + tok) * d;
       const T* rr = zref + (static_cast<size_t>(b) * N + tok) * d;
-      for (int c = lane; c < chunks; c += kWave) acc += sq_diff16(zr + c * kPer, rr + c * kPer);
+      // chunks lane, lane+64, ... in that order; 4 pairs of loads in flight at a time
+      for (int c0 = lane; c0 < chunks; c0 += 4 * kWave) {
+        uint4 za[4], ra[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = c0 + q * kWave < chunks ? c0 + q * kWave : c0;
+          za[q] = *reinterpret_cast<const uint4*>(zr + c * kPer);
+          ra[q] = *reinterpret_cast<const uint4*>(rr + c * kPer);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (c0 + q * kWave < chunks) acc += sq_diff16(za[q], ra[q], T{});
+      }
     }
     u[j] = acc;
   }

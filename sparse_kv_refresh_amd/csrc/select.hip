@@ -42,13 +42,29 @@ constexpr int kSelWaves = kSelThreads / kWave;
 struct SelShared {
   uint32_t hist[256];
   int red[kSelWaves];
-  uint32_t sel, rem;
+  uint64_t red64[kSelWaves];
+  uint32_t sel, rem, whole;
   float red4[4];
 };
 
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, kWave);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, kWave);
+    const uint64_t w = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = w < v ? w : v;
+  }
+  return v;
+}
+
 // The count-th largest key (1 <= count < N) by an MSB-first radix select:
-// 8 passes of an 8-bit digit histogram in LDS, the bucket found by a
-// wave-wide suffix scan.  key_of(j, i) gives the key of token i, held in
+// up to 8 passes of an 8-bit digit histogram in LDS, the bucket found by a
+// wave-wide suffix scan.  Once the bucket that holds the answer is taken
+// whole (its size equals the rank still wanted inside it -- with distinct
+// scores this happens after two or three passes), the answer is that
+// bucket's smallest key, found by one block-wide minimum instead of the
+// remaining passes.  key_of(j, i) gives the key of token i, held in
 // register slot j when KPT > 0 (i = tid + j*1024); with KPT == 0 it is
 // recomputed for every i.  All threads of the block call it.
 template <int KPT, class KeyOf>
@@ -108,13 +124,43 @@ __device__ uint64_t radix_threshold(KeyOf key_of, int N, uint32_t count, SelShar
             }
           }
         }
+        const uint32_t hs = sel == 4 * lane + 3 ? h3 : sel == 4 * lane + 2 ? h2 : sel == 4 * lane + 1 ? h1 : h0;
         sh.sel = sel;
         sh.rem = remaining - c;
+        sh.whole = hs == remaining - c ? 1u : 0u;
       }
     }
     __syncthreads();
     prefix |= static_cast<uint64_t>(sh.sel) << shift;
     remaining = sh.rem;
+    if (sh.whole && shift > 0) {
+      // every key of the bucket is selected: the answer is its minimum
+      const uint64_t mask = ~0ull << shift;
+      uint64_t mn = ~0ull;
+      if constexpr (KPT > 0) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const int i = tid + j * kSelThreads;
+          if (i < N) {
+            const uint64_t key = key_of(j, i);
+            if ((key & mask) == prefix && key < mn) mn = key;
+          }
+        }
+      } else {
+        for (int i = tid; i < N; i += kSelThreads) {
+          const uint64_t key = key_of(0, i);
+          if ((key & mask) == prefix && key < mn) mn = key;
+        }
+      }
+      mn = wave_min_u64(mn);
+      if (lane == 0) sh.red64[wid] = mn;
+      __syncthreads();
+      uint64_t r = ~0ull;
+#pragma unroll
+      for (int w = 0; w < kSelWaves; ++w) r = sh.red64[w] < r ? sh.red64[w] : r;
+      __syncthreads();   // sh is reused by the caller
+      return r;
+    }
   }
   return prefix;
 }
@@ -122,12 +168,12 @@ __device__ uint64_t radix_threshold(KeyOf key_of, int N, uint32_t count, SelShar
 // Ascending-order compaction of the tokens with flag_of(j, i) set into idx,
 // ages reset on the set and +1 elsewhere; returns the set size.  One
 // 1024-token tile at a time with a block-wide ballot/popcount scan.
-template <int KPT, class FlagOf>
-__device__ int compact_set(FlagOf flag_of, int N, int32_t* __restrict__ idx, int32_t* __restrict__ age,
-                           SelShared& sh) {
+template <int KPT, class FlagOf, class AgeOf>
+__device__ int compact_set(FlagOf flag_of, AgeOf age_of, int N, int32_t* __restrict__ idx,
+                           int32_t* __restrict__ age, SelShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   int base = 0;
-  auto tile = [&](int i, bool flag) {
+  auto tile = [&](int j, int i, bool flag) {
     const uint64_t ball = __ballot(flag);
     const int wpre = __popcll(ball & ((1ull << lane) - 1ull));
     if (lane == 0) sh.red[wid] = __popcll(ball);
@@ -140,7 +186,7 @@ __device__ int compact_set(FlagOf flag_of, int N, int32_t* __restrict__ idx, int
       tot += c;
     }
     if (flag) idx[base + off + wpre] = i;
-    if (i < N) age[i] = flag ? 0 : age[i] + 1;
+    if (i < N) age[i] = flag ? 0 : age_of(j, i) + 1;
     base += tot;
     __syncthreads();
   };
@@ -149,23 +195,31 @@ __device__ int compact_set(FlagOf flag_of, int N, int32_t* __restrict__ idx, int
     for (int j = 0; j < KPT; ++j) {
       if (j * kSelThreads >= N) break;
       const int i = tid + j * kSelThreads;
-      tile(i, i < N && flag_of(j, i));
+      tile(j, i, i < N && flag_of(j, i));
     }
   } else {
     for (int t0 = 0; t0 < N; t0 += kSelThreads) {
       const int i = t0 + tid;
-      tile(i, i < N && flag_of(0, i));
+      tile(0, i, i < N && flag_of(0, i));
     }
   }
   for (int i = base + tid; i < N; i += kSelThreads) idx[i] = -1;
   return base;
 }
 
-// block-wide count of forced tokens (age >= G)
-__device__ int count_forced(const int32_t* __restrict__ age, int N, int G, SelShared& sh) {
+// block-wide count of forced tokens (age >= G); the ages come from the
+// registers ag (token tid + j*1024 in slot j) when KPT > 0
+template <int KPT>
+__device__ int count_forced(const int32_t* __restrict__ age, const int (&ag)[KPT > 0 ? KPT : 1], int N, int G,
+                            SelShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   int nf = 0;
-  for (int i = tid; i < N; i += kSelThreads) nf += age[i] >= G;
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) nf += (tid + j * kSelThreads < N && ag[j] >= G) ? 1 : 0;
+  } else {
+    for (int i = tid; i < N; i += kSelThreads) nf += age[i] >= G;
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) nf += __shfl_xor(nf, o, kWave);
   if (lane == 0) sh.red[wid] = nf;
@@ -193,33 +247,55 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
   idx += eoff;
   __shared__ SelShared sh;
 
+  constexpr int NK = KPT > 0 ? KPT : 1;
+  uint64_t keys[NK];
+  int ag[NK];
   float total = 0.f;
-  if constexpr (SCORED) total = usum_total(si.usum + static_cast<size_t>(b) * si.nblocks, si.nblocks, sh.red4);
+  if constexpr (KPT > 0) {
+    // every token load is issued before the first use
+    float pa[KPT], pb[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int i = tid + j * kSelThreads;
+      const size_t ic = eoff + (i < N ? i : 0);
+      if constexpr (SCORED) {
+        pa[j] = si.mass[ic];
+        pb[j] = si.surprise[ic];
+      } else {
+        pa[j] = score[ic];
+        pb[j] = 0.f;
+      }
+      ag[j] = age[i < N ? i : 0];
+    }
+    if constexpr (SCORED) total = usum_total(si.usum + static_cast<size_t>(b) * si.nblocks, si.nblocks, sh.red4);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int i = tid + j * kSelThreads;
+      keys[j] = 0;
+      if (i < N) {
+        float sc = pa[j];
+        if constexpr (SCORED) {
+          sc = combine_score(pa[j], pb[j], total, si.w_attn_norm, si.w_surprise);
+          si.score_out[eoff + i] = sc;
+        }
+        keys[j] = rank_key(sc, ag[j] >= G, i);
+      }
+    }
+  } else {
+    if constexpr (SCORED) {
+      total = usum_total(si.usum + static_cast<size_t>(b) * si.nblocks, si.nblocks, sh.red4);
+      for (int i = tid; i < N; i += kSelThreads)
+        si.score_out[eoff + i] = combine_score(si.mass[eoff + i], si.surprise[eoff + i], total, si.w_attn_norm,
+                                               si.w_surprise);
+    }
+  }
   auto get_score = [&](int i) -> float {
     if constexpr (SCORED)
       return combine_score(si.mass[eoff + i], si.surprise[eoff + i], total, si.w_attn_norm, si.w_surprise);
     else
       return score[eoff + i];
   };
-
-  constexpr int NK = KPT > 0 ? KPT : 1;
-  uint64_t keys[NK];
-  if constexpr (KPT > 0) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int i = tid + j * kSelThreads;
-      keys[j] = 0;
-      if (i < N) {
-        const float sc = get_score(i);
-        if constexpr (SCORED) si.score_out[eoff + i] = sc;
-        keys[j] = rank_key(sc, age[i] >= G, i);
-      }
-    }
-  } else {
-    if constexpr (SCORED)
-      for (int i = tid; i < N; i += kSelThreads) si.score_out[eoff + i] = get_score(i);
-  }
-  const int n_forced = count_forced(age, N, G, sh);
+  const int n_forced = count_forced<KPT>(age, ag, N, G, sh);
 
   int ke = k > n_forced ? k : n_forced;
   if (ke > rows_cap) ke = rows_cap;
@@ -230,8 +306,12 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
   };
   uint64_t thr = 0;
   if (!take_all && !take_none) thr = radix_threshold<KPT>(key_of, N, static_cast<uint32_t>(ke), sh);
-  compact_set<KPT>([&](int j, int i) { return take_all || (!take_none && key_of(j, i) >= thr); }, N, idx, age,
-                   sh);
+  auto age_of = [&](int j, int i) -> int {
+    if constexpr (KPT > 0) return ag[j];
+    else return age[i];
+  };
+  compact_set<KPT>([&](int j, int i) { return take_all || (!take_none && key_of(j, i) >= thr); }, age_of, N, idx,
+                   age, sh);
   if (tid == 0) {
     k_eff_out[b] = ke;
     if (n_forced_out) n_forced_out[b] = n_forced;
@@ -259,15 +339,29 @@ __global__ __launch_bounds__(kSelThreads) void select_union_kernel(
 
   constexpr int NK = KPT > 0 ? KPT : 1;
   uint64_t kp[NK], ku[NK];
+  int ag[NK];
   if constexpr (KPT > 0) {
+    // every token load is issued before the first use
+    float pm[KPT], pu[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int i = tid + j * kSelThreads, ic = i < N ? i : 0;
+      pm[j] = mass[ic];
+      pu[j] = surprise[ic];
+      ag[j] = age[ic];
+    }
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int i = tid + j * kSelThreads;
-      kp[j] = i < N ? rank_key(mass[i], false, i) : 0;
-      ku[j] = i < N ? rank_key(surprise[i], false, i) : 0;
+      kp[j] = i < N ? rank_key(pm[j], false, i) : 0;
+      ku[j] = i < N ? rank_key(pu[j], false, i) : 0;
     }
   }
-  const int n_forced = count_forced(age, N, G, sh);
+  const int n_forced = count_forced<KPT>(age, ag, N, G, sh);
+  auto age_of = [&](int j, int i) -> int {
+    if constexpr (KPT > 0) return ag[j];
+    else return age[i];
+  };
   auto kp_of = [&](int j, int i) -> uint64_t {
     if constexpr (KPT > 0) return kp[j];
     else return rank_key(mass[i], false, i);
@@ -285,9 +379,9 @@ __global__ __launch_bounds__(kSelThreads) void select_union_kernel(
   else if (n_surprise > 0) tu = radix_threshold<KPT>(ku_of, N, static_cast<uint32_t>(n_surprise), sh);
   const int ke = compact_set<KPT>(
       [&](int j, int i) {
-        return age[i] >= G || (tp != kNone && kp_of(j, i) >= tp) || (tu != kNone && ku_of(j, i) >= tu);
+        return age_of(j, i) >= G || (tp != kNone && kp_of(j, i) >= tp) || (tu != kNone && ku_of(j, i) >= tu);
       },
-      N, idx, age, sh);
+      age_of, N, idx, age, sh);
   if (tid == 0) {
     k_eff_out[b] = ke;
     if (n_forced_out) n_forced_out[b] = n_forced;
