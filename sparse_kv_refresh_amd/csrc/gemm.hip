@@ -691,11 +691,18 @@ __device__ __forceinline__ SkTile sk_tile(const GemmArgs& g, int t, int tiles_m,
 
 // Resident workgroups of a configuration: two per CU when they fit (4 waves,
 // <= 80 KiB LDS), else one.
+#ifndef WAMC_SK_MAX_PER_CU
+#define WAMC_SK_MAX_PER_CU 2
+#endif
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
 struct SkConfig {
   static constexpr int kThreads = 64 * WGM * WGN;
   static constexpr int kLds = STAGES * (BM + BN) * BK * 2;
-  static constexpr int kPerCu = (kThreads == 256 && kLds <= 80 * 1024) ? 2 : 1;
+  // resident workgroups per CU: as many 4-wave workgroups as the LDS holds
+  // (at most WAMC_SK_MAX_PER_CU); one for the 8-wave tiles
+  static constexpr int kPerCu = kThreads == 256 ? (160 * 1024 / kLds < WAMC_SK_MAX_PER_CU ? 160 * 1024 / kLds
+                                                                                          : WAMC_SK_MAX_PER_CU)
+                                                : 1;
   static constexpr int kP = 256 * kPerCu;
   static constexpr size_t kTileBytes = static_cast<size_t>(BM) * BN * 4;
 };
@@ -915,10 +922,18 @@ constexpr bool kGemmBig = WAMC_GEMM_BIG != 0;
 #ifndef WAMC_SK_BN
 #define WAMC_SK_BN 128
 #endif
-// (measured on the d=1536 shapes: 128x256 / 256x128 wave tiles, BK 32 with
-// 4 or 6 stages, BK 64 with 3 stages, and raised wave priority around the
-// MFMAs were all slower than 128x128, BK 64, 2 stages, 2 workgroups per CU)
-using SkSmall = SkConfig<WAMC_SK_BM, WAMC_SK_BN, WAMC_SK_BK, WAMC_SK_STAGES, 2, 2>;
+#ifndef WAMC_SK_WGM
+#define WAMC_SK_WGM 2
+#endif
+#ifndef WAMC_SK_WGN
+#define WAMC_SK_WGN 2
+#endif
+// (measured on the d=1536 shapes: 128x256 / 256x128 wave tiles; 256x128 and
+// 128x256 tiles on 8 waves with BK 64 and 2 or 3 stages or BK 32 and 4;
+// BK 32 with 3 to 6 stages; 3 or 4 workgroups per CU with BK 32; and raised
+// wave priority around the MFMAs were all slower than 128x128, BK 64,
+// 2 stages, 2 independent 4-wave workgroups per CU)
+using SkSmall = SkConfig<WAMC_SK_BM, WAMC_SK_BN, WAMC_SK_BK, WAMC_SK_STAGES, WAMC_SK_WGM, WAMC_SK_WGN>;
 using SkBig = SkConfig<256, 256, 32, 4, 2, 4>;
 
 GemmScratch gemm_scratch(int B, int rows_cap, int d, int F) {
@@ -1060,7 +1075,7 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   if (!use_ks2 && use_sk && big) {
     launch_sk<256, 256, 32, 4, 2, 4>(epi, g, s);
   } else if (!use_ks2 && use_sk) {
-    launch_sk<WAMC_SK_BM, WAMC_SK_BN, WAMC_SK_BK, WAMC_SK_STAGES, 2, 2>(epi, g, s);
+    launch_sk<WAMC_SK_BM, WAMC_SK_BN, WAMC_SK_BK, WAMC_SK_STAGES, WAMC_SK_WGM, WAMC_SK_WGN>(epi, g, s);
   } else if (use_ks2) {
     const unsigned grid = static_cast<unsigned>(t128);
     WAMC_EPI_DISPATCH(epi, (gemm_bf16_dtl_ks2_kernel<E, 64, 2><<<grid, kKs2Threads, 0, s>>>(g)));
