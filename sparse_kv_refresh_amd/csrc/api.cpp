@@ -321,9 +321,11 @@ ZeroJob counter_clear(void* ws, const WsLayout& L) {
 
 // One layer on rows [b*rows_cap, b*rows_cap + k_eff[b]): reads x_in, writes
 // x_out (may alias x_in).
+// rows_lo: a lower bound on every k_eff[b] known on the host (0 when unknown),
+// from which the GEMM tile shape is chosen.
 hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_in, float* x_out,
-                     const int32_t* idx, const int32_t* k_eff, int32_t rows_cap, void* kc, void* vc,
-                     void* ws, const WsLayout& L, hipStream_t s, bool h1_ready = false,
+                     const int32_t* idx, const int32_t* k_eff, int32_t rows_cap, int32_t rows_lo, void* kc,
+                     void* vc, void* ws, const WsLayout& L, hipStream_t s, bool h1_ready = false,
                      const ZeroJob& zj = ZeroJob{}) {
   const bool bf16 = d->dtype == WAMC_BF16;
   const size_t es = act_size(d);
@@ -349,6 +351,7 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
   GemmArgs g{};
   g.rows_cap = rows_cap;
   g.k_eff = k_eff;
+  g.rows_lo = k_eff ? rows_lo : rows_cap;
   g.M = M;
   g.n_tokens = d->n_tokens;
   g.d_model = D;
@@ -446,7 +449,7 @@ hipError_t run_score(const wamc_dims* d, const void* z, const void* zref, const 
 // and run every layer on them.
 hipError_t run_refresh_rows(const wamc_dims* dims, const wamc_layer_w* layers, const void* z, void* zref,
                             void* k_cache, void* v_cache, const int32_t* idx, const int32_t* k_eff, float* layer_out,
-                            int32_t rows_cap, void* ws, const WsLayout& L, hipStream_t s) {
+                            int32_t rows_cap, int32_t rows_lo, void* ws, const WsLayout& L, hipStream_t s) {
   KernelTimer* tm = active_timer();
   const bool bf16 = dims->dtype == WAMC_BF16;
   const int B = dims->batch, N = dims->n_tokens, D = dims->d_model;
@@ -466,7 +469,7 @@ hipError_t run_refresh_rows(const wamc_dims* dims, const wamc_layer_w* layers, c
     float* xout = layer_out ? layer_out + l * out_elems : x;
     void* kc = static_cast<char*>(k_cache) + l * layer_elems * es;
     void* vc = static_cast<char*>(v_cache) + l * layer_elems * es;
-    e = run_layer(dims, &layers[l], xin, xout, idx, k_eff, rows_cap, kc, vc, ws, L, s, l == 0 && fuse_ln);
+    e = run_layer(dims, &layers[l], xin, xout, idx, k_eff, rows_cap, rows_lo, kc, vc, ws, L, s, l == 0 && fuse_ln);
   }
   return e;
 }
@@ -598,7 +601,7 @@ int wamc_refresh_layer(const wamc_dims* dims, int32_t layer, const wamc_layer_w*
   OPT_PTR(ws);
   if ((st = check_device(fn))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(fn, run_layer(dims, w, x, x, idx, k_eff, rows_cap, k_cache_l, v_cache_l, ws, L, s, false,
+  return hip_status(fn, run_layer(dims, w, x, x, idx, k_eff, rows_cap, 0, k_cache_l, v_cache_l, ws, L, s, false,
                                   counter_clear(ws, L)), s);
 }
 
@@ -664,8 +667,9 @@ int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const 
     }
   }
   if (e != hipSuccess) return hip_status(fn, e, s);
+  // k_eff = max(k, forced) >= k when the library selects; a supplied set's size is device data
   return hip_status(fn, run_refresh_rows(dims, layers, z, zref, k_cache, v_cache, idx_out, k_eff_out, layer_out,
-                                         rows_cap, ws, L, s), s);
+                                         rows_cap, idx_override ? 0 : k, ws, L, s), s);
 }
 
 int wamc_select_union(const wamc_dims* dims, const float* mass, const float* surprise, int32_t* age,
@@ -737,8 +741,9 @@ int wamc_prefill_chunk_union(const wamc_dims* dims, const wamc_layer_w* layers, 
                             n_surprise, dims->age_bound, idx_out, k_eff_out, nullptr, s);
   }
   if (e != hipSuccess) return hip_status(fn, e, s);
+  // the union holds at least the larger of the two budgets
   return hip_status(fn, run_refresh_rows(dims, layers, z, zref, k_cache, v_cache, idx_out, k_eff_out, layer_out,
-                                         rows_cap, ws, L, s), s);
+                                         rows_cap, std::max(n_attn, n_surprise), ws, L, s), s);
 }
 
 int wamc_text_kv(const wamc_dims* dims, const wamc_layer_w* layers, const void* text, void* ws, size_t ws_bytes,
@@ -815,7 +820,7 @@ int wamc_dense_prefill(const wamc_dims* dims, const wamc_layer_w* layers, const 
     float* xout = layer_out ? layer_out + l * layer_elems : x;
     void* kc = static_cast<char*>(k_cache) + l * layer_elems * es;
     void* vc = static_cast<char*>(v_cache) + l * layer_elems * es;
-    e = run_layer(dims, &layers[l], xin, xout, nullptr, nullptr, N, kc, vc, ws, L, s, l == 0 && fuse_ln);
+    e = run_layer(dims, &layers[l], xin, xout, nullptr, nullptr, N, N, kc, vc, ws, L, s, l == 0 && fuse_ln);
   }
   return hip_status(fn, e, s);
 }

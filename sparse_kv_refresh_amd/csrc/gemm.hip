@@ -694,6 +694,9 @@ __device__ __forceinline__ SkTile sk_tile(const GemmArgs& g, int t, int tiles_m,
 #ifndef WAMC_SK_MAX_PER_CU
 #define WAMC_SK_MAX_PER_CU 2
 #endif
+#ifndef WAMC_SK_GRID_ROUNDS
+#define WAMC_SK_GRID_ROUNDS 3
+#endif
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
 struct SkConfig {
   static constexpr int kThreads = 64 * WGM * WGN;
@@ -733,13 +736,19 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   const int ndp = (tiles / P) * P;        // tiles done one per workgroup
   const int r = tiles - ndp;              // tail tiles, split along K
   const int nk = g.K / BK;
-  const int h = blockIdx.x;
-  int S = 1, u = 0;
-  if (h >= ndp) {
-    if (r == 0) return;
-    // S minimising (rounds of r*S pieces) x (piece overhead + nk/S k-tiles), with
-    // the pieces within the grid and the partial slots and >= kSkMinIters k-tiles each
-    const int room = min(static_cast<int>(gridDim.x) - ndp, slots);
+  // Work items: the ndp tiles done whole, then the r*S pieces of the split
+  // tail.  Workgroup h takes items h, h + G, h + 2G, ... (G = the grid, a
+  // multiple of P and so of the 8 XCDs: an item runs on the XCD its remapped
+  // index belongs to).  A grid capped at a few rounds of resident workgroups
+  // keeps launches sized for many more rows than k_eff from paying for
+  // thousands of workgroups that would only exit.
+  // S minimises (rounds of r*S pieces) x (piece overhead + nk/S k-tiles),
+  // with the pieces within the grid's spare workgroups and the partial slots
+  // and >= kSkMinIters k-tiles each.
+  const int G = static_cast<int>(gridDim.x);
+  int S = 1;
+  if (r > 0) {
+    const int room = min(max(G - ndp, 0), slots);
     const int smax = max(1, min(min(kSkMaxSplit, nk / kSkMinIters), room / r));
     float best = static_cast<float>((r + P - 1) / P) * static_cast<float>(kSkPieceCost + nk);
     for (int c = 2; c <= smax; ++c) {
@@ -750,9 +759,8 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
         S = c;
       }
     }
-    if (h - ndp >= r * S) return;
-    u = xcd_remap(h - ndp, r * S);
   }
+  const int W = ndp + r * S;
 
   // one LDS object only: a second __shared__ variable makes the compiler wait
   // for the tile loads in flight before every LDS read (it cannot tell the
@@ -767,138 +775,144 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   const bf16_t* Wt = static_cast<const bf16_t*>(g.w);
   const int K = g.K;
 
-  // this workgroup's piece: tile tl, k-tiles [kk0, kk1)
-  SkTile tl;
-  int kk0 = 0, kk1 = nk, tt = 0;
-  if (h < ndp) {
-    tl = sk_tile<BM, BN>(g, xcd_remap(h, ndp), tiles_m, tiles_n);
-  } else {
-    tt = u / S;
-    const int sp = u - tt * S;   // split index
-    tl = sk_tile<BM, BN>(g, ndp + tt, tiles_m, tiles_n);
-    kk0 = sp * nk / S;
-    kk1 = (sp + 1) * nk / S;
-  }
+  for (int w = blockIdx.x; w < W; w += G) {
+    // this item: tile tl, k-tiles [kk0, kk1); a piece of a split tile when split
+    const bool split = w >= ndp && S > 1;
+    SkTile tl;
+    int kk0 = 0, kk1 = nk, tt = 0, u = 0;
+    if (w < ndp) {
+      tl = sk_tile<BM, BN>(g, xcd_remap(w, ndp), tiles_m, tiles_n);
+    } else {
+      u = xcd_remap(w - ndp, r * S);
+      tt = u / S;
+      const int sp = u - tt * S;   // split index
+      tl = sk_tile<BM, BN>(g, ndp + tt, tiles_m, tiles_n);
+      kk0 = sp * nk / S;
+      kk1 = (sp + 1) * nk / S;
+    }
 
-  int goff[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int il = i < LOADS_A ? i : i - LOADS_A;
-    const int c = (il * NW + wid) * 64 + lane;
-    const int row = c / CPR;
-    const int kc = swz_kc<CPR>(row, c % CPR);
-    if (i < LOADS_A) goff[i] = min(tl.m0 + row, g.M - 1) * K + kc * 8 + kk0 * BK;
-    else goff[i] = min(tl.n0 + row, g.Nout - 1) * K + kc * 8 + kk0 * BK;
-  }
-  auto issue = [&](int kt, int stage) {
+    int goff[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const bf16_t* src = (i < LOADS_A ? A : Wt) + goff[i] + kt * BK;
       const int il = i < LOADS_A ? i : i - LOADS_A;
-      uint4* dst = &lds[stage][(i < LOADS_A ? 0 : CHUNKS_A) + (il * NW + wid) * 64];
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
+      const int c = (il * NW + wid) * 64 + lane;
+      const int row = c / CPR;
+      const int kc = swz_kc<CPR>(row, c % CPR);
+      if (i < LOADS_A) goff[i] = min(tl.m0 + row, g.M - 1) * K + kc * 8 + kk0 * BK;
+      else goff[i] = min(tl.n0 + row, g.Nout - 1) * K + kc * 8 + kk0 * BK;
     }
-  };
+    auto issue = [&](int kt, int stage) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const bf16_t* src = (i < LOADS_A ? A : Wt) + goff[i] + kt * BK;
+        const int il = i < LOADS_A ? i : i - LOADS_A;
+        uint4* dst = &lds[stage][(i < LOADS_A ? 0 : CHUNKS_A) + (il * NW + wid) * 64];
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
+      }
+    };
 
-  f32x16_t acc[TI][TJ];
+    f32x16_t acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
+      for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
 
-  const int ra = wm * WTM + col;
-  const int rb = wn * WTN + col;
-  const int n = kk1 - kk0;
+    const int ra = wm * WTM + col;
+    const int rb = wn * WTN + col;
+    const int n = kk1 - kk0;
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < n) issue(p, p);
-  for (int q = 0; q < n; ++q) {
-    // tile q has landed once at most (tiles issued after it) x LOADS loads remain
-    wait_tiles_ahead<LOADS, STAGES - 2>(min(STAGES - 2, n - 1 - q));
-    __builtin_amdgcn_s_barrier();
-    if (q + STAGES - 1 < n) issue(q + STAGES - 1, (q + STAGES - 1) % STAGES);
-    const uint4* as = lds[q % STAGES];
-    const uint4* ws = as + CHUNKS_A;
+    for (int p = 0; p < STAGES - 1; ++p)
+      if (p < n) issue(p, p);
+    for (int q = 0; q < n; ++q) {
+      // tile q has landed once at most (tiles issued after it) x LOADS loads remain
+      wait_tiles_ahead<LOADS, STAGES - 2>(min(STAGES - 2, n - 1 - q));
+      __builtin_amdgcn_s_barrier();
+      if (q + STAGES - 1 < n) issue(q + STAGES - 1, (q + STAGES - 1) % STAGES);
+      const uint4* as = lds[q % STAGES];
+      const uint4* ws = as + CHUNKS_A;
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int kc = 2 * s + half;
-      bf16x8_t af[TI], bfr[TJ];
+      for (int s = 0; s < BK / 16; ++s) {
+        const int kc = 2 * s + half;
+        bf16x8_t af[TI], bfr[TJ];
 #pragma unroll
-      for (int i = 0; i < TI; ++i) af[i] = __builtin_bit_cast(bf16x8_t, as[swz<CPR>(ra + 32 * i, kc)]);
+        for (int i = 0; i < TI; ++i) af[i] = __builtin_bit_cast(bf16x8_t, as[swz<CPR>(ra + 32 * i, kc)]);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) bfr[j] = __builtin_bit_cast(bf16x8_t, ws[swz<CPR>(rb + 32 * j, kc)]);
+        for (int j = 0; j < TJ; ++j) bfr[j] = __builtin_bit_cast(bf16x8_t, ws[swz<CPR>(rb + 32 * j, kc)]);
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      }
+    }
+
+    auto finish = [&]() {
+      __syncthreads();   // every wave is done with the LDS stages
+      int* tab = reinterpret_cast<int*>(&lds[0][0]);
+      fill_row_table<EPI, BM, NT>(g, tl.m0, tab, tl.mend);
+      __syncthreads();
+      tile_epilogue<EPI, BM, BN, TI, TJ, WTM, WTN>(g, acc, tl.m0, tl.n0, wm, wn, half, col, tab);
+    };
+    if (!split) {
+      finish();
+    } else {
+      // Partial tiles live in scratch slot u (piece u of the tail).  They are
+      // written and read as relaxed system-scope atomics (sc0 sc1 accesses that go
+      // to the coherence point and back), so no cache-wide write-back or
+      // invalidate is needed between the workgroups of one tile.
+      unsigned long long* part = reinterpret_cast<unsigned long long*>(g.sk_partial);
+      const size_t own = static_cast<size_t>(u) * (BM * BN / 2);   // 8-byte words
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
-  }
-
-  auto finish = [&]() {
-    __syncthreads();   // every wave is done with the LDS stages
-    int* tab = reinterpret_cast<int*>(&lds[0][0]);
-    fill_row_table<EPI, BM, NT>(g, tl.m0, tab, tl.mend);
-    __syncthreads();
-    tile_epilogue<EPI, BM, BN, TI, TJ, WTM, WTN>(g, acc, tl.m0, tl.n0, wm, wn, half, col, tab);
-  };
-  if (S == 1) {
-    finish();
-    return;
-  }
-  // Partial tiles live in scratch slot u (piece u of the tail).  They are
-  // written and read as relaxed system-scope atomics (sc0 sc1 accesses that go
-  // to the coherence point and back), so no cache-wide write-back or
-  // invalidate is needed between the workgroups of one tile.
-  unsigned long long* part = reinterpret_cast<unsigned long long*>(g.sk_partial);
-  const size_t own = static_cast<size_t>(u) * (BM * BN / 2);   // 8-byte words
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int v2 = 0; v2 < 8; ++v2) {
-        const unsigned long long x = (static_cast<unsigned long long>(__float_as_uint(acc[i][j][2 * v2 + 1])) << 32) |
-                                     __float_as_uint(acc[i][j][2 * v2]);
-        __hip_atomic_store(part + own + static_cast<size_t>(((i * TJ + j) * 8 + v2) * NT + tid), x,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          for (int v2 = 0; v2 < 8; ++v2) {
+            const unsigned long long x = (static_cast<unsigned long long>(__float_as_uint(acc[i][j][2 * v2 + 1])) << 32) |
+                                         __float_as_uint(acc[i][j][2 * v2]);
+            __hip_atomic_store(part + own + static_cast<size_t>(((i * TJ + j) * 8 + v2) * NT + tid), x,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          }
+      // the stores have reached the coherence point before the arrival is counted
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        int* cnt = &g.sk_counters[ndp + tt];
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        const int last = old == S - 1 ? 1 : 0;
+        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);   // ready for the next launch
+        *s_last = last;
       }
-  // the stores have reached the coherence point before the arrival is counted
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    int* cnt = &g.sk_counters[ndp + tt];
-    const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    const int last = old == S - 1 ? 1 : 0;
-    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);   // ready for the next launch
-    *s_last = last;
-  }
-  __syncthreads();
-  if (!*s_last) return;
+      __syncthreads();
+      if (*s_last) {
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
-  for (int v = 0; v < S; ++v) {
-    const unsigned long long* src = part + static_cast<size_t>(tt * S + v) * (BM * BN / 2);
+          for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
+        for (int v = 0; v < S; ++v) {
+          const unsigned long long* src = part + static_cast<size_t>(tt * S + v) * (BM * BN / 2);
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+          for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        // one 32x32 block at a time keeps the loads' registers few
-        unsigned long long p[8];
+            for (int j = 0; j < TJ; ++j) {
+              // one 32x32 block at a time keeps the loads' registers few
+              unsigned long long p[8];
 #pragma unroll
-        for (int v2 = 0; v2 < 8; ++v2)
-          p[v2] = __hip_atomic_load(src + static_cast<size_t>(((i * TJ + j) * 8 + v2) * NT + tid), __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_SYSTEM);
+              for (int v2 = 0; v2 < 8; ++v2)
+                p[v2] = __hip_atomic_load(src + static_cast<size_t>(((i * TJ + j) * 8 + v2) * NT + tid), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_SYSTEM);
 #pragma unroll
-        for (int v2 = 0; v2 < 8; ++v2) {
-          acc[i][j][2 * v2] += __uint_as_float(static_cast<unsigned>(p[v2]));
-          acc[i][j][2 * v2 + 1] += __uint_as_float(static_cast<unsigned>(p[v2] >> 32));
+              for (int v2 = 0; v2 < 8; ++v2) {
+                acc[i][j][2 * v2] += __uint_as_float(static_cast<unsigned>(p[v2]));
+                acc[i][j][2 * v2 + 1] += __uint_as_float(static_cast<unsigned>(p[v2] >> 32));
+              }
+            }
         }
+        finish();
       }
+    }
+    __syncthreads();   // the next item's tile loads overwrite the LDS read above
   }
-  finish();
 }
 
 #ifndef WAMC_GEMM_BIG
@@ -958,8 +972,10 @@ static void launch_sk(GemmEpi epi, const GemmArgs& g, hipStream_t s) {
   using Cfg = SkConfig<BM, BN, BK, STAGES, WGM, WGN>;
   const int B = g.M / g.rows_cap;
   const long long tiles_cap = static_cast<long long>(B) * ((g.rows_cap + BM - 1) / BM) * ((g.Nout + BN - 1) / BN);
-  // one workgroup per tile at the most rows; at least P so few tiles can be split
-  const unsigned grid = static_cast<unsigned>(std::max<long long>(tiles_cap, Cfg::kP));
+  // one workgroup per tile at the most rows, at least P so few tiles can be
+  // split, at most WAMC_SK_GRID_ROUNDS rounds of P (the workgroups loop)
+  const long long cap = static_cast<long long>(WAMC_SK_GRID_ROUNDS) * Cfg::kP;
+  const unsigned grid = static_cast<unsigned>(std::min(std::max<long long>(tiles_cap, Cfg::kP), cap));
   constexpr int NT = Cfg::kThreads;
   WAMC_EPI_DISPATCH(epi, (gemm_bf16_sk_kernel<E, BM, BN, BK, STAGES, WGM, WGN><<<grid, NT, 0, s>>>(g)));
 }
@@ -1069,8 +1085,12 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
                        (g.K < 4096 || t128 > 128);
   const bool use_sk = dtl_ok && WAMC_GEMM_SK && g.sk_partial && g.sk_counters &&
                       g.sk_partial_bytes >= SkSmall::kTileBytes;
-  // 256-wide tiles need d >= 256 (a QKV tile crosses at most one of the Q|K|V edges)
-  const long long t256 = static_cast<long long>((g.M + 255) / 256) * ((g.Nout + 255) / 256);
+  // 256-wide tiles need d >= 256 (a QKV tile crosses at most one of the Q|K|V edges).  They are
+  // chosen from the rows known on the host to be valid: a launch sized for many more rows than
+  // k_eff turns out to be would otherwise run 256-row tiles over a few rows (2.4x slower at 32 rows)
+  const long long rows_known = g.k_eff ? std::min(g.rows_lo, g.rows_cap) : g.rows_cap;
+  const long long t256 = static_cast<long long>(g.M / g.rows_cap) * ((rows_known + 255) / 256) *
+                         ((g.Nout + 255) / 256);
   const bool big = kGemmBig && g.d_model >= 256 && g.sk_partial_bytes >= SkBig::kTileBytes && t256 >= 2 * SkBig::kP;
   if (!use_ks2 && use_sk && big) {
     launch_sk<256, 256, 32, 4, 2, 4>(epi, g, s);

@@ -109,6 +109,7 @@ struct GemmArgs {
   int M, Nout, K;       // M = B * rows_cap
   int rows_cap;         // rows per episode
   const int32_t* k_eff; // nullable: valid rows per episode
+  int rows_lo;          // host-side lower bound on k_eff[b] (the tile shape is chosen for it; 0 = unknown)
   // EPI_QKV: out cols [0,d) -> q_out[m, c]; [d,2d) -> k cache row; [2d,3d) -> v cache row
   void* q_out;
   void* k_cache;        // [B, N, d] act (this layer)
