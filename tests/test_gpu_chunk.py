@@ -124,6 +124,39 @@ def test_bench_workload_full_size():
     _compare_chunk(wl, eng2, states, [res], lo, 1)
 
 
+def test_large_tile_split_schedule():
+    """c2 shapes with k = 3840 of N = 4096, the launch sized for every token
+    (rows_cap = N) and the library's own selection: the MLP up projection
+    takes 256x256 tiles (525 of them at 3840 rows: two full rounds of 256)
+    with the 13-tile last round split along K.  The selection is checked
+    against the oracle's rule on the GPU scores, the chunk against the oracle
+    chunk on that refresh set."""
+    wl = W.preset("c2_layer").with_(k=3840)
+    r = W.make_rollout(wl, chunks=2)
+    prec = O.Precision(wl.dtype)
+    states = _oracle_states(wl, r, prec)
+    eng = engine(wl, r)
+    eng.dense(batch_z(wl, r, 0))
+    eng.age.copy_(to_dev(np.stack(r.ages0)))
+    lo = torch.zeros((1, 1, wl.n_tokens, wl.d_model), dtype=torch.float32, device=DEV)
+    age_before = to_np(eng.age[0]).copy()
+    eng.chunk(batch_z(wl, r, 1), batch_q(wl, r, 1), wl.k, layer_out=lo)
+    torch.cuda.synchronize()
+    sel_idx, sel_k, _, _ = O.select(to_np(eng.score[0]), age_before, wl.k, wl.age_bound, cap=wl.n_tokens)
+    assert sel_k == wl.k, "fewer forced tokens than k: the 525-tile case"
+    assert int(eng.k_eff[0]) == sel_k and np.array_equal(to_np(eng.idx[0])[:sel_k], sel_idx)
+    res = O.refresh_chunk(states[0], r.z[0][1], r.qa[0][1], r.weights, wl.k, wl.age_bound, wl.n_heads,
+                          wl.ln_eps, wl.w_attn, wl.w_surprise, prec, idx_override=sel_idx)
+    _compare_chunk(wl, eng, states, [res], lo, 1)
+
+
+def test_ffn_not_multiple_of_64():
+    """FFN 520 (a multiple of 8, not of 64): the down projection's K takes the
+    plain bf16 GEMM kernel instead of the direct-to-LDS ones; dense prefill
+    and two refresh chunks on the oracle's sets."""
+    _run_override_rollout(W.preset("t_bf16_small").with_(d_ffn=520), 3)
+
+
 def test_stack_slice_d1536():
     _run_override_rollout(W.preset("t_bf16_stack"), 3)
 

@@ -83,9 +83,10 @@ def test_refresh_layer_wide(m, spare):
     """The d=1536, FFN 8960 layer over N=4096 cached tokens with m refreshed
     rows, the launch sized for the rows (rows_cap = m) or for every token
     (rows_cap = N, k_eff = m read on the device): covers the GEMM schedules
-    that split K over several workgroups, the one-tile-per-workgroup
-    rounds, and (m = N: 560 tiles of 256x256 in the MLP up projection) the
-    large-tile schedule with a split last round."""
+    that split K over several workgroups and the one-tile-per-workgroup
+    rounds of 128x128 tiles (a single-layer call knows no lower bound on
+    k_eff on the host, so it never takes the 256x256 tiles; the chunk test
+    with k = 3840 covers those)."""
     wl = W.preset("c2_layer")
     r = W.make_rollout(wl, chunks=1)
     prec = O.Precision(wl.dtype)
