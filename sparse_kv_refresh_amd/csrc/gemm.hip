@@ -162,13 +162,134 @@ __device__ __forceinline__ void fill_row_table(const GemmArgs& g, int m0, int* t
 // The bf16 kernels issue the MFMA with the weight fragment as operand A and
 // the activation fragment as operand B, i.e. they compute C^T blocks.  In the
 // 32x32 output layout that gives lane (half, col) ONE output row per block
-//   lr = wm*(BM/2) + i*32 + col
+//   lr = wm*WTM + i*32 + col
 // and, for element group g (v = 4g..4g+3), FOUR consecutive output columns
-//   n = n0 + wn*(BN/2) + j*32 + g*8 + half*4 + (0..3),
-// so each lane checks its row once and stores 4 columns with one 8-byte
-// (bf16) or 16-byte (f32) access.
-template <int EPI, int BM, int BN, int TI, int TJ, int WTM = BM / 2, int WTN = BN / 2>
-__device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t (&acc)[TI][TJ], int m0, int n0,
+//   n = n0 + wn*WTN + j*32 + g*8 + half*4 + (0..3).
+// Stored from that layout, one store instruction would touch 32 rows with 8
+// or 16 bytes each.  So the epilogue goes through LDS, one 32-row block per
+// wave row at a time: the waves holding accumulators write them (raw f32)
+// into a [WGM*32][BN+4] staging tile, then all NT threads of the workgroup
+// take 16-byte row chunks of it, apply bias / GELU / gate and residual with
+// loads of whole rows, and store whole rows.  The arithmetic per element is
+// the same as element-wise: v = acc + bias; out = act(v), or
+// out = resid + gate * v (one fma).
+template <int BM, int BN, int WTM>
+constexpr int epi_stage_bytes() {
+  return (BM / WTM) * 32 * (BN + 4) * 4;
+}
+
+template <int EPI, int BM, int BN, int TI, int TJ, int WTM, int WTN, int NT>
+__device__ __forceinline__ void tile_epilogue_staged(const GemmArgs& g, const f32x16_t (&acc)[TI][TJ], int n0, int wm,
+                                              int wn, int half, int col, const int* tab, float* stage, bool writer) {
+  constexpr int WGM = BM / WTM;
+  constexpr int SROWS = WGM * 32;          // staged rows per step
+  constexpr int SSTRIDE = BN + 4;          // floats; breaks bank aliasing of the row-wise writes
+  constexpr bool F32OUT = EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN || EPI == EPI_RESID_PLAIN;
+  constexpr int EPC = F32OUT ? 4 : 8;      // output elements per 16-byte chunk
+  constexpr int CPR = BN / EPC;            // chunks per row
+  constexpr int PER = SROWS * CPR / NT;    // chunks per thread per step
+  static_assert(PER * NT == SROWS * CPR && PER >= 1, "epilogue chunks / threads");
+  const int tid = threadIdx.x;
+  const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
+  const int d = g.d_model;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    // phase 1: raw accumulators of rows wm*WTM + i*32 + col -> staging row wm*32 + col
+    if (writer) {
+      float* srow = stage + (wm * 32 + col) * SSTRIDE + wn * WTN + half * 4;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg)
+          *reinterpret_cast<float4*>(srow + j * 32 + gg * 8) =
+              make_float4(acc[i][j][4 * gg + 0], acc[i][j][4 * gg + 1], acc[i][j][4 * gg + 2], acc[i][j][4 * gg + 3]);
+    }
+    __syncthreads();
+    // phase 2: chunk q -> staging row sr = q / CPR, columns (q % CPR)*EPC ..
+    float v[PER][EPC];
+    int rr[PER], nn[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int q = tid + p * NT;
+      const int sr = q / CPR, cc = q % CPR;
+      const int lr = (sr / 32) * WTM + i * 32 + (sr % 32);   // row within the tile
+      nn[p] = n0 + cc * EPC;
+      rr[p] = lr;
+      const float* sp = stage + sr * SSTRIDE + cc * EPC;
+#pragma unroll
+      for (int e = 0; e < EPC; e += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(sp + e);
+        v[p][e] = x.x; v[p][e + 1] = x.y; v[p][e + 2] = x.z; v[p][e + 3] = x.w;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int n = nn[p];
+      const bool nok = n < g.Nout;   // Nout % 8 == 0: a chunk lies wholly inside or outside
+      const int nc = nok ? n : 0;
+      const int rq = tab[rr[p]];
+      // bias (and gate) of the chunk's columns, then the element-wise step
+      float bsv[EPC];
+      if constexpr (EPC == 8) {
+        const uint4 bb = *reinterpret_cast<const uint4*>(bias + nc);
+        const uint32_t w[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bsv[2 * e] = __uint_as_float(w[e] << 16);
+          bsv[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+      } else {
+        const uint2 bb = *reinterpret_cast<const uint2*>(bias + nc);
+        bsv[0] = __uint_as_float(bb.x << 16); bsv[1] = __uint_as_float(bb.x & 0xffff0000u);
+        bsv[2] = __uint_as_float(bb.y << 16); bsv[3] = __uint_as_float(bb.y & 0xffff0000u);
+      }
+      if constexpr (F32OUT) {
+        float gt[4] = {1.f, 1.f, 1.f, 1.f};   // EPI_RESID_PLAIN: ungated
+        if constexpr (EPI != EPI_RESID_PLAIN) {
+          const uint2 gg = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(g.gate) + nc);
+          gt[0] = __uint_as_float(gg.x << 16); gt[1] = __uint_as_float(gg.x & 0xffff0000u);
+          gt[2] = __uint_as_float(gg.y << 16); gt[3] = __uint_as_float(gg.y & 0xffff0000u);
+        }
+        const size_t o = static_cast<size_t>(rq < 0 ? 0 : rq) * g.Nout + nc;
+        const float4 xin = *reinterpret_cast<const float4*>(g.resid_in + o);
+        float4 xo;
+        xo.x = fmaf(gt[0], v[p][0] + bsv[0], xin.x);
+        xo.y = fmaf(gt[1], v[p][1] + bsv[1], xin.y);
+        xo.z = fmaf(gt[2], v[p][2] + bsv[2], xin.z);
+        xo.w = fmaf(gt[3], v[p][3] + bsv[3], xin.w);
+        if (rq >= 0 && nok) *reinterpret_cast<float4*>(g.resid_out + o) = xo;
+      } else {
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y[e] = v[p][e] + bsv[e];
+          if constexpr (EPI == EPI_GELU) y[e] = gelu_erf_fast(y[e]);
+        }
+        uint4 w;
+        w.x = pack_bf16x2(y[0], y[1]);
+        w.y = pack_bf16x2(y[2], y[3]);
+        w.z = pack_bf16x2(y[4], y[5]);
+        w.w = pack_bf16x2(y[6], y[7]);
+        if constexpr (EPI == EPI_QKV || EPI == EPI_KV) {
+          // a chunk of 8 columns lies in one of Q | K | V (d % 8 == 0)
+          const int wr = nc / d, c = nc - wr * d;
+          const int which = wr + (EPI == EPI_KV ? 1 : 0);
+          const int r = which == 0 ? rq : tab[BM + rr[p]];
+          bf16_t* dst = static_cast<bf16_t*>(which == 0 ? g.q_out : (which == 1 ? g.k_cache : g.v_cache));
+          if (r >= 0 && nok) *reinterpret_cast<uint4*>(dst + static_cast<size_t>(r) * d + c) = w;
+        } else {
+          if (rq >= 0 && nok) *reinterpret_cast<uint4*>(static_cast<bf16_t*>(g.g_out) + static_cast<size_t>(rq) * g.Nout + nc) = w;
+        }
+      }
+    }
+    __syncthreads();   // the next step's staging overwrites these rows
+  }
+}
+
+// Element-wise store from the MFMA layout (see above): one row per lane and
+// block, four consecutive columns per element group.
+template <int EPI, int BM, int BN, int TI, int TJ, int WTM, int WTN>
+__device__ __forceinline__ void tile_epilogue_direct(const GemmArgs& g, const f32x16_t (&acc)[TI][TJ], int m0, int n0,
                                               int wm, int wn, int half, int col, const int* tab) {
   (void)m0;
   // The lane's TJ*4 column groups.  Nout % 4 == 0, so a group lies wholly
@@ -259,6 +380,21 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t 
   }
 }
 
+// Epilogue choice (measured at d = 1536): staging pays for the QKV epilogue,
+// whose K/V rows scatter to cache rows (QKV 55 -> 51 us at 2458 rows); for
+// the residual epilogues it breaks even and for GELU it costs 4 us, so those
+// store from the MFMA layout directly.
+template <int EPI, int BM, int BN, int TI, int TJ, int WTM, int WTN, int NT>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const f32x16_t (&acc)[TI][TJ], int m0, int n0,
+                                              int wm, int wn, int half, int col, const int* tab, float* stage,
+                                              bool writer) {
+  if constexpr (EPI == EPI_QKV || EPI == EPI_KV) {
+    tile_epilogue_staged<EPI, BM, BN, TI, TJ, WTM, WTN, NT>(g, acc, n0, wm, wn, half, col, tab, stage, writer);
+  } else {
+    if (writer) tile_epilogue_direct<EPI, BM, BN, TI, TJ, WTM, WTN>(g, acc, m0, n0, wm, wn, half, col, tab);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA GEMM
 // ---------------------------------------------------------------------------
@@ -275,8 +411,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) 
   const int m0 = tm * kBM, n0 = tn * kBN;
   if (tile_empty(g, m0, kBM)) return;
 
-  __shared__ bf16_t As[2][kBM * kLdsK];
-  __shared__ bf16_t Ws[2][kBN * kLdsK];
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][kBM * kLdsK];
+  __shared__ __attribute__((aligned(16))) bf16_t Ws[2][kBN * kLdsK];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
@@ -341,7 +477,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) 
   int* tab = reinterpret_cast<int*>(&As[0][0]);   // the last k-tile ended with a barrier
   fill_row_table<EPI, kBM>(g, m0, tab);
   __syncthreads();
-  tile_epilogue<EPI, kBM, kBN, 2, 2>(g, acc, m0, n0, wm, wn, half, col, tab);
+  static_assert(epi_stage_bytes<kBM, kBN, kBM / 2>() <= sizeof(Ws), "epilogue staging fits the W tiles");
+  tile_epilogue<EPI, kBM, kBN, 2, 2, kBM / 2, kBN / 2, kGemmThreads>(g, acc, m0, n0, wm, wn, half, col, tab,
+                                                                     reinterpret_cast<float*>(&Ws[0][0]), true);
 }
 
 // ---------------------------------------------------------------------------
@@ -493,7 +631,11 @@ void gemm_bf16_dtl_kernel(GemmArgs g) {
   int* tab = reinterpret_cast<int*>(&lds[0][0]);
   fill_row_table<EPI, BM>(g, m0, tab);
   __syncthreads();
-  tile_epilogue<EPI, BM, BN, TI, TJ>(g, acc, m0, n0, wm, wn, half, col, tab);
+  // staging after the row table
+  static_assert(2 * BM * 4 + epi_stage_bytes<BM, BN, BM / 2>() <= sizeof(lds), "epilogue staging fits the LDS");
+  tile_epilogue<EPI, BM, BN, TI, TJ, BM / 2, BN / 2, kGemmThreads>(
+      g, acc, m0, n0, wm, wn, half, col, tab, reinterpret_cast<float*>(reinterpret_cast<char*>(&lds[0][0]) + 2 * BM * 4),
+      true);
 }
 
 // ---------------------------------------------------------------------------
@@ -615,15 +757,19 @@ __global__ __launch_bounds__(kKs2Threads, 1) void gemm_bf16_dtl_ks2_kernel(GemmA
     fill_row_table<EPI, BM>(g, m0, tab);
   }
   __syncthreads();
-  if (grp == 1) return;
-  const float* src = xch + static_cast<size_t>(gw) * 64 * 64 + lane;
+  if (grp == 0) {
+    const float* src = xch + static_cast<size_t>(gw) * 64 * 64 + lane;
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] += src[((i * TJ + j) * 16 + v) * 64];
-  tile_epilogue<EPI, BM, BN, TI, TJ>(g, acc, m0, n0, wm, wn, half, col, tab);
+        for (int v = 0; v < 16; ++v) acc[i][j][v] += src[((i * TJ + j) * 16 + v) * 64];
+  }
+  __syncthreads();   // the exchange area is read; it now stages the epilogue (both groups store)
+  static_assert(epi_stage_bytes<BM, BN, BM / 2>() <= sizeof(lds[0]), "epilogue staging fits the exchange area");
+  tile_epilogue<EPI, BM, BN, TI, TJ, BM / 2, BN / 2, kKs2Threads>(g, acc, m0, n0, wm, wn, half, col, tab, xch,
+                                                                  grp == 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -851,7 +997,11 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
       int* tab = reinterpret_cast<int*>(&lds[0][0]);
       fill_row_table<EPI, BM, NT>(g, tl.m0, tab, tl.mend);
       __syncthreads();
-      tile_epilogue<EPI, BM, BN, TI, TJ, WTM, WTN>(g, acc, tl.m0, tl.n0, wm, wn, half, col, tab);
+      // staging after the row table, clear of the split flag at the end
+      static_assert(2 * BM * 4 + epi_stage_bytes<BM, BN, WTM>() + 16 <= sizeof(lds), "epilogue staging fits the LDS");
+      tile_epilogue<EPI, BM, BN, TI, TJ, WTM, WTN, NT>(
+          g, acc, tl.m0, tl.n0, wm, wn, half, col, tab,
+          reinterpret_cast<float*>(reinterpret_cast<char*>(&lds[0][0]) + 2 * BM * 4), true);
     };
     if (!split) {
       finish();
