@@ -251,8 +251,11 @@ int wamc_dense_prefill(const wamc_dims* dims, const wamc_layer_w* layers, const 
                        void* k_cache, void* v_cache, int32_t* age, float* layer_out, void* ws,
                        size_t ws_bytes, void* stream);
 
-/* Optional per-kernel timing (HIP events recorded around every kernel launch
- * on the launch stream; off by default).  Enabling clears the registry.
+/* Optional per-kernel timing, off by default.  While on, every kernel launch
+ * carries a pair of HIP events (hipExtLaunchKernel) that the runtime stamps
+ * with that kernel's own start and end on the launch stream; a step made of
+ * several small kernels (the age update from a caller-given set) is timed by
+ * events recorded around it.  Enabling clears the registry.
  * wamc_timing_count returns the number of kernel kinds seen; wamc_timing_get
  * synchronises the recorded events and returns, for kind i, its name, the
  * number of launches and the summed launch durations in milliseconds. */

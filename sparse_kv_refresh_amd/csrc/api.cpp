@@ -60,11 +60,9 @@ class EventTimer final : public KernelTimer {
   std::mutex mu;
   bool enabled = false;
   std::vector<Kind> kinds;
-  std::vector<Rec> pending;
+  std::vector<Rec> open;      // scopes begun, not yet ended
+  std::vector<Rec> pending;   // ended, events not yet read
   std::vector<hipEvent_t> pool;
-
-  static thread_local int cur_kind;
-  static thread_local hipEvent_t cur_start;
 
   hipEvent_t get_event() {
     if (!pool.empty()) {
@@ -77,8 +75,15 @@ class EventTimer final : public KernelTimer {
     return e;
   }
 
-  void begin(const char* kind, hipStream_t s) override {
+  bool begin(const char* kind, hipStream_t s, bool markers, hipEvent_t* start, hipEvent_t* stop) override {
     std::lock_guard<std::mutex> lk(mu);
+    hipEvent_t a = get_event();
+    hipEvent_t b = a ? get_event() : nullptr;
+    if (!a || !b || (markers && hipEventRecord(a, s) != hipSuccess)) {
+      if (a) pool.push_back(a);
+      if (b) pool.push_back(b);
+      return false;
+    }
     int k = -1;
     for (size_t i = 0; i < kinds.size(); ++i)
       if (kinds[i].name == kind) k = static_cast<int>(i);
@@ -86,27 +91,28 @@ class EventTimer final : public KernelTimer {
       kinds.push_back(Kind{kind, 0, 0.0});
       k = static_cast<int>(kinds.size()) - 1;
     }
-    cur_kind = k;
-    cur_start = get_event();
-    if (cur_start && hipEventRecord(cur_start, s) != hipSuccess) {
-      pool.push_back(cur_start);
-      cur_start = nullptr;
-    }
+    open.push_back(Rec{k, a, b});
+    *start = a;
+    *stop = b;
+    return true;
   }
 
-  void end(hipStream_t s) override {
+  void end(hipStream_t s, bool markers, hipEvent_t start, hipEvent_t stop, int launched) override {
     std::lock_guard<std::mutex> lk(mu);
-    if (!cur_start) return;
-    hipEvent_t e = get_event();
-    if (!e) return;
-    if (hipEventRecord(e, s) != hipSuccess) {
-      pool.push_back(e);
-      pool.push_back(cur_start);
-      cur_start = nullptr;
+    for (size_t i = open.size(); i-- > 0;) {
+      if (open[i].a != start) continue;
+      const Rec r = open[i];
+      open.erase(open.begin() + static_cast<long>(i));
+      // a scope whose kernel never launched (or that launched more than the
+      // one kernel the events describe) leaves no record
+      if (launched == 1 && (!markers || hipEventRecord(stop, s) == hipSuccess)) {
+        pending.push_back(r);
+      } else {
+        pool.push_back(r.a);
+        pool.push_back(r.b);
+      }
       return;
     }
-    pending.push_back(Rec{cur_kind, cur_start, e});
-    cur_start = nullptr;
   }
 
   void resolve() {
@@ -123,8 +129,6 @@ class EventTimer final : public KernelTimer {
     pending.clear();
   }
 };
-thread_local int EventTimer::cur_kind = 0;
-thread_local hipEvent_t EventTimer::cur_start = nullptr;
 
 EventTimer& timer_registry() {
   static EventTimer* t = new EventTimer();   // lives until process exit
@@ -644,11 +648,10 @@ int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   KernelTimer* tm = active_timer();
-  const bool bf16 = dims->dtype == WAMC_BF16;
-  const int B = dims->batch, N = dims->n_tokens, D = dims->d_model;
+  const int B = dims->batch, N = dims->n_tokens;
   hipError_t e;
   if (idx_override) {
-    TimedLaunch t(tm, "ages_from_set", s);
+    TimedLaunch t(tm, "ages_from_set", s, /*several_kernels=*/true);
     e = launch_ages_from_set(idx_override, k_eff_override, B, N, rows_cap, idx_out, k_eff_out, age, s);
   } else {
     // scoring's last step (sum of U, the weighted sum) runs inside the selection kernel

@@ -471,10 +471,10 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s, KernelT
     const long long units = static_cast<long long>((a.rows_cap + kAttnQ - 1) / kAttnQ) * a.H * a.B;
     const long long spare = units > kAttnP ? units + kAttnP : kAttnP;
     const unsigned grid = static_cast<unsigned>(a.part ? spare : units);
-    attn_bf16_kernel<<<grid, kAttnThreads2, 0, s>>>(a, scale2);
+    launch(attn_bf16_kernel, grid, kAttnThreads2, 0, s, a, scale2);
   } else {
     const dim3 grid((a.rows_cap + 3) / 4, a.H, a.B);
-    attn_f32_kernel<<<grid, 256, 0, s>>>(a, scale2);
+    launch(attn_f32_kernel, grid, 256, 0, s, a, scale2);
   }
   return hipGetLastError();
 }

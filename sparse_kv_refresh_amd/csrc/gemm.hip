@@ -1127,7 +1127,7 @@ static void launch_sk(GemmEpi epi, const GemmArgs& g, hipStream_t s) {
   const long long cap = static_cast<long long>(WAMC_SK_GRID_ROUNDS) * Cfg::kP;
   const unsigned grid = static_cast<unsigned>(std::min(std::max<long long>(tiles_cap, Cfg::kP), cap));
   constexpr int NT = Cfg::kThreads;
-  WAMC_EPI_DISPATCH(epi, (gemm_bf16_sk_kernel<E, BM, BN, BK, STAGES, WGM, WGN><<<grid, NT, 0, s>>>(g)));
+  WAMC_EPI_DISPATCH(epi, (launch(gemm_bf16_sk_kernel<E, BM, BN, BK, STAGES, WGM, WGN>, grid, NT, 0, s, g)));
 }
 
 // ---------------------------------------------------------------------------
@@ -1197,7 +1197,7 @@ static const char* gemm_name(const GemmArgs& g, GemmEpi e) {
 template <int BM, int BN, int BK, int STAGES>
 static void launch_dtl(GemmEpi epi, const GemmArgs& g, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(((g.M + BM - 1) / BM) * ((g.Nout + BN - 1) / BN));
-  WAMC_EPI_DISPATCH(epi, (gemm_bf16_dtl_kernel<E, BM, BN, BK, STAGES><<<grid, kGemmThreads, 0, s>>>(g)));
+  WAMC_EPI_DISPATCH(epi, (launch(gemm_bf16_dtl_kernel<E, BM, BN, BK, STAGES>, grid, kGemmThreads, 0, s, g)));
 }
 
 #ifndef WAMC_GEMM_TILE
@@ -1248,7 +1248,7 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
     launch_sk<WAMC_SK_BM, WAMC_SK_BN, WAMC_SK_BK, WAMC_SK_STAGES, WAMC_SK_WGM, WAMC_SK_WGN>(epi, g, s);
   } else if (use_ks2) {
     const unsigned grid = static_cast<unsigned>(t128);
-    WAMC_EPI_DISPATCH(epi, (gemm_bf16_dtl_ks2_kernel<E, 64, 2><<<grid, kKs2Threads, 0, s>>>(g)));
+    WAMC_EPI_DISPATCH(epi, (launch(gemm_bf16_dtl_ks2_kernel<E, 64, 2>, grid, kKs2Threads, 0, s, g)));
   } else if (dtl_ok) {
     switch (pick_tile(g)) {
       case 2: launch_dtl<128, 256, 32, 3>(epi, g, s); break;
@@ -1259,10 +1259,10 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
     }
   } else if (bf16) {
     const unsigned grid = static_cast<unsigned>(((g.M + kBM - 1) / kBM) * ((g.Nout + kBN - 1) / kBN));
-    WAMC_EPI_DISPATCH(epi, (gemm_bf16_kernel<E><<<grid, kGemmThreads, 0, s>>>(g)));
+    WAMC_EPI_DISPATCH(epi, (launch(gemm_bf16_kernel<E>, grid, kGemmThreads, 0, s, g)));
   } else {
     const unsigned grid = static_cast<unsigned>(((g.M + kFBM - 1) / kFBM) * ((g.Nout + kFBN - 1) / kFBN));
-    WAMC_EPI_DISPATCH(epi, (gemm_f32_kernel<E><<<grid, 256, 0, s>>>(g)));
+    WAMC_EPI_DISPATCH(epi, (launch(gemm_f32_kernel<E>, grid, 256, 0, s, g)));
   }
   return hipGetLastError();
 }

@@ -2,30 +2,83 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace wamc {
 
-// Records a pair of HIP events around each timed launch on the launch stream
-// (only while timing is enabled).  Implemented in api.cpp.
+// Optional per-kernel timer, implemented in api.cpp.  While timing is on, a
+// TimedLaunch scope takes a pair of HIP events from it.  The one kernel that
+// the scope launches through wamc::launch carries them: hipExtLaunchKernelGGL
+// stamps them with that kernel's own start and end on the device, which is
+// the interval a kernel trace reports.  A scope that launches several kernels
+// (`markers`) records the events around them on the stream instead.
 class KernelTimer {
  public:
   virtual ~KernelTimer() = default;
-  virtual void begin(const char* kind, hipStream_t s) = 0;
-  virtual void end(hipStream_t s) = 0;
+  // Returns false (no events) when no event could be had.
+  virtual bool begin(const char* kind, hipStream_t s, bool markers, hipEvent_t* start, hipEvent_t* stop) = 0;
+  // `launched` = kernels that took the events (1 is a valid record).
+  virtual void end(hipStream_t s, bool markers, hipEvent_t start, hipEvent_t stop, int launched) = 0;
 };
+
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  int launched = 0;
+};
+
+// The events of the TimedLaunch scope open on this host thread (null outside one).
+inline thread_local LaunchEvents* t_launch_events = nullptr;
 
 struct TimedLaunch {
   KernelTimer* t;
   hipStream_t s;
-  TimedLaunch(KernelTimer* timer, const char* kind, hipStream_t stream) : t(timer), s(stream) {
-    if (t) t->begin(kind, s);
+  bool markers;
+  bool on = false;
+  LaunchEvents ev;
+  LaunchEvents* outer;
+  TimedLaunch(KernelTimer* timer, const char* kind, hipStream_t stream, bool several_kernels = false)
+      : t(timer), s(stream), markers(several_kernels), outer(t_launch_events) {
+    if (t) on = t->begin(kind, s, markers, &ev.start, &ev.stop);
+    if (on && !markers) t_launch_events = &ev;
   }
   ~TimedLaunch() {
-    if (t) t->end(s);
+    if (on && !markers) t_launch_events = outer;
+    if (on) t->end(s, markers, ev.start, ev.stop, markers ? 1 : ev.launched);
   }
+  TimedLaunch(const TimedLaunch&) = delete;
+  TimedLaunch& operator=(const TimedLaunch&) = delete;
 };
+
+// kernel<<<grid, block, shmem, s>>>(args...) through the runtime's launch
+// call; inside a TimedLaunch scope the first such launch carries the scope's
+// events.  Errors are left for hipGetLastError, as with <<<>>>.
+template <typename... KArgs, typename... Args>
+inline void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                   Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  std::tuple<KArgs...> vals{static_cast<KArgs>(args)...};
+  void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+  std::apply([&ptrs](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  hipEvent_t a = nullptr, b = nullptr;
+  if (LaunchEvents* ev = t_launch_events) {
+    if (ev->launched++ == 0) {
+      a = ev->start;
+      b = ev->stop;
+    }
+  }
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  if (a)
+    (void)hipExtLaunchKernel(fn, grid, block, ptrs, shmem, s, a, b, 0);
+  else
+    (void)hipLaunchKernel(fn, grid, block, ptrs, shmem, s);
+}
 
 // ----- selection (select.hip) -----
 hipError_t launch_select(const float* score, int32_t* age, int B, int N, int k, int G, int rows_cap,

@@ -79,10 +79,10 @@ hipError_t launch_gather(bool bf16, const void* z, void* zref, const int32_t* id
   TimedLaunch t(timer, "gather", s);
   const dim3 grid((rows_cap + 3) / 4, B);
   if (bf16)
-    gather_kernel<bf16_t><<<grid, kRowThreads, 0, s>>>(static_cast<const bf16_t*>(z),
+    launch(gather_kernel<bf16_t>, grid, kRowThreads, 0, s, static_cast<const bf16_t*>(z),
         static_cast<bf16_t*>(zref), idx, k_eff, N, d, rows_cap, x, age_zero, zj);
   else
-    gather_kernel<float><<<grid, kRowThreads, 0, s>>>(static_cast<const float*>(z),
+    launch(gather_kernel<float>, grid, kRowThreads, 0, s, static_cast<const float*>(z),
         static_cast<float*>(zref), idx, k_eff, N, d, rows_cap, x, age_zero, zj);
   return hipGetLastError();
 }
@@ -256,11 +256,11 @@ hipError_t launch_gather_ln(bool bf16, const void* z, void* zref, const int32_t*
   const dim3 grid((rows_cap + 3) / 4, B);
   const int nc = row_chunks(d);
   if (bf16) {
-    WAMC_ROW_NC_DISPATCH(nc, if constexpr (NC > 0) gather_ln_kernel<NC, bf16_t><<<grid, kRowThreads, 0, s>>>(
+    WAMC_ROW_NC_DISPATCH(nc, if constexpr (NC > 0) launch(gather_ln_kernel<NC, bf16_t>, grid, kRowThreads, 0, s,
         static_cast<const bf16_t*>(z), static_cast<bf16_t*>(zref), idx, k_eff, N, d, rows_cap, x, age_zero,
         static_cast<const bf16_t*>(shift), static_cast<const bf16_t*>(scale), eps, static_cast<bf16_t*>(h), zj))
   } else {
-    WAMC_ROW_NC_DISPATCH(nc, if constexpr (NC > 0) gather_ln_kernel<NC, float><<<grid, kRowThreads, 0, s>>>(
+    WAMC_ROW_NC_DISPATCH(nc, if constexpr (NC > 0) launch(gather_ln_kernel<NC, float>, grid, kRowThreads, 0, s,
         static_cast<const float*>(z), static_cast<float*>(zref), idx, k_eff, N, d, rows_cap, x, age_zero,
         static_cast<const float*>(shift), static_cast<const float*>(scale), eps, static_cast<float*>(h), zj))
   }
@@ -326,18 +326,18 @@ hipError_t launch_ln_mod(bool bf16, const float* x, const void* shift, const voi
   const bool mod = shift != nullptr;
   const int nc = row_chunks(d);
   if (bf16 && mod) {
-    WAMC_ROW_NC_DISPATCH(nc, ln_mod_kernel<NC, bf16_t, true><<<grid, kRowThreads, 0, s>>>(x,
+    WAMC_ROW_NC_DISPATCH(nc, launch(ln_mod_kernel<NC, bf16_t, true>, grid, kRowThreads, 0, s, x,
         static_cast<const bf16_t*>(shift), static_cast<const bf16_t*>(scale), rows_cap, k_eff, d, eps,
         static_cast<bf16_t*>(h), zj))
   } else if (bf16) {
-    WAMC_ROW_NC_DISPATCH(nc, ln_mod_kernel<NC, bf16_t, false><<<grid, kRowThreads, 0, s>>>(x, nullptr, nullptr,
+    WAMC_ROW_NC_DISPATCH(nc, launch(ln_mod_kernel<NC, bf16_t, false>, grid, kRowThreads, 0, s, x, nullptr, nullptr,
         rows_cap, k_eff, d, eps, static_cast<bf16_t*>(h), zj))
   } else if (mod) {
-    WAMC_ROW_NC_DISPATCH(nc, ln_mod_kernel<NC, float, true><<<grid, kRowThreads, 0, s>>>(x,
+    WAMC_ROW_NC_DISPATCH(nc, launch(ln_mod_kernel<NC, float, true>, grid, kRowThreads, 0, s, x,
         static_cast<const float*>(shift), static_cast<const float*>(scale), rows_cap, k_eff, d, eps,
         static_cast<float*>(h), zj))
   } else {
-    WAMC_ROW_NC_DISPATCH(nc, ln_mod_kernel<NC, float, false><<<grid, kRowThreads, 0, s>>>(x, nullptr, nullptr,
+    WAMC_ROW_NC_DISPATCH(nc, launch(ln_mod_kernel<NC, float, false>, grid, kRowThreads, 0, s, x, nullptr, nullptr,
         rows_cap, k_eff, d, eps, static_cast<float*>(h), zj))
   }
   return hipGetLastError();

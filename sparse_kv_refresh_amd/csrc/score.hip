@@ -474,20 +474,20 @@ hipError_t launch_score_mass(bool bf16, const void* qa, const void* kc, int B, i
   if (bf16) {
     {
       TimedLaunch t(timer, "score_pass1", s);
-      score_pass1_bf16<<<grid, kScoreThreads, 0, s>>>(static_cast<const bf16_t*>(qa),
+      launch(score_pass1_bf16, grid, kScoreThreads, 0, s, static_cast<const bf16_t*>(qa),
           static_cast<const bf16_t*>(kc), B, H, N, A, d, p.chunk_keys, p.nchunks, scale2, ms);
     }
     TimedLaunch t(timer, "score_pass2", s);
-    score_pass2_bf16<<<grid, kScoreThreads, 0, s>>>(static_cast<const bf16_t*>(qa),
+    launch(score_pass2_bf16, grid, kScoreThreads, 0, s, static_cast<const bf16_t*>(qa),
         static_cast<const bf16_t*>(kc), B, H, N, A, d, p.chunk_keys, p.nchunks, scale2, ms, part);
   } else {
     {
       TimedLaunch t(timer, "score_pass1", s);
-      score_pass1_f32<<<grid, 256, 0, s>>>(static_cast<const float*>(qa), static_cast<const float*>(kc),
+      launch(score_pass1_f32, grid, 256, 0, s, static_cast<const float*>(qa), static_cast<const float*>(kc),
           B, H, N, A, d, dh, p.chunk_keys, p.nchunks, scale2, ms);
     }
     TimedLaunch t(timer, "score_pass2", s);
-    score_pass2_f32<<<grid, 256, 2 * A * sizeof(float), s>>>(static_cast<const float*>(qa),
+    launch(score_pass2_f32, grid, 256, 2 * A * sizeof(float), s, static_cast<const float*>(qa),
         static_cast<const float*>(kc), B, H, N, A, d, dh, p.chunk_keys, p.nchunks, scale2, ms, part);
   }
   return hipGetLastError();
@@ -499,10 +499,10 @@ hipError_t launch_score_partials(bool bf16, const float* part, int LH, const flo
   TimedLaunch t(timer, "score_combine", s);
   const dim3 grid(p.comb_blocks, B);
   if (bf16)
-    score_combine1<bf16_t><<<grid, kCombThreads, 0, s>>>(part, LH, mass_in, static_cast<const bf16_t*>(z),
+    launch(score_combine1<bf16_t>, grid, kCombThreads, 0, s, part, LH, mass_in, static_cast<const bf16_t*>(z),
         static_cast<const bf16_t*>(zref), N, d, mass_tmp, surprise_tmp, usum);
   else
-    score_combine1<float><<<grid, kCombThreads, 0, s>>>(part, LH, mass_in, static_cast<const float*>(z),
+    launch(score_combine1<float>, grid, kCombThreads, 0, s, part, LH, mass_in, static_cast<const float*>(z),
         static_cast<const float*>(zref), N, d, mass_tmp, surprise_tmp, usum);
   return hipGetLastError();
 }
@@ -511,7 +511,7 @@ hipError_t launch_score_finish(const float* mass_tmp, const float* surprise_tmp,
                                float w_attn_norm, float w_surprise, const ScorePlan& p, float* score,
                                float* mass_out, float* surprise_out, hipStream_t s, KernelTimer* timer) {
   TimedLaunch t(timer, "score_combine", s);
-  score_combine2<<<dim3((N + 255) / 256, B), 256, 0, s>>>(mass_tmp, surprise_tmp, usum, p.comb_blocks, N,
+  launch(score_combine2, dim3((N + 255) / 256, B), 256, 0, s, mass_tmp, surprise_tmp, usum, p.comb_blocks, N,
       w_attn_norm, w_surprise, score, mass_out, surprise_out);
   return hipGetLastError();
 }

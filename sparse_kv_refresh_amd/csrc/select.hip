@@ -393,15 +393,15 @@ static void launch_select_impl(const float* score, const ScoreInputs& si, int32_
                                int rows_cap, int32_t* idx, int32_t* k_eff, int32_t* n_forced, hipStream_t s) {
   const dim3 grid(B), block(kSelThreads);
   if (N <= 1024)
-    select_topk_kernel<1, SCORED><<<grid, block, 0, s>>>(score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+    launch(select_topk_kernel<1, SCORED>, grid, block, 0, s, score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
   else if (N <= 2048)
-    select_topk_kernel<2, SCORED><<<grid, block, 0, s>>>(score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+    launch(select_topk_kernel<2, SCORED>, grid, block, 0, s, score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
   else if (N <= 4096)
-    select_topk_kernel<4, SCORED><<<grid, block, 0, s>>>(score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+    launch(select_topk_kernel<4, SCORED>, grid, block, 0, s, score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
   else if (N <= 8192)
-    select_topk_kernel<8, SCORED><<<grid, block, 0, s>>>(score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+    launch(select_topk_kernel<8, SCORED>, grid, block, 0, s, score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
   else
-    select_topk_kernel<0, SCORED><<<grid, block, 0, s>>>(score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
+    launch(select_topk_kernel<0, SCORED>, grid, block, 0, s, score, si, age, N, k, G, rows_cap, idx, k_eff, n_forced);
 }
 
 hipError_t launch_select(const float* score, int32_t* age, int B, int N, int k, int G, int rows_cap,
@@ -421,15 +421,15 @@ hipError_t launch_select_union(const float* mass, const float* surprise, int32_t
                                hipStream_t s) {
   const dim3 grid(B), block(kSelThreads);
   if (N <= 1024)
-    select_union_kernel<1><<<grid, block, 0, s>>>(mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
+    launch(select_union_kernel<1>, grid, block, 0, s, mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
   else if (N <= 2048)
-    select_union_kernel<2><<<grid, block, 0, s>>>(mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
+    launch(select_union_kernel<2>, grid, block, 0, s, mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
   else if (N <= 4096)
-    select_union_kernel<4><<<grid, block, 0, s>>>(mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
+    launch(select_union_kernel<4>, grid, block, 0, s, mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
   else if (N <= 8192)
-    select_union_kernel<8><<<grid, block, 0, s>>>(mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
+    launch(select_union_kernel<8>, grid, block, 0, s, mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
   else
-    select_union_kernel<0><<<grid, block, 0, s>>>(mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
+    launch(select_union_kernel<0>, grid, block, 0, s, mass, surprise, age, N, n_attn, n_surprise, G, idx, k_eff, n_forced);
   return hipGetLastError();
 }
 
@@ -466,9 +466,9 @@ hipError_t launch_ages_from_set(const int32_t* idx_in, const int32_t* k_in, int 
   const int t = 256;
   const unsigned g = static_cast<unsigned>((total + t - 1) / t);
   if (idx_in != idx_out || k_in != k_out)
-    copy_set_kernel<<<g, t, 0, s>>>(idx_in, k_in, B, N, rows_cap, idx_out, k_out);
-  age_increment_kernel<<<g, t, 0, s>>>(age, total);
-  age_reset_kernel<<<dim3((rows_cap + t - 1) / t, B), t, 0, s>>>(age, idx_out, k_out, N, rows_cap);
+    launch(copy_set_kernel, g, t, 0, s, idx_in, k_in, B, N, rows_cap, idx_out, k_out);
+  launch(age_increment_kernel, g, t, 0, s, age, total);
+  launch(age_reset_kernel, dim3((rows_cap + t - 1) / t, B), t, 0, s, age, idx_out, k_out, N, rows_cap);
   return hipGetLastError();
 }
 
