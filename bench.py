@@ -12,9 +12,10 @@ ages U{0..3} so some tokens are forced.
 
 Printed as one JSON line: ms per refresh chunk (the metric), the library's own
 dense prefill of the same chunk, the speedup and its k_eff/N bound, refreshed
-tokens/s, the roofline of the dominant kernel (HIP events around every launch
-in a second pass of the same K steps), and the CPU oracle timed on a bounded
-sample of the same workload.
+tokens/s, the roofline of the dominant kernel (a second pass of the same K
+steps in which every launch carries HIP events stamped with that kernel's own
+start and end), and the CPU oracle timed on a bounded sample of the same
+workload.  Every timed loop starts once the GPU clocks are up (clock_warm).
 """
 from __future__ import annotations
 
@@ -39,8 +40,10 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps before each timed loop; default: as many as fill %.2f s "
+                         "(at least 5), enough for the GPU clocks to ramp up after idle" % WARM_SECONDS)
     ap.add_argument("--config", default="c2_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
@@ -65,6 +68,28 @@ def parse():
                     help="the pages' union rule on the 30-layer stack at budgets (b_a, b_s) = (0.4, 0.1) and "
                          "(0.6, 0.1), G = 2 (one JSON line each)")
     return ap.parse_args()
+
+
+WARM_SECONDS = 0.15
+
+
+def clock_warm(fn, min_calls: int = 1, seconds: float = WARM_SECONDS) -> int:
+    """Call fn at least `min_calls` times and until `seconds` of wall time have
+    passed; returns the number of calls.  After an idle gap (0.2 s is enough)
+    the GPU needs about 40 ms of back-to-back work to bring its clocks back up:
+    on the one-layer d=1536 chunk, steps timed straight after idle read
+    0.45 ms and fall to a flat 0.382 ms after ~100 steps.  Every timed loop
+    here starts behind such a warm-up so that it times the steady state."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+        if n >= min_calls and time.perf_counter() - t0 >= seconds:
+            return n
 
 
 def kernel_work(wl, k_eff_total: int):
@@ -188,7 +213,7 @@ def run_sweep(args):
         eng = wamc.Engine(wamc.dims_for(wl), weights, N, dev)
         for frac in (0.0, 0.1, 0.25, 0.5, 0.75, 1.0):
             k = int(round(frac * N))
-            eng.dense(zs[0])
+            clock_warm(lambda: eng.dense(zs[0]))
             before = eng.snapshot() if k == 0 else None
             check = {}
             for t in range(1, T):
@@ -254,7 +279,7 @@ def run_union(args):
     eng = wamc.Engine(wamc.dims_for(base), weights, N, dev)
     for b_a, b_s in ((0.4, 0.1), (0.6, 0.1)):
         na, ns = wamc.budget_rows(b_a, N), wamc.budget_rows(b_s, N)
-        eng.dense(zs[0])
+        clock_warm(lambda: eng.dense(zs[0]))
         keffs = []
         for t in range(1, T):
             ev[2 * t].record(stream)
@@ -315,9 +340,7 @@ def run_small_n(args):
             eng.dense(z1)
 
         def eager(fn, reps=20):
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
+            clock_warm(fn, 3)
             a.record(stream)
             for _ in range(reps):
                 fn()
@@ -335,9 +358,7 @@ def run_small_n(args):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 fn()
-            for _ in range(3):
-                g.replay()
-            torch.cuda.synchronize()
+            clock_warm(g.replay, 3)
             a.record(stream)
             for _ in range(reps):
                 g.replay()
@@ -386,6 +407,10 @@ def run_capacity(args):
     idx = torch.arange(N, dtype=torch.int32, device=dev)[None].contiguous()
     ws = torch.empty(wamc.workspace_bytes(dims1, N), dtype=torch.uint8, device=dev)
     rows = list(range(32, N + 1, 32)) + ([N] if N % 32 else [])
+    keff_n = torch.tensor([N], dtype=torch.int32, device=dev)
+    xw = x0.clone()  # the call updates its rows in place
+    clock_warm(lambda: wamc.refresh_layer(dims1, 0, w1, xw, idx, keff_n, N, kc, vc, ws, stream=stream))
+    del xw
     curve = []
     for m in rows:
         keff = torch.tensor([m], dtype=torch.int32, device=dev)
@@ -412,6 +437,11 @@ def run_capacity(args):
         for name, kk in (("k", k), ("fill", k_fill)):
             eng = wamc.Engine(wamc.dims_for(wl), weights, kk, dev)
             eng.dense(z0)
+
+            def chunk_from_zero_ages():
+                eng.age.zero_()
+                eng.chunk(z1, q1, kk, stream=stream)
+            clock_warm(chunk_from_zero_ages)
             ts = []
             for _ in range(6):
                 eng.age.zero_()
@@ -454,7 +484,10 @@ def run_plateau(args):
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     rows = list(range(32, N + 1, 32)) + ([N] if N % 32 else [])
     curves = {}
+    keff_n = torch.tensor([N], dtype=torch.int32, device=dev)
+    xw = x0.clone()  # the call updates its rows in place
     for mode in ("rows_cap_m", "rows_cap_N"):
+        clock_warm(lambda: wamc.refresh_layer(dims, 0, w, xw, idx, keff_n, N, kc, vc, ws, stream=stream))
         times = []
         for m in rows:
             cap = m if mode == "rows_cap_m" else N
@@ -545,10 +578,16 @@ def main():
     def dense_step():
         eng.dense(z1, stream=stream)
 
-    def timed(fn, steps, warmup):
+    def warm(fn, warmup):
+        if warmup is None:
+            return clock_warm(fn, 5)
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
+        return warmup
+
+    def timed(fn, steps, warmup):
+        w = warm(fn, warmup)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         a.record(stream)
@@ -557,12 +596,12 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return a.elapsed_time(b) / steps, 1e3 * wall / steps
+        return a.elapsed_time(b) / steps, 1e3 * wall / steps, w
 
     if args.profile_steps:
         if args.profile_events:
             wamc.timing_enable(True)
-        ms, _ = timed(refresh_step, args.steps, args.warmup)
+        ms, _, w = timed(refresh_step, args.steps, args.warmup)
         if args.profile_events:
             kt = wamc.timing_read()
             wamc.timing_enable(False)
@@ -573,19 +612,17 @@ def main():
             for _ in range(3):
                 dst.copy_(src)
             torch.cuda.synchronize()
-        print(json.dumps({"profile_steps": args.steps, "ms_per_step": ms}))
+        print(json.dumps({"profile_steps": args.steps, "warmup": w, "ms_per_step": ms}))
         return
 
-    ms_refresh, wall_refresh = timed(refresh_step, args.steps, args.warmup)
+    ms_refresh, wall_refresh, warm_refresh = timed(refresh_step, args.steps, args.warmup)
     k_eff = eng.k_eff.cpu().numpy().astype(np.int64)
     k_total = int(k_eff.sum())
-    ms_dense, _ = timed(dense_step, args.steps, max(1, args.warmup // 2))
+    ms_dense, _, _ = timed(dense_step, args.steps, args.warmup)
     # restore a refresh-ready state (the dense steps reset every age to 0)
     eng.dense(z0)
     eng.age.copy_(torch.from_numpy(np.stack(r.ages0)).to(dev))
-    for _ in range(args.warmup):
-        refresh_step()
-    torch.cuda.synchronize()
+    warm(refresh_step, args.warmup)
 
     # per-kernel pass: HIP events around every launch, same K steps
     wamc.timing_enable(True)
@@ -633,7 +670,7 @@ def main():
         "unit": "ms/chunk",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warm_refresh,
         "ms_per_step": ms_refresh,
         "higher_is_better": False,
         "scaling": "weak",
@@ -652,7 +689,8 @@ def main():
         "wall_ms_per_step": wall_refresh,
         "roofline": roof,
         "kernels": kernels,
-        "kernel_timing": "second pass of the same steps with HIP events around every launch on the launch stream",
+        "kernel_timing": "second pass of the same steps; every launch carries HIP events stamped with the "
+                         "kernel's own start and end on the launch stream (hipExtLaunchKernel)",
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

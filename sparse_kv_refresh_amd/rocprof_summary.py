@@ -1,11 +1,13 @@
 """Summaries of rocprofv3 output databases (rocpd SQLite files).
 
-    python -m sparse_kv_refresh_amd.rocprof_summary stats  <run_results.db> [--steps K]
+    python -m sparse_kv_refresh_amd.rocprof_summary stats  <run_results.db> [--steps K --warmup W]
     python -m sparse_kv_refresh_amd.rocprof_summary traffic <fetch.db> <write.db> --kernel NAME
         [--config c2_layer] [--skip-first N] [--out FILE]
 
 `stats` prints the per-kernel launch count, total and average duration from a
-`--kernel-trace` run.  `traffic` turns two `--pmc FETCH_SIZE` / `--pmc
+`--kernel-trace` run.  Given the run's W warm-up and K timed steps, a kernel
+launched a whole number of times per step is summarised over its dispatches
+of the last K steps only; other kernels (copies, fills) over all of them.  `traffic` turns two `--pmc FETCH_SIZE` / `--pmc
 WRITE_SIZE` runs into HBM bytes per launch of one kernel; each counter is
 scaled by what it reads for a plain 1 GiB device-to-device copy captured in
 the same run (bench.py --copy-calibration), so counter quirks of the chip
@@ -48,6 +50,22 @@ def kernel_stats(db: str):
     return [(n, int(c), float(t), float(a)) for n, c, t, a in rows]
 
 
+def kernel_stats_timed(db: str, steps: int, warmup: int):
+    """Per kernel name: count, total and mean duration in microseconds of its
+    dispatches in the last `steps` of `warmup + steps` steps, by start time
+    (the kernels view holds ns)."""
+    con = sqlite3.connect(db)
+    per = collections.defaultdict(list)
+    for n, dur in con.execute("select name, duration from kernels order by start"):
+        per[n].append(float(dur))
+    out = []
+    for n, ds in per.items():
+        if len(ds) % (steps + warmup) == 0:
+            ds = ds[-(len(ds) // (steps + warmup)) * steps:]
+        out.append((n, len(ds), sum(ds) / 1e3, sum(ds) / len(ds) / 1e3))
+    return sorted(out, key=lambda r: -r[2])
+
+
 def counters(db: str, name: str):
     con = sqlite3.connect(db)
     out = collections.defaultdict(list)
@@ -77,7 +95,8 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     a = sub.add_parser("stats")
     a.add_argument("db")
-    a.add_argument("--steps", type=int, default=0)
+    a.add_argument("--steps", type=int, default=0, help="timed steps of the run")
+    a.add_argument("--warmup", type=int, default=0, help="warm-up steps of the run, before the timed ones")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_db")
     b.add_argument("write_db")
@@ -93,7 +112,8 @@ def main(argv=None):
     if args.cmd == "stats":
         # the rocpd top_kernels view reports durations in microseconds
         print(f"{'kernel':90s} {'calls':>6s} {'total_us':>11s} {'avg_us':>9s}")
-        for n, c, t, av in kernel_stats(args.db):
+        rows = kernel_stats_timed(args.db, args.steps, args.warmup) if args.steps > 0 else kernel_stats(args.db)
+        for n, c, t, av in rows:
             print(f"{n[:90]:90s} {c:6d} {t:11.1f} {av:9.2f}")
         return
 
