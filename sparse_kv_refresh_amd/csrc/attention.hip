@@ -204,26 +204,76 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
 
-  // one 32-key half (kb) of tile t held in LDS stage `stage`
-  auto half_tile = [&](int t, int stage, int kb) {
+  // One 64-key tile t held in LDS stage `stage`.  Both 32-key halves are
+  // multiplied first (S^T = K Q^T) and the running max moves once per tile.
+  // LDS reads are issued a phase ahead of the MFMAs that consume them (the V^T
+  // fragments of a half while the previous products run), and the
+  // exponentials of the second half are computed while the P V products of
+  // the first half run on the matrix pipe.  `ragged` is true only for the
+  // last tile when N is not a multiple of 64 (a separate instantiation, so
+  // full tiles carry no per-element key test).
+  auto tile_step = [&](int t, int stage, auto ragged) {
     const uint4* Ks = Ks0 + stage * (kKsBytes / 16);
-    f32x16_t sacc = f32x16_t{};
-    const int krow = kb * 32 + col;
+    auto read_k = [&](int kb, bf16x8_t (&kf)[8]) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, Ks[ks_chunk(krow, 2 * s + half)]);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8_t, qf[s]), sacc, 0, 0, 0);
+      for (int s = 0; s < 8; ++s) kf[s] = __builtin_bit_cast(bf16x8_t, Ks[ks_chunk(kb * 32 + col, 2 * s + half)]);
+    };
+    // V^T fragment (tt, db) of half kb: dh row db*32 + col, keys kb*32 + 16*tt + half*4 + {0..3, 8..11}
+    auto read_v = [&](int kb, bf16x8_t (&vf)[8]) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16_t* vr = &Vt[(db * 32 + col) * kVtStride + kb * 32 + 16 * tt + half * 4];
+          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+          vf[tt * 4 + db] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        }
+    };
+    auto qk = [&](const bf16x8_t (&kf)[8]) {
+      f32x16_t acc = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], __builtin_bit_cast(bf16x8_t, qf[s]), acc, 0, 0, 0);
+      return acc;
+    };
+    bf16x8_t ka[8], kb1[8], v0[8], v1[8];
+    read_k(0, ka);
+    __builtin_amdgcn_sched_barrier(0);
+    // S for the first half, each MFMA followed by one K read of the second
+    // half; then S for the second half, each MFMA followed by one V^T read of
+    // the first half (each read lands in registers its MFMA has just freed)
+    read_k(1, kb1);
+    f32x16_t s0 = qk(ka);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
     }
-    // sacc[v]: key t*64 + kb*32 + (v/4)*8 + half*4 + v%4, query col
-    const int kbase = t * kAttnKeys + kb * 32;
-    if (kbase + 32 > N) {
+    __builtin_amdgcn_sched_barrier(0);
+    read_v(0, v0);
+    f32x16_t s1 = qk(kb1);
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (kbase + (v / 4) * 8 + half * 4 + (v % 4) >= N) sacc[v] = -INFINITY;
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
     }
-    float tmax = sacc[0];
+    __builtin_amdgcn_sched_barrier(0);
+    // s<kb>[v]: key t*64 + kb*32 + (v/4)*8 + half*4 + v%4, query col
+    if constexpr (decltype(ragged)::value) {
+      const int kbase = t * kAttnKeys;
 #pragma unroll
-    for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, sacc[v]);
+      for (int v = 0; v < 16; ++v) {
+        const int kv = kbase + (v / 4) * 8 + half * 4 + (v % 4);
+        if (kv >= N) s0[v] = -INFINITY;
+        if (kv + 32 >= N) s1[v] = -INFINITY;
+      }
+    }
+    float tmax = s0[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, s0[v]);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s1[v]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
     if (__ballot(tmax > m_run + lazy)) {
       const float m_new = fmaxf(m_run, tmax);
@@ -234,32 +284,46 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
       m_run = m_new;
     }
     const float mb = -m_run * scale2;
+    // P^T fragment tt of half kb covers keys kb*32 + 16*tt + (j/4)*8 + half*4 + j%4
+    auto probs = [&](f32x16_t& sacc, bf16x8_t (&pk)[2]) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale2, mb));
-      sacc[v] = p;
-      l_run += p;
-    }
-    // O^T[dh][q] += V^T[dh][key] P^T[key][q]; step tt covers keys
-    // kb*32 + 16*tt + (j/4)*8 + half*4 + j%4 for slot j
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      uint4 pk;
-      pk.x = pack_bf16x2(sacc[8 * tt + 0], sacc[8 * tt + 1]);
-      pk.y = pack_bf16x2(sacc[8 * tt + 2], sacc[8 * tt + 3]);
-      pk.z = pack_bf16x2(sacc[8 * tt + 4], sacc[8 * tt + 5]);
-      pk.w = pack_bf16x2(sacc[8 * tt + 6], sacc[8 * tt + 7]);
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pk);
-      const int koff = kb * 32 + 16 * tt + half * 4;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16_t* vr = &Vt[(db * 32 + col) * kVtStride + koff];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale2, mb));
+        sacc[v] = p;
+        l_run += p;
       }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        uint4 w;
+        w.x = pack_bf16x2(sacc[8 * tt + 0], sacc[8 * tt + 1]);
+        w.y = pack_bf16x2(sacc[8 * tt + 2], sacc[8 * tt + 3]);
+        w.z = pack_bf16x2(sacc[8 * tt + 4], sacc[8 * tt + 5]);
+        w.w = pack_bf16x2(sacc[8 * tt + 6], sacc[8 * tt + 7]);
+        pk[tt] = __builtin_bit_cast(bf16x8_t, w);
+      }
+    };
+    auto pv = [&](const bf16x8_t (&vf)[8], const bf16x8_t (&pk)[2]) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[tt * 4 + db], pk[tt], o[db], 0, 0, 0);
+    };
+    bf16x8_t p0[2], p1[2];
+    probs(s0, p0);
+    read_v(1, v1);
+    __builtin_amdgcn_sched_barrier(0);
+    pv(v0, p0);
+    probs(s1, p1);
+    // one MFMA of the first half's P V, then a share of the second half's
+    // exponentials, eight times
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 3);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    pv(v1, p1);
   };
 
   issue_k(0, 0);
@@ -275,8 +339,10 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
     lds_barrier();   // V^T visible; the prefetches stay in flight
     const int t = kt0 + it * kGroups + grp;
     if (t < kt1) {
-      half_tile(t, it & 1, 0);
-      half_tile(t, it & 1, 1);
+      if ((t + 1) * kAttnKeys > N)
+        tile_step(t, it & 1, std::true_type{});
+      else
+        tile_step(t, it & 1, std::false_type{});
     }
   }
 
