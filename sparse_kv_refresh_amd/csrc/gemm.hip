@@ -530,6 +530,34 @@ __device__ __forceinline__ int swz(int row, int kc) {
   return row * CPR + swz_kc<CPR>(row, kc);
 }
 
+// One BK-deep stage of a wave's TI x TJ block of 32x32 tiles, A rows from
+// `as`, W rows from `ws`.  The fragments of k-step s+1 are read before the
+// MFMAs of step s issue (the scheduling fence keeps that order), so their LDS
+// latency runs under those MFMAs.
+template <int BK, int TI, int TJ, int CPR>
+__device__ __forceinline__ void mma_stage(const uint4* as, const uint4* ws, int ra, int rb, int half,
+                                          f32x16_t (&acc)[TI][TJ]) {
+  bf16x8_t af[2][TI], bfr[2][TJ];
+  auto load = [&](int s, int b) {
+    const int kc = 2 * s + half;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) af[b][i] = __builtin_bit_cast(bf16x8_t, as[swz<CPR>(ra + 32 * i, kc)]);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) bfr[b][j] = __builtin_bit_cast(bf16x8_t, ws[swz<CPR>(rb + 32 * j, kc)]);
+  };
+  load(0, 0);
+#pragma unroll
+  for (int s = 0; s < BK / 16; ++s) {
+    if (s + 1 < BK / 16) load(s + 1, (s + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s & 1][j], af[s & 1][i], acc[i][j], 0, 0, 0);
+  }
+}
+
 template <int EPI, int BM, int BN, int BK, int STAGES>
 __global__ __launch_bounds__(kGemmThreads, (STAGES * (BM + BN) * BK * 2 <= 80 * 1024) ? 2 : 1)
 void gemm_bf16_dtl_kernel(GemmArgs g) {
@@ -975,21 +1003,7 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
       __builtin_amdgcn_s_barrier();
       if (q + STAGES - 1 < n) issue(q + STAGES - 1, (q + STAGES - 1) % STAGES);
       const uint4* as = lds[q % STAGES];
-      const uint4* ws = as + CHUNKS_A;
-#pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
-        const int kc = 2 * s + half;
-        bf16x8_t af[TI], bfr[TJ];
-#pragma unroll
-        for (int i = 0; i < TI; ++i) af[i] = __builtin_bit_cast(bf16x8_t, as[swz<CPR>(ra + 32 * i, kc)]);
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) bfr[j] = __builtin_bit_cast(bf16x8_t, ws[swz<CPR>(rb + 32 * j, kc)]);
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-      }
+      mma_stage<BK, TI, TJ, CPR>(as, as + CHUNKS_A, ra, rb, half, acc);
     }
 
     auto finish = [&]() {
