@@ -834,6 +834,30 @@ constexpr int kSkMaxSplit = WAMC_SK_MAX_SPLIT;   // most pieces per tile
 #endif
 // fixed cost of one piece (pipeline fill, partial store, arrival, fix-up), in k-tiles
 constexpr int kSkPieceCost = WAMC_SK_PIECE_COST;
+// k-tiles from which the launch grid makes room for a split tail
+constexpr int kSkLongK = 64;
+
+// Pieces per tile for r tail tiles of nk k-tiles each, P resident
+// workgroups and room for `room` pieces: S minimises (rounds of r*S pieces)
+// x (piece overhead + nk/S k-tiles), each piece >= kSkMinIters k-tiles.  The
+// host sizes the grid with it and the kernel re-derives it from k_eff.
+__host__ __device__ inline int sk_split(int r, int nk, int P, int room) {
+  if (r <= 0) return 1;
+  int smax = nk / kSkMinIters;
+  if (smax > kSkMaxSplit) smax = kSkMaxSplit;
+  if (smax > room / r) smax = room / r;
+  int S = 1;
+  float best = static_cast<float>((r + P - 1) / P) * static_cast<float>(kSkPieceCost + nk);
+  for (int c = 2; c <= smax; ++c) {
+    const float cost = static_cast<float>((r * c + P - 1) / P) *
+                       (static_cast<float>(kSkPieceCost) + static_cast<float>(nk) / static_cast<float>(c));
+    if (cost < best) {
+      best = cost;
+      S = c;
+    }
+  }
+  return S;
+}
 
 struct SkTile {
   int m0, mend, n0;   // first row, end of the episode's valid rows, first column
@@ -912,28 +936,11 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   const int nk = g.K / BK;
   // Work items: the ndp tiles done whole, then the r*S pieces of the split
   // tail.  Workgroup h takes items h, h + G, h + 2G, ... (G = the grid, a
-  // multiple of P and so of the 8 XCDs: an item runs on the XCD its remapped
-  // index belongs to).  A grid capped at a few rounds of resident workgroups
-  // keeps launches sized for many more rows than k_eff from paying for
-  // thousands of workgroups that would only exit.
-  // S minimises (rounds of r*S pieces) x (piece overhead + nk/S k-tiles),
-  // with the pieces within the grid's spare workgroups and the partial slots
-  // and >= kSkMinIters k-tiles each.
+  // multiple of the 8 XCDs: an item runs on the XCD its remapped index
+  // belongs to).  The pieces fit the grid's spare workgroups and the partial
+  // slots.
   const int G = static_cast<int>(gridDim.x);
-  int S = 1;
-  if (r > 0) {
-    const int room = min(max(G - ndp, 0), slots);
-    const int smax = max(1, min(min(kSkMaxSplit, nk / kSkMinIters), room / r));
-    float best = static_cast<float>((r + P - 1) / P) * static_cast<float>(kSkPieceCost + nk);
-    for (int c = 2; c <= smax; ++c) {
-      const float cost = static_cast<float>((r * c + P - 1) / P) * (static_cast<float>(kSkPieceCost) +
-                                                                    static_cast<float>(nk) / c);
-      if (cost < best) {
-        best = cost;
-        S = c;
-      }
-    }
-  }
+  const int S = sk_split(r, nk, P, min(max(G - ndp, 0), slots));
   const int W = ndp + r * S;
 
   // one LDS object only: a second __shared__ variable makes the compiler wait
@@ -1136,10 +1143,26 @@ static void launch_sk(GemmEpi epi, const GemmArgs& g, hipStream_t s) {
   using Cfg = SkConfig<BM, BN, BK, STAGES, WGM, WGN>;
   const int B = g.M / g.rows_cap;
   const long long tiles_cap = static_cast<long long>(B) * ((g.rows_cap + BM - 1) / BM) * ((g.Nout + BN - 1) / BN);
-  // one workgroup per tile at the most rows, at least P so few tiles can be
-  // split, at most WAMC_SK_GRID_ROUNDS rounds of P (the workgroups loop)
-  const long long cap = static_cast<long long>(WAMC_SK_GRID_ROUNDS) * Cfg::kP;
-  const unsigned grid = static_cast<unsigned>(std::min(std::max<long long>(tiles_cap, Cfg::kP), cap));
+  // One workgroup per tile at the most rows, at least P so that few tiles
+  // can be split, at most WAMC_SK_GRID_ROUNDS rounds of P (the workgroups
+  // loop), a multiple of the 8 XCDs.  With a long K the grid also makes room
+  // for the split of the tail (the split the kernel derives, given that
+  // room): at 2808 rows the d=1536 down projection's 264 tiles of 140
+  // k-tiles run as 792 pieces, 126.7 -> 118.9 us.  With a short K the
+  // partial-tile traffic and fix-up of a split cost more than they save (the
+  // QKV tail at 2458 rows: 47.1 -> 52.5 us as two-piece tiles), so the grid
+  // leaves no room for one.
+  constexpr long long P = Cfg::kP;
+  const long long cap = static_cast<long long>(WAMC_SK_GRID_ROUNDS) * P;
+  const long long ndp = tiles_cap / P * P, r = tiles_cap - ndp;
+  const long long slots = std::min<long long>(static_cast<long long>(g.sk_partial_bytes / Cfg::kTileBytes), 2 * P);
+  const long long room = std::max<long long>(std::min(cap - ndp, slots), 0);
+  const int nk = g.K / BK;
+  const int S = nk >= kSkLongK && r > 0 && r <= room
+                    ? sk_split(static_cast<int>(r), nk, static_cast<int>(P), static_cast<int>(room))
+                    : 1;
+  const long long items = ndp + r * S;
+  const unsigned grid = static_cast<unsigned>((std::min(std::max(items, P), cap) + 7) / 8 * 8);
   constexpr int NT = Cfg::kThreads;
   WAMC_EPI_DISPATCH(epi, (launch(gemm_bf16_sk_kernel<E, BM, BN, BK, STAGES, WGM, WGN>, grid, NT, 0, s, g)));
 }
