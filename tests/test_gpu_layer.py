@@ -78,7 +78,7 @@ def test_refresh_layer_parity(name):
 
 
 @pytest.mark.parametrize("m,spare", [(37, False), (37, True), (300, True), (1100, False), (1100, True),
-                                     (2458, False), (4096, False)])
+                                     (2458, False), (2808, False), (4096, False)])
 def test_refresh_layer_wide(m, spare):
     """The d=1536, FFN 8960 layer over N=4096 cached tokens with m refreshed
     rows, the launch sized for the rows (rows_cap = m) or for every token
@@ -86,7 +86,9 @@ def test_refresh_layer_wide(m, spare):
     that split K over several workgroups and the one-tile-per-workgroup
     rounds of 128x128 tiles (a single-layer call knows no lower bound on
     k_eff on the host, so it never takes the 256x256 tiles; the chunk test
-    with k = 3840 covers those)."""
+    with k = 3840 covers those).  At 2808 rows the down projection's 264
+    tiles of 140 k-tiles run as 792 pieces, more than one round of
+    workgroups, from a grid sized for them."""
     wl = W.preset("c2_layer")
     r = W.make_rollout(wl, chunks=1)
     prec = O.Precision(wl.dtype)
