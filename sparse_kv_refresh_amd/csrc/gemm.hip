@@ -1257,6 +1257,21 @@ static int pick_tile(const GemmArgs& g) {
   return WAMC_GEMM_TILE != 0 ? WAMC_GEMM_TILE : 1;
 }
 
+// 128x192 tiles (4 waves of 64x96, two resident workgroups per CU as for
+// 128x128) when, over the rows known to be valid, they need fewer rounds of
+// the 512 resident workgroups by more than their 1.5x larger tiles cost: the
+// QKV projection at 2458 rows is 720 tiles of 128x128 (1.4 rounds, run as
+// two) or 480 of 128x192 (one round).  Only the QKV and GELU epilogues take
+// them: with the residual epilogues the 64x96 wave tile spills.
+static bool wide_tiles_pay(const GemmArgs& g, long long rows_known) {
+  constexpr long long P = SkConfig<128, 192, 64, 2, 2, 2>::kP;
+  static_assert(SkConfig<128, 192, 64, 2, 2, 2>::kP == SkConfig<128, 128, 64, 2, 2, 2>::kP, "same residency");
+  const long long mt = static_cast<long long>(g.M / g.rows_cap) * ((rows_known + 127) / 128);
+  const long long r128 = (mt * ((g.Nout + 127) / 128) + P - 1) / P;
+  const long long r192 = (mt * ((g.Nout + 191) / 192) + P - 1) / P;
+  return g.sk_partial_bytes >= SkConfig<128, 192, 64, 2, 2, 2>::kTileBytes && 3 * r192 < 2 * r128;
+}
+
 hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer) {
   if (g.M <= 0 || g.Nout <= 0) return hipSuccess;
   TimedLaunch t(timer, gemm_name(g, epi), s);
@@ -1281,6 +1296,8 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   const bool big = kGemmBig && g.d_model >= 256 && g.sk_partial_bytes >= SkBig::kTileBytes && t256 >= 2 * SkBig::kP;
   if (!use_ks2 && use_sk && big) {
     launch_sk<256, 256, 32, 4, 2, 4>(epi, g, s);
+  } else if (!use_ks2 && use_sk && (epi == EPI_QKV || epi == EPI_GELU) && wide_tiles_pay(g, rows_known)) {
+    launch_sk<128, 192, 64, 2, 2, 2>(epi, g, s);
   } else if (!use_ks2 && use_sk) {
     launch_sk<WAMC_SK_BM, WAMC_SK_BN, WAMC_SK_BK, WAMC_SK_STAGES, WAMC_SK_WGM, WAMC_SK_WGN>(epi, g, s);
   } else if (use_ks2) {
