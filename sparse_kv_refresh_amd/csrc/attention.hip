@@ -5,9 +5,10 @@
 // unrefreshed tokens and the fresh K/V of refreshed ones (the QKV epilogue
 // has already written the fresh rows into the cache).  Non-causal, no mask.
 //
-// bf16 path (head_dim 128): flash-style, one workgroup per (128-query tile,
-// head, episode), 4 waves x 32 queries, keys streamed through LDS 64 at a
-// time with an online softmax (log2 domain, f32).
+// bf16 path (head_dim 128): flash-style, one workgroup of 8 waves per
+// (128-query tile, head, episode); two groups of 4 waves x 32 queries take
+// alternate 64-key tiles and merge (o, max, sum) at the end; online softmax
+// in the log2 domain, f32.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K is the A operand (read from
 //     LDS), Q^T the B operand (held in registers for the whole sweep).  The
 //     result layout gives each lane one query and 32 of the tile's keys, so
@@ -15,13 +16,14 @@
 //   * O^T += V^T P^T on the same MFMA: P^T is taken straight from the S^T
 //     accumulator registers (converted to bf16), V^T comes from a transposed
 //     copy of the V tile in LDS; each A fragment is two 8-byte LDS reads.
-//   * The next tile's K/V rows are fetched into registers while the current
-//     tile is multiplied (single LDS buffer, two barriers per tile); V is
-//     transposed in registers (4 keys x 8 dh per thread) and written to LDS
-//     as 8-byte rows of V^T.
-//   * Softmax VALU work is kept minimal: the scale is folded into one FMA
-//     feeding v_exp_f32, only the last (ragged) tile is masked, and the
-//     output rescale is lazy.
+//   * K tiles go global -> LDS by direct loads, double-buffered; the next
+//     tile's V rows are fetched into registers while the current tile is
+//     multiplied, then transposed (4 keys x 8 dh per thread) and written to
+//     LDS as 8-byte rows of V^T (two barriers per tile).
+//   * Per tile: both halves of S first, each MFMA followed by one LDS read
+//     for the next phase; one max per tile (lazy rescale); the second
+//     half's exponentials between the first half's P V MFMAs.  Only the
+//     ragged last tile is masked, in its own instantiation.
 // fp32 path: one wavefront per query row with a VALU online softmax.
 #include "common.h"
 #include "launch.h"
