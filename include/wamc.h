@@ -255,7 +255,8 @@ int wamc_dense_prefill(const wamc_dims* dims, const wamc_layer_w* layers, const 
  * carries a pair of HIP events (hipExtLaunchKernel) that the runtime stamps
  * with that kernel's own start and end on the launch stream; a step made of
  * several small kernels (the age update from a caller-given set) is timed by
- * events recorded around it.  Enabling clears the registry.
+ * events recorded around it.  Enabling clears the registry.  A diagnostic for
+ * eager calls: leave it off while a stream is being captured into a graph.
  * wamc_timing_count returns the number of kernel kinds seen; wamc_timing_get
  * synchronises the recorded events and returns, for kind i, its name, the
  * number of launches and the summed launch durations in milliseconds. */
