@@ -15,8 +15,11 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name", ["c1_tiny", "t_fp32_ragged", "t_bf16_small", "t_bf16_batch", "t_bf16_text",
-                                  "t_fp32_text"])
+                                  "t_fp32_text", "c2_layer"])
 def test_dense_parity(name):
+    """c2_layer is the benchmark's layer at full size (N=4096): its MLP up
+    projection runs on 128x192 tiles with a ragged last column tile (8960
+    columns)."""
     wl = W.preset(name)
     r = W.make_rollout(wl, chunks=1)
     prec = O.Precision(wl.dtype)
