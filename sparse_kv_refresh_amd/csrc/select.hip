@@ -11,9 +11,10 @@
 //    (2^31-1 - index)(31), so "largest key" = forced first, then higher
 //    score, then lower index; keys live in registers (up to 8 per thread, N <= 8192; larger N
 //    recomputes them from global memory in each pass);
-//  * the k_eff-th largest key is found by an MSB-first radix select: 8 passes
-//    of an 8-bit digit histogram in LDS, the bucket found by a wave-wide
-//    suffix scan -- no sort at all;
+//  * the k_eff-th largest key is found by an MSB-first radix select over
+//    the group it lies in (forced or not): 8-bit digit histograms in LDS
+//    from the highest bit in which the group's keys differ, the bucket found
+//    by a wave-wide suffix scan -- no sort at all;
 //  * the refresh set = keys >= that threshold, compacted in ascending token
 //    order with a block-wide ballot/popcount scan, which also yields the
 //    new ages.
@@ -43,6 +44,7 @@ struct SelShared {
   uint32_t hist[256];
   int red[kSelWaves];
   uint64_t red64[kSelWaves];
+  uint64_t red64b[kSelWaves];
   uint32_t sel, rem, whole;
   float red4[4];
 };
@@ -58,8 +60,21 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
   return v;
 }
 
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, kWave);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, kWave);
+    const uint64_t w = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
 // The count-th largest key (1 <= count < N) by an MSB-first radix select:
-// up to 8 passes of an 8-bit digit histogram in LDS, the bucket found by a
+// passes of an 8-bit digit histogram in LDS over the keys of the group the
+// answer lies in (the n_top keys with the top bit set, or the others), from
+// the highest bit in which the group's keys differ; the bucket is found by a
 // wave-wide suffix scan.  Once the bucket that holds the answer is taken
 // whole (its size equals the rank still wanted inside it -- with distinct
 // scores this happens after two or three passes), the answer is that
@@ -68,12 +83,54 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
 // register slot j when KPT > 0 (i = tid + j*1024); with KPT == 0 it is
 // recomputed for every i.  All threads of the block call it.
 template <int KPT, class KeyOf>
-__device__ uint64_t radix_threshold(KeyOf key_of, int N, uint32_t count, SelShared& sh) {
+__device__ uint64_t radix_threshold(KeyOf key_of, int N, uint32_t count, uint32_t n_top, SelShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  uint64_t prefix = 0;
-  uint32_t remaining = count;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    const uint64_t hi_mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
+  // The answer lies among the n_top keys with the top bit set (the forced
+  // tokens) when count <= n_top, else among the others at rank count - n_top.
+  // The group's smallest and largest keys share every bit above the highest
+  // bit in which they differ, so the first pass starts there instead of at
+  // bit 63 (where the forced bit and the shared exponent bits of the scores
+  // would take passes that split nothing).
+  const bool top = count <= n_top;
+  uint32_t remaining = top ? count : count - n_top;
+  uint64_t mx = 0, mn = ~0ull;
+  auto fold = [&](uint64_t key) {
+    if ((key >> 63) == (top ? 1ull : 0ull)) {
+      mx = key > mx ? key : mx;
+      mn = key < mn ? key : mn;
+    }
+  };
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int i = tid + j * kSelThreads;
+      if (i < N) fold(key_of(j, i));
+    }
+  } else {
+    for (int i = tid; i < N; i += kSelThreads) fold(key_of(0, i));
+  }
+  mx = wave_max_u64(mx);
+  mn = wave_min_u64(mn);
+  if (lane == 0) {
+    sh.red64[wid] = mn;
+    sh.red64b[wid] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    mn = sh.red64[w] < mn ? sh.red64[w] : mn;
+    mx = sh.red64b[w] > mx ? sh.red64b[w] : mx;
+  }
+  __syncthreads();   // sh is reused below
+  if (mx == mn) return mx;   // a group of one key
+  // bits >= fixed are known: those of the group's common prefix, then each
+  // pass's digit; a pass takes the (up to 8) next bits below them
+  int fixed = 64 - __clzll(static_cast<long long>(mx ^ mn));   // the highest differing bit + 1 (<= 63)
+  uint64_t prefix = mx & (~0ull << fixed);
+  while (fixed > 0) {
+    const int shift = fixed > 8 ? fixed - 8 : 0;
+    const uint64_t hi_mask = ~0ull << fixed;
+    const uint32_t dmask = (1u << (fixed - shift)) - 1u;
     if (tid < 256) sh.hist[tid] = 0;
     __syncthreads();
     if constexpr (KPT > 0) {
@@ -82,13 +139,13 @@ __device__ uint64_t radix_threshold(KeyOf key_of, int N, uint32_t count, SelShar
         const int i = tid + j * kSelThreads;
         if (i < N) {
           const uint64_t key = key_of(j, i);
-          if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+          if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[static_cast<uint32_t>(key >> shift) & dmask], 1u);
         }
       }
     } else {
       for (int i = tid; i < N; i += kSelThreads) {
         const uint64_t key = key_of(0, i);
-        if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+        if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[static_cast<uint32_t>(key >> shift) & dmask], 1u);
       }
     }
     __syncthreads();
@@ -133,27 +190,28 @@ __device__ uint64_t radix_threshold(KeyOf key_of, int N, uint32_t count, SelShar
     __syncthreads();
     prefix |= static_cast<uint64_t>(sh.sel) << shift;
     remaining = sh.rem;
+    fixed = shift;
     if (sh.whole && shift > 0) {
       // every key of the bucket is selected: the answer is its minimum
       const uint64_t mask = ~0ull << shift;
-      uint64_t mn = ~0ull;
+      uint64_t m = ~0ull;
       if constexpr (KPT > 0) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
           const int i = tid + j * kSelThreads;
           if (i < N) {
             const uint64_t key = key_of(j, i);
-            if ((key & mask) == prefix && key < mn) mn = key;
+            if ((key & mask) == prefix && key < m) m = key;
           }
         }
       } else {
         for (int i = tid; i < N; i += kSelThreads) {
           const uint64_t key = key_of(0, i);
-          if ((key & mask) == prefix && key < mn) mn = key;
+          if ((key & mask) == prefix && key < m) m = key;
         }
       }
-      mn = wave_min_u64(mn);
-      if (lane == 0) sh.red64[wid] = mn;
+      m = wave_min_u64(m);
+      if (lane == 0) sh.red64[wid] = m;
       __syncthreads();
       uint64_t r = ~0ull;
 #pragma unroll
@@ -305,7 +363,8 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     else return rank_key(get_score(i), age[i] >= G, i);
   };
   uint64_t thr = 0;
-  if (!take_all && !take_none) thr = radix_threshold<KPT>(key_of, N, static_cast<uint32_t>(ke), sh);
+  if (!take_all && !take_none)
+    thr = radix_threshold<KPT>(key_of, N, static_cast<uint32_t>(ke), static_cast<uint32_t>(n_forced), sh);
   auto age_of = [&](int j, int i) -> int {
     if constexpr (KPT > 0) return ag[j];
     else return age[i];
@@ -374,9 +433,9 @@ __global__ __launch_bounds__(kSelThreads) void select_union_kernel(
   const uint64_t kNone = ~0ull;
   uint64_t tp = kNone, tu = kNone;
   if (n_attn >= N) tp = 0;
-  else if (n_attn > 0) tp = radix_threshold<KPT>(kp_of, N, static_cast<uint32_t>(n_attn), sh);
+  else if (n_attn > 0) tp = radix_threshold<KPT>(kp_of, N, static_cast<uint32_t>(n_attn), 0u, sh);
   if (n_surprise >= N) tu = 0;
-  else if (n_surprise > 0) tu = radix_threshold<KPT>(ku_of, N, static_cast<uint32_t>(n_surprise), sh);
+  else if (n_surprise > 0) tu = radix_threshold<KPT>(ku_of, N, static_cast<uint32_t>(n_surprise), 0u, sh);
   const int ke = compact_set<KPT>(
       [&](int j, int i) {
         return age_of(j, i) >= G || (tp != kNone && kp_of(j, i) >= tp) || (tu != kNone && ku_of(j, i) >= tu);
