@@ -41,11 +41,11 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 
 struct SelShared {
-  uint32_t hist[256];
+  uint32_t hist[3][256];     // a pass's histogram rotates through three buffers
   int red[kSelWaves];
+  int red2[2][kSelWaves];    // per-wave counts of the compaction, alternating
   uint64_t red64[kSelWaves];
   uint64_t red64b[kSelWaves];
-  uint32_t sel, rem, whole;
   float red4[4];
 };
 
@@ -121,77 +121,83 @@ __device__ uint64_t radix_threshold(KeyOf key_of, int N, uint32_t count, uint32_
     mn = sh.red64[w] < mn ? sh.red64[w] : mn;
     mx = sh.red64b[w] > mx ? sh.red64b[w] : mx;
   }
+  // the first pass's histogram; every wave is past any earlier reader of it
+  if (tid < 256) sh.hist[0][tid] = 0;
   __syncthreads();   // sh is reused below
   if (mx == mn) return mx;   // a group of one key
   // bits >= fixed are known: those of the group's common prefix, then each
   // pass's digit; a pass takes the (up to 8) next bits below them
   int fixed = 64 - __clzll(static_cast<long long>(mx ^ mn));   // the highest differing bit + 1 (<= 63)
   uint64_t prefix = mx & (~0ull << fixed);
-  while (fixed > 0) {
+  // One barrier per pass: pass p counts into buffer p%3 (zeroed during the
+  // pass before) and zeroes buffer (p+1)%3, whose last readers finished
+  // before the previous barrier; every wave then finds the bucket itself.
+  for (int pass = 0; fixed > 0; ++pass) {
     const int shift = fixed > 8 ? fixed - 8 : 0;
     const uint64_t hi_mask = ~0ull << fixed;
     const uint32_t dmask = (1u << (fixed - shift)) - 1u;
-    if (tid < 256) sh.hist[tid] = 0;
-    __syncthreads();
+    uint32_t* hist = sh.hist[pass % 3];
+    if (tid < 256) sh.hist[(pass + 1) % 3][tid] = 0;
     if constexpr (KPT > 0) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const int i = tid + j * kSelThreads;
         if (i < N) {
           const uint64_t key = key_of(j, i);
-          if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[static_cast<uint32_t>(key >> shift) & dmask], 1u);
+          if ((key & hi_mask) == prefix) atomicAdd(&hist[static_cast<uint32_t>(key >> shift) & dmask], 1u);
         }
       }
     } else {
       for (int i = tid; i < N; i += kSelThreads) {
         const uint64_t key = key_of(0, i);
-        if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[static_cast<uint32_t>(key >> shift) & dmask], 1u);
+        if ((key & hi_mask) == prefix) atomicAdd(&hist[static_cast<uint32_t>(key >> shift) & dmask], 1u);
       }
     }
     __syncthreads();
-    if (wid == 0) {
-      // lane l owns bins 4l..4l+3; suffix sums find the bucket that holds
-      // the remaining-th largest key
-      const uint32_t h0 = sh.hist[4 * lane], h1 = sh.hist[4 * lane + 1];
-      const uint32_t h2 = sh.hist[4 * lane + 2], h3 = sh.hist[4 * lane + 3];
-      const uint32_t s = h0 + h1 + h2 + h3;
-      uint32_t suf = s;
+    // lane l owns bins 4l..4l+3; suffix sums find the bucket that holds the
+    // remaining-th largest key (exactly one lane does)
+    const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+    const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+    const uint32_t s4 = h0 + h1 + h2 + h3;
+    uint32_t suf = s4;
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t v = __shfl_down(suf, o, kWave);
-        if (lane + o < kWave) suf += v;
-      }
-      const uint32_t above = suf - s;
-      if (above < remaining && remaining <= suf) {
-        uint32_t c = above;
-        uint32_t sel;
-        if (c + h3 >= remaining) {
-          sel = 4 * lane + 3;
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t v = __shfl_down(suf, o, kWave);
+      if (lane + o < kWave) suf += v;
+    }
+    const uint32_t above = suf - s4;
+    const bool found = above < remaining && remaining <= suf;
+    uint32_t sel = 0, rem = 0, whole = 0;
+    if (found) {
+      uint32_t c = above;
+      if (c + h3 >= remaining) {
+        sel = 4 * lane + 3;
+      } else {
+        c += h3;
+        if (c + h2 >= remaining) {
+          sel = 4 * lane + 2;
         } else {
-          c += h3;
-          if (c + h2 >= remaining) {
-            sel = 4 * lane + 2;
+          c += h2;
+          if (c + h1 >= remaining) {
+            sel = 4 * lane + 1;
           } else {
-            c += h2;
-            if (c + h1 >= remaining) {
-              sel = 4 * lane + 1;
-            } else {
-              c += h1;
-              sel = 4 * lane;
-            }
+            c += h1;
+            sel = 4 * lane;
           }
         }
-        const uint32_t hs = sel == 4 * lane + 3 ? h3 : sel == 4 * lane + 2 ? h2 : sel == 4 * lane + 1 ? h1 : h0;
-        sh.sel = sel;
-        sh.rem = remaining - c;
-        sh.whole = hs == remaining - c ? 1u : 0u;
       }
+      const uint32_t hs = sel == 4 * lane + 3 ? h3 : sel == 4 * lane + 2 ? h2 : sel == 4 * lane + 1 ? h1 : h0;
+      rem = remaining - c;
+      whole = hs == rem ? 1u : 0u;
     }
-    __syncthreads();
-    prefix |= static_cast<uint64_t>(sh.sel) << shift;
-    remaining = sh.rem;
+    const int fl = __builtin_ctzll(__ballot(found));
+    sel = __shfl(sel, fl, kWave);
+    rem = __shfl(rem, fl, kWave);
+    whole = __shfl(whole, fl, kWave);
+    prefix |= static_cast<uint64_t>(sel) << shift;
+    remaining = rem;
     fixed = shift;
-    if (sh.whole && shift > 0) {
+    if (whole && shift > 0) {
       // every key of the bucket is selected: the answer is its minimum
       const uint64_t mask = ~0ull << shift;
       uint64_t m = ~0ull;
@@ -230,23 +236,27 @@ template <int KPT, class FlagOf, class AgeOf>
 __device__ int compact_set(FlagOf flag_of, AgeOf age_of, int N, int32_t* __restrict__ idx,
                            int32_t* __restrict__ age, SelShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  int base = 0;
+  int base = 0, parity = 0;
+  // one barrier per tile: the per-wave counts alternate between two arrays,
+  // and a wave can only write tile t+1's counts after every wave passed the
+  // barrier of tile t, that is after reading tile t-1's
   auto tile = [&](int j, int i, bool flag) {
     const uint64_t ball = __ballot(flag);
     const int wpre = __popcll(ball & ((1ull << lane) - 1ull));
-    if (lane == 0) sh.red[wid] = __popcll(ball);
+    int* red = sh.red2[parity];
+    parity ^= 1;
+    if (lane == 0) red[wid] = __popcll(ball);
     __syncthreads();
     int off = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) {
-      const int c = sh.red[w];
+      const int c = red[w];
       off += w < wid ? c : 0;
       tot += c;
     }
     if (flag) idx[base + off + wpre] = i;
     if (i < N) age[i] = flag ? 0 : age_of(j, i) + 1;
     base += tot;
-    __syncthreads();
   };
   if constexpr (KPT > 0) {
 #pragma unroll
