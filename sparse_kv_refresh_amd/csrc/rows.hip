@@ -125,7 +125,8 @@ template <int NC, typename T>
 __device__ __forceinline__ void load_row(const T* __restrict__ p, int d, int lane, float (&v)[NC][4]) {
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-    if (j * 256 >= d) break;
+    // chunks past d read column 0 (valid memory) and are never used; no
+    // branch, so every load of the row is in flight at once
     const int c = lane * 4 + j * 256;
     const int cc = c < d ? c : 0;
     if constexpr (sizeof(T) == 2) {
@@ -167,17 +168,25 @@ __device__ __forceinline__ void row_stats(const float (&v)[NC][4], int d, int la
   rstd = 1.0f / sqrtf(var + eps);
 }
 
-// h = (v - mean) * rstd, times (1 + scale) plus shift when MOD, rounded to T;
-// the shift/scale chunks are loaded as one batch first
+// The shift/scale chunks of a row, loaded in the same batch as the row itself
+// (they do not depend on it), so that one memory round trip covers both.
+template <int NC, typename T, bool MOD>
+struct RowMod {
+  float sh[NC][4], sc[NC][4];
+  __device__ __forceinline__ void load(const T* __restrict__ shift, const T* __restrict__ scale, int d, int lane) {
+    if constexpr (MOD) {
+      load_row<NC>(shift, d, lane, sh);
+      load_row<NC>(scale, d, lane, sc);
+    }
+  }
+};
+
+// h = (v - mean) * rstd, times (1 + scale) plus shift when MOD, rounded to T
 template <int NC, typename T, bool MOD>
 __device__ __forceinline__ void row_norm_store(const float (&v)[NC][4], int d, int lane, float mean, float rstd,
-                                               const T* __restrict__ shift, const T* __restrict__ scale,
-                                               T* __restrict__ hr) {
-  float sh[NC][4], sc[NC][4];
-  if constexpr (MOD) {
-    load_row<NC>(shift, d, lane, sh);
-    load_row<NC>(scale, d, lane, sc);
-  }
+                                               const RowMod<NC, T, MOD>& md, T* __restrict__ hr) {
+  const auto& sh = md.sh;
+  const auto& sc = md.sc;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     if (j * 256 >= d) break;
@@ -224,6 +233,8 @@ __global__ __launch_bounds__(kRowThreads) void gather_ln_kernel(
   float* xr = x + row * d;
   float v[NC][4];
   load_row<NC>(z + src, d, lane, v);
+  RowMod<NC, T, true> md;
+  md.load(shift, scale, d, lane);
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     if (j * 256 >= d) break;
@@ -244,7 +255,7 @@ __global__ __launch_bounds__(kRowThreads) void gather_ln_kernel(
   if (age_zero && lane == 0) age_zero[static_cast<size_t>(b) * N + t] = 0;
   float mean, rstd;
   row_stats(v, d, lane, eps, mean, rstd);
-  row_norm_store<NC, T, true>(v, d, lane, mean, rstd, shift, scale, h + row * d);
+  row_norm_store<NC, T, true>(v, d, lane, mean, rstd, md, h + row * d);
 }
 
 hipError_t launch_gather_ln(bool bf16, const void* z, void* zref, const int32_t* idx, const int32_t* k_eff, int B,
@@ -283,9 +294,11 @@ __global__ __launch_bounds__(kRowThreads) void ln_mod_kernel(
   if constexpr (NC > 0) {
     float v[NC][4];
     load_row<NC>(x + row * d, d, lane, v);
+    RowMod<NC, T, MOD> md;
+    md.load(shift, scale, d, lane);
     float mean, rstd;
     row_stats(v, d, lane, eps, mean, rstd);
-    row_norm_store<NC, T, MOD>(v, d, lane, mean, rstd, shift, scale, h + row * d);
+    row_norm_store<NC, T, MOD>(v, d, lane, mean, rstd, md, h + row * d);
   } else {
     // rows too long for registers: three streaming passes, same chunk
     // assignment and summation order
