@@ -20,7 +20,6 @@ workload.  Every timed loop starts once the GPU clocks are up (clock_warm).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -120,12 +119,6 @@ def kernel_work(wl, k_eff_total: int):
     }
 
 
-def source_hash(name: str) -> str:
-    p = os.path.join(ROOT, "sparse_kv_refresh_amd", "csrc", name)
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
 KERNEL_SOURCE = {"gemm_qkv": "gemm.hip", "gemm_out_resid": "gemm.hip", "gemm_up_gelu": "gemm.hip",
                  "gemm_down_resid": "gemm.hip", "attention": "attention.hip", "score_pass1": "score.hip",
                  "score_pass2": "score.hip", "select": "select.hip", "gather": "rows.hip", "gather_ln": "rows.hip", "ln_mod": "rows.hip"}
@@ -139,6 +132,7 @@ def measured_traffic(kind: str, config: str):
         return None
     with open(path) as f:
         rec = json.load(f)
+    from sparse_kv_refresh_amd.rocprof_summary import source_hash
     if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCE[kind]):
         return None
     return rec.get("hbm_bytes_per_launch")

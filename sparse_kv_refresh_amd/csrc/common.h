@@ -108,23 +108,30 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
 }
 
-// erf by the rational approximation of Abramowitz & Stegun, Handbook of
-// Mathematical Functions (1964), formula 7.1.26: for x >= 0,
-//   erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
-//   t = 1 / (1 + p x),  |error| <= 1.5e-7,
-// extended to x < 0 by oddness.  Used where the result is rounded to bf16
-// (relative precision 2^-8), so the approximation error is invisible.
-__device__ __forceinline__ float erf_as7126(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
-                                       -0.284496736f), 0.254829592f);
-  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
-  return copysignf(1.0f - poly * e, x);
-}
-
+// GELU with erf by the approximation of Abramowitz & Stegun, Handbook of
+// Mathematical Functions (1964), formula 7.1.28: for u >= 0,
+//   erf(u) = 1 - (1 + a1 u + a2 u^2 + ... + a6 u^6)^-16,  |error| <= 3e-7.
+// Here u = |x| / sqrt(2), folded into the coefficients (c_i = a_i 2^(-i/2)),
+// and with r = (1 + c1 |x| + ... + c6 |x|^6)^-16 = 1 - erf(|x|/sqrt(2)):
+//   GELU(x) = x (1 + erf(x/sqrt2)) / 2 = max(x, 0) - |x| r / 2
+// (for x < 0 the left side is x r / 2).  One reciprocal and no exponential;
+// for large |x| the 16th power overflows to +inf and r to 0, which is the
+// limit.  Used where the result is rounded to bf16 (relative precision
+// 2^-8), so the approximation error does not show.
 __device__ __forceinline__ float gelu_erf_fast(float x) {
-  return 0.5f * x * (1.0f + erf_as7126(x * 0.70710678118654752440f));
+  const float ax = fabsf(x);
+  float q = fmaf(ax, 5.38297490e-06f, 4.88906371e-05f);
+  q = fmaf(q, ax, 3.80035744e-05f);
+  q = fmaf(q, ax, 3.27762635e-03f);
+  q = fmaf(q, ax, 2.11410057e-02f);
+  q = fmaf(q, ax, 4.98673469e-02f);
+  q = fmaf(q, ax, 1.0f);
+  q *= q;
+  q *= q;
+  q *= q;
+  q *= q;
+  const float r = __builtin_amdgcn_rcpf(q);
+  return fmaf(-0.5f * ax, r, fmaxf(x, 0.0f));
 }
 
 }  // namespace wamc

@@ -85,9 +85,15 @@ def copy_factor(vals: dict, counter: str) -> float:
 
 
 def source_hash(fname: str) -> str:
-    p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", fname)
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel's source file together with the shared headers it
+    includes (every csrc/*.h, in name order), so that a change to either
+    marks the counters taken before it as stale."""
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    h = hashlib.sha256()
+    for name in [fname] + sorted(n for n in os.listdir(d) if n.endswith(".h")):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def main(argv=None):
