@@ -14,12 +14,11 @@
 //     result layout gives each lane one query and 32 of the tile's keys, so
 //     the row max / row sum need one cross-half exchange only.
 //   * O^T += V^T P^T on the same MFMA: P^T is taken straight from the S^T
-//     accumulator registers (converted to bf16), V^T comes from a transposed
-//     copy of the V tile in LDS; each A fragment is two 8-byte LDS reads.
-//   * K tiles go global -> LDS by direct loads, double-buffered; the next
-//     tile's V rows are fetched into registers while the current tile is
-//     multiplied, then transposed (4 keys x 8 dh per thread) and written to
-//     LDS as 8-byte rows of V^T (two barriers per tile).
+//     accumulator registers (converted to bf16); the V^T A fragments are
+//     read from the V tile, kept in LDS in its own [key][dh] layout, by
+//     gfx950's transposing LDS read (ds_read_b64_tr_b16, two per fragment).
+//   * K and V tiles go global -> LDS by direct loads, double-buffered, one
+//     barrier per tile.
 //   * Per tile: both halves of S first, each MFMA followed by one LDS read
 //     for the next phase; one max per tile (lazy rescale); the second
 //     half's exponentials between the first half's P V MFMAs.  Only the
@@ -39,7 +38,6 @@ constexpr int kAttnThreads = 256;
 constexpr int kAttnQ = 128;            // queries per workgroup
 constexpr int kAttnKeys = 64;          // keys per tile
 constexpr int kDh = 128;
-constexpr int kVtStride = kAttnKeys + 4;
 
 // Lazy rescaling: the running max only moves when a tile's max exceeds it by
 // more than 2^kLazy in probability (log2 units), so most tiles skip the
@@ -47,14 +45,25 @@ constexpr int kVtStride = kAttnKeys + 4;
 constexpr float kLazy = 8.0f;
 constexpr int kGroups = 2;                      // key-split groups of 4 waves
 constexpr int kAttnThreads2 = kAttnThreads * kGroups;
-constexpr int kKsBytes = kAttnKeys * kDh * 2;   // one K tile, 256-byte rows, XOR-swizzled chunks
-constexpr int kVtElems = kDh * kVtStride;
+constexpr int kKsBytes = kAttnKeys * kDh * 2;   // one K or V tile, 256-byte rows, XOR-swizzled chunks
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // 16-byte chunk c (0..15) of K row r lives at chunk c ^ (r & 15): the 16 rows
 // of one ds_read_b128 phase then cover all 64 banks.
 __device__ __forceinline__ int ks_chunk(int row, int c) { return row * 16 + (c ^ (row & 15)); }
+
+// 16-byte chunk c of V row r lives at chunk c ^ ((r & 3) << 2).  A
+// transposing read (below) has the 32 lanes of each half-wave fetch 8 bytes
+// from 4 consecutive rows x 8 chunk halves; the XOR spreads those 4 rows over
+// the 4 quarters of the 256-byte bank window, so the 32 reads are disjoint.
+__device__ __forceinline__ int vs_chunk(int row, int c) { return row * 16 + (c ^ ((row & 3) << 2)); }
+
+// ds_read_b64_tr_b16, as measured on gfx950: within each group of 16 lanes,
+// result lane 4*a + e receives in its slot j (j-th 16-bit element of the
+// 64 bits) element e of the 4 elements read by lane 4*j + a of the group.
+typedef short attn_v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) attn_v4i16_t lds_v4i16_t;
 
 // Key-split of the last round: with P workgroups resident (one per CU) and T
 // active (query tile, head, episode) units -- only tiles holding refreshed
@@ -129,18 +138,19 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   const int q0 = qt * kAttnQ;
   const int kt0 = c * ntiles / C, kt1 = (c + 1) * ntiles / C;   // this piece's key tiles
 
-  // per group: K tiles double-buffered (filled by direct-to-LDS loads), V^T
-  // single-buffered (written from registers).  Separate arrays, so the
-  // compiler can see that the K prefetch never writes the V^T it reads.
-  __shared__ uint4 ks_all[kGroups][2][kKsBytes / 16];
-  __shared__ __attribute__((aligned(16))) bf16_t vt_all[kGroups][kVtElems];
+  // per group and stage: a K tile, then a V tile, filled by direct-to-LDS
+  // loads.  One LDS object only: with a second one the compiler cannot tell
+  // the direct-to-LDS writes in flight from the reads and waits for the
+  // prefetch before every tile.
+  constexpr int kTileChunks = kKsBytes / 16, kStageChunks = 2 * kTileChunks;
+  __shared__ uint4 kv_all[kGroups][2][kStageChunks];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int grp = wid >> 2, gw = wid & 3, gtid = tid & (kAttnThreads - 1);
+  const int grp = wid >> 2, gw = wid & 3;
   const int half = lane >> 5, col = lane & 31;
   const int N = a.N, d = a.d;
-  uint4* Ks0 = &ks_all[grp][0][0];
-  bf16_t* Vt = vt_all[grp];
+  uint4* Ks0 = &kv_all[grp][0][0];
+  uint4* Vs0 = Ks0 + kTileChunks;
   const bf16_t* Kc = static_cast<const bf16_t*>(a.k_cache) + static_cast<size_t>(b) * N * d + h * kDh;
   const bf16_t* Vc = static_cast<const bf16_t*>(a.v_cache) + static_cast<size_t>(b) * N * d + h * kDh;
 
@@ -166,38 +176,36 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
       const int row = c >> 4, ch = (c & 15) ^ (row & 15);
       const int key = min(t * kAttnKeys + row, N - 1);   // rows past N: a valid row, masked later
       const bf16_t* src = Kc + static_cast<size_t>(key) * d + ch * 8;
-      uint4* dst = Ks0 + stage * (kKsBytes / 16) + (i * 4 + gw) * 64;
+      uint4* dst = Ks0 + stage * kStageChunks + (i * 4 + gw) * 64;
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
     }
   };
-  const int vkb = gtid & 15, vdb = gtid >> 4;
-  uint4 rv[4];
-  auto load_v = [&](int it) {
+  // V tile rows in the same order, swizzled by vs_chunk
+  auto issue_v = [&](int it, int stage) {
     const int t = kt0 + it * kGroups + grp;
+    if (t >= kt1) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kv = t * kAttnKeys + vkb * 4 + i;
-      rv[i] = (t < kt1 && kv < N) ? *reinterpret_cast<const uint4*>(Vc + static_cast<size_t>(kv) * d + vdb * 8)
-                                     : make_uint4(0, 0, 0, 0);
+      const int c = (i * 4 + gw) * 64 + lane;
+      const int row = c >> 4, ch = (c & 15) ^ ((row & 3) << 2);
+      const int key = min(t * kAttnKeys + row, N - 1);   // rows past N: a valid row, its probability is 0
+      const bf16_t* src = Vc + static_cast<size_t>(key) * d + ch * 8;
+      uint4* dst = Vs0 + stage * kStageChunks + (i * 4 + gw) * 64;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
     }
   };
-  auto store_v = [&]() {
-    // Vt[dh][key]: for each of the 8 dh of this block, the 4 keys' values
-    const uint32_t w0[4] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w};
-    const uint32_t w1[4] = {rv[1].x, rv[1].y, rv[1].z, rv[1].w};
-    const uint32_t w2[4] = {rv[2].x, rv[2].y, rv[2].z, rv[2].w};
-    const uint32_t w3[4] = {rv[3].x, rv[3].y, rv[3].z, rv[3].w};
+  // Transposing reads of V: lane (16*G + 4*j + a) reads 4 dh of one key row;
+  // G = 2*h2 + g1 picks the half-wave h2 (the MFMA's k-half) and the 16-dh
+  // half g1 of a 32-dh block, j the key within a group of 4, a the 4-dh
+  // quarter.  Byte offset within a tile: row*256 + swizzled chunk*16 +
+  // (a & 1)*8, with row = (keys before the group) + 4*h2 + j and chunk
+  // 4*db + 2*g1 + (a >> 1); the XOR of vs_chunk only touches the chunk's
+  // bits 2-3, so the chunk is 4*(db ^ j) + 2*g1 + (a >> 1).
+  const int tr_g = lane >> 4, tr_j = (lane >> 2) & 3, tr_a = lane & 3;
+  const int tr_base = ((tr_g >> 1) * 4 + tr_j) * 256 + (tr_g & 1) * 32 + tr_a * 8;
+  int tr_db[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint2 ev, od;
-      ev.x = __byte_perm(w0[j], w1[j], 0x5410);   // dh 2j:   keys 0, 1
-      ev.y = __byte_perm(w2[j], w3[j], 0x5410);   //          keys 2, 3
-      od.x = __byte_perm(w0[j], w1[j], 0x7632);   // dh 2j+1: keys 0, 1
-      od.y = __byte_perm(w2[j], w3[j], 0x7632);
-      *reinterpret_cast<uint2*>(&Vt[(vdb * 8 + 2 * j) * kVtStride + vkb * 4]) = ev;
-      *reinterpret_cast<uint2*>(&Vt[(vdb * 8 + 2 * j + 1) * kVtStride + vkb * 4]) = od;
-    }
-  };
+  for (int db = 0; db < 4; ++db) tr_db[db] = tr_base + ((db ^ tr_j) << 6);
 
   // running max in raw logit units (the softmax scale is folded into exp2)
   float m_run = -INFINITY, l_run = 0.f;
@@ -214,22 +222,26 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   // the first half run on the matrix pipe.  `ragged` is true only for the
   // last tile when N is not a multiple of 64 (a separate instantiation, so
   // full tiles carry no per-element key test).
-  auto tile_step = [&](int t, int stage, auto ragged) {
-    const uint4* Ks = Ks0 + stage * (kKsBytes / 16);
+  auto tile_step = [&](int t, int stage, auto ragged, int it) {
+    const uint4* Ks = Ks0 + stage * kStageChunks;
     auto read_k = [&](int kb, bf16x8_t (&kf)[8]) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) kf[s] = __builtin_bit_cast(bf16x8_t, Ks[ks_chunk(kb * 32 + col, 2 * s + half)]);
     };
-    // V^T fragment (tt, db) of half kb: dh row db*32 + col, keys kb*32 + 16*tt + half*4 + {0..3, 8..11}
+    // V^T fragment (tt, db) of half kb: dh row db*32 + col, slot j <-> key
+    // kb*32 + 16*tt + (j/4)*8 + half*4 + j%4, the key order of the P^T
+    // fragment; slots 0-3 and 4-7 are one transposing read each
+    const char* Vb = reinterpret_cast<const char*>(Vs0 + stage * kStageChunks);
     auto read_v = [&](int kb, bf16x8_t (&vf)[8]) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const bf16_t* vr = &Vt[(db * 32 + col) * kVtStride + kb * 32 + 16 * tt + half * 4];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-          vf[tt * 4 + db] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          const char* p0 = Vb + tr_db[db] + (kb * 32 + 16 * tt) * 256;
+          const attn_v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p0));
+          const attn_v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p0 + 8 * 256));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          vf[tt * 4 + db] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
         }
     };
     auto qk = [&](const bf16x8_t (&kf)[8]) {
@@ -314,6 +326,11 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
     bf16x8_t p0[2], p1[2];
     probs(s0, p0);
     read_v(1, v1);
+    // The next tile's loads go out here, after this tile's last LDS read:
+    // the compiler cannot match the transposing reads against direct-to-LDS
+    // writes in flight and would wait for every such write before them.
+    issue_k(it + 1, (it + 1) & 1);
+    issue_v(it + 1, (it + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
     pv(v0, p0);
     probs(s1, p1);
@@ -329,31 +346,38 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   };
 
   issue_k(0, 0);
-  load_v(0);
-  for (int it = 0; it < iters; ++it) {
-    // K tile `it` (direct to LDS) and the V rows in registers have landed ...
+  issue_v(0, 0);
+  // The ragged tile, when there is one in this piece, is tile ntiles - 1 and
+  // falls in the last iteration; that iteration runs after the loop, both
+  // groups in the masking instantiation, so that each path through the loop
+  // body issues its prefetch after its own last LDS read (two instantiations
+  // in one body would be laid out one after the other under an exec mask,
+  // and the second would wait for the first's prefetch).
+  const int full_iters = (kt1 == ntiles && ntiles * kAttnKeys > N) ? iters - 1 : iters;
+  for (int it = 0; it < full_iters; ++it) {
+    // this thread's K and V loads of tile `it` have landed in LDS ...
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));   // vmcnt(0)
-    // ... and every wave is done with the previous tile's LDS
+    // ... and everybody's, and every wave is done with the stage that the
+    // prefetch of tile it + 1 (issued inside the step) overwrites
     __builtin_amdgcn_s_barrier();
-    store_v();
-    issue_k(it + 1, (it + 1) & 1);
-    load_v(it + 1);
-    lds_barrier();   // V^T visible; the prefetches stay in flight
     const int t = kt0 + it * kGroups + grp;
-    if (t < kt1) {
-      if ((t + 1) * kAttnKeys > N)
-        tile_step(t, it & 1, std::true_type{});
-      else
-        tile_step(t, it & 1, std::false_type{});
-    }
+    if (t < kt1) tile_step(t, it & 1, std::false_type{}, it);
+  }
+  if (full_iters < iters) {
+    const int it = full_iters;
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));   // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    const int t = kt0 + it * kGroups + grp;
+    if (t < kt1) tile_step(t, it & 1, std::true_type{}, it);
   }
 
   // merge the two key groups: group 1 hands (o, m, l) to group 0 through LDS
-  // (o in the K buffers, 64 floats per lane; m and l in the V^T buffers)
+  // (o in the first 64 KiB of the tile buffers, 64 floats per lane; m and l
+  // after it)
   __syncthreads();
-  float* xo = reinterpret_cast<float*>(&ks_all[0][0][0]);
-  float* xml = reinterpret_cast<float*>(&vt_all[0][0]);
-  static_assert(4 * 64 * 64 * 4 <= sizeof(ks_all), "exchange of o fits the K buffers");
+  float* xo = reinterpret_cast<float*>(&kv_all[0][0][0]);
+  float* xml = xo + 4 * 64 * 64;
+  static_assert(4 * 64 * 64 * 4 + 4 * 2 * 64 * 4 + 16 <= sizeof(kv_all), "exchange of o, m, l and the flag fits the tile buffers");
   if (grp == 1) {
     float* dst = xo + static_cast<size_t>(gw) * 64 * 64 + lane;
 #pragma unroll
