@@ -864,12 +864,9 @@ struct SkTile {
 };
 
 // Active tile t (grouped order: 8 row tiles per column sweep) -> its rows/columns.
-#ifndef WAMC_SK_GROUP_M
-#define WAMC_SK_GROUP_M 8
-#endif
 template <int BM, int BN>
 __device__ __forceinline__ SkTile sk_tile(const GemmArgs& g, int t, int tiles_m, int tiles_n) {
-  constexpr int GM = WAMC_SK_GROUP_M;
+  constexpr int GM = 8;
   const int group = t / (GM * tiles_n);
   const int first_m = group * GM;
   const int gsize = min(tiles_m - first_m, GM);
