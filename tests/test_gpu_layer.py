@@ -92,11 +92,29 @@ def test_refresh_layer_wide(m, spare):
     with k = 3840 covers those).  At 2808 rows the down projection's 264
     tiles of 140 k-tiles run as 792 pieces, more than one round of
     workgroups, from a grid sized for them."""
-    wl = W.preset("c2_layer")
+    _check_refresh_layer(W.preset("c2_layer"), m, spare, seed=m)
+
+
+@pytest.mark.parametrize("n", [33, 65, 130, 257, 1000, 4000, 4095])
+def test_refresh_layer_key_tiles(n):
+    """The attention's key-tile paths, on a d=256 layer (two heads of 128)
+    with up to 40 refreshed rows, so that its two (query tile, head) units
+    are cut into key ranges wherever N has enough tiles: a single ragged
+    tile (N < 64); a ragged last tile falling to either key group of the
+    last iteration (odd and even tile counts); pieces of several tiles whose
+    last piece ends in the ragged tile (N = 4000, 4095); and the fresh K/V
+    of the refreshed rows written before the attention reads them."""
+    wl = W.preset("t_bf16_small", views=1, rows=1, cols=n, k=min(40, n))
+    _check_refresh_layer(wl, wl.k, False, seed=n)
+
+
+def _check_refresh_layer(wl, m, spare, seed):
+    """One wamc_refresh_layer call (twice, reusing the workspace) on m random
+    rows of an N-token cache against the oracle's block."""
     r = W.make_rollout(wl, chunks=1)
     prec = O.Precision(wl.dtype)
     N, d = wl.n_tokens, wl.d_model
-    rng = np.random.default_rng(m)
+    rng = np.random.default_rng(seed)
     idx = np.sort(rng.choice(N, size=m, replace=False)).astype(np.int32)
     Kc = prec.store(rng.standard_normal((N, d)).astype(np.float32) * 0.5)
     Vc = prec.store(rng.standard_normal((N, d)).astype(np.float32) * 0.5)
