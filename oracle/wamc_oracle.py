@@ -11,8 +11,8 @@ What it computes, with the page each step follows (titles as printed):
 * "WAM-Cache: Staleness-Bounded KV Reuse for Efficient World Action Models"
   - §3 "Preliminaries": a DiT module is self-attention + MLP, each with a
     residual; Q/K/V are linear projections of the module input; every query
-    attends over all S_v keys and values.  (The text cross-attention of that
-    module is not part of this path.)
+    attends over all S_v keys and values; the module's text cross-attention
+    (keys and values projected from the instruction) is optional here.
   - §4.1 "Overview": per-token state = layerwise cached K/V, a reference
     embedding stored at the token's last refresh, an age counter of
     consecutive reuses and the action expert's attention mass from the
@@ -62,9 +62,11 @@ WAM-Cache §4.2-4.4 are lost in the text):
   H2, GELU output), the residual stream staying float32.
 
 Parity pins: every function below is checked by the CPU tests against closed
-forms, library routines, brute force or a scalar second formulation, except
-full multi-chunk rollouts with stale caches ("parity unpinned" beyond the
-invariants the tests check: they have no printed worked example).
+forms, library routines, brute force, hand-worked values or a scalar second
+formulation (surprise, combine and the reference update against hand-worked
+multi-chunk values), except full multi-chunk rollouts with stale caches
+("parity unpinned" beyond the invariants the tests check: they have no
+printed worked example).
 """
 from __future__ import annotations
 
@@ -263,7 +265,11 @@ def attention_mass(qa: np.ndarray, K: np.ndarray, n_heads: int, prec: Precision)
 
 
 def surprise(z: np.ndarray, zref: np.ndarray, prec: Precision) -> np.ndarray:
-    """U_i = sum_c (z[i,c] - zref[i,c])^2."""
+    """U_i = sum_c (z[i,c] - zref[i,c])^2: the squared Euclidean distance
+    over the d channels between token i's current input embedding and its
+    reference embedding (WAM-Cache §4.2 "Latent Surprise": how far the
+    embedding moved since the token was last refreshed; §4.1 for the
+    reference)."""
     diff = prec.load(z) - prec.load(zref)
     return (diff * diff).sum(axis=1)
 
@@ -377,6 +383,15 @@ def ages_after(age: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return new
 
 
+def update_reference(zref: np.ndarray, z: np.ndarray, idx: np.ndarray) -> None:
+    """The reference embedding of a token is the input embedding it had at
+    its most recent refresh (WAM-Cache §4.1): refreshed rows take this
+    chunk's z, every other row keeps the one stored when it was last
+    refreshed (so a token that moves while being reused accumulates
+    surprise against that older embedding)."""
+    zref[idx] = z[idx]
+
+
 # --------------------------------------------------------------------------
 # one refresh chunk (WAM-Cache §4.1-4.4)
 # --------------------------------------------------------------------------
@@ -415,7 +430,7 @@ def refresh_chunk(state: State, z: np.ndarray, qa: Optional[np.ndarray], weights
     state.age = age
     zl = prec.load(z)
     X = zl[idx].copy()
-    state.zref[idx] = zl[idx]
+    update_reference(state.zref, zl, idx)
     outs = []
     for l in range(len(weights)):
         X = block(X, idx, weights[l], state.K[l], state.V[l], n_heads, eps, prec,
