@@ -70,7 +70,10 @@ enum wamc_dtype { WAMC_FP32 = 0, WAMC_BF16 = 1 };
 /* Model and method sizes.  Supported: d_model == n_heads * head_dim;
  * d_model and d_ffn multiples of 8; fp32: head_dim <= 128; bf16: head_dim ==
  * 128.  n_tokens (N) >= 1, n_action (A) >= 1 (used by wamc_score only),
- * age_bound (G) >= 0. */
+ * age_bound (G) >= 0.  Range: batch * n_tokens <= 2^30, d_model <= 2^20,
+ * d_ffn <= 2^22 and batch * n_tokens * d_model <= 2^40 (WAMC_ERR_ARG
+ * beyond; the GEMM tiles address up to 256 rows of d_ffn elements with
+ * 32-bit offsets from a 64-bit tile base). */
 typedef struct {
   int32_t batch;        /* B episodes */
   int32_t n_layers;     /* L */

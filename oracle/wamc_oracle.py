@@ -90,11 +90,14 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     NaN stays NaN (quiet bit forced so truncation cannot make it inf).
     """
     x32 = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x32.view(np.uint32).astype(np.uint64)
+    bits = x32.view(np.uint32)
+    # no wrap-around in 32 bits: the largest non-NaN pattern is 0xFF800000
+    r = bits + (np.uint32(0x7FFF) + ((bits >> 16) & np.uint32(1)))
+    r &= np.uint32(0xFFFF0000)
     nan = np.isnan(x32)
-    r = ((bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
-    r = np.where(nan, (bits.astype(np.uint32) | 0x00400000) & 0xFFFF0000, r)
-    return r.astype(np.uint32).view(np.float32).reshape(x32.shape)
+    if nan.any():
+        r = np.where(nan, (bits | np.uint32(0x00400000)) & np.uint32(0xFFFF0000), r)
+    return r.view(np.float32).reshape(x32.shape)
 
 
 class Precision:
@@ -115,7 +118,7 @@ class Precision:
     def store(self, x: np.ndarray) -> np.ndarray:
         """Value written to a storage point (cache, Q, H1, O, H2, GELU out)."""
         if self.bf16:
-            return round_bf16(x).astype(self.acc)
+            return round_bf16(x)
         return np.asarray(x, dtype=self.acc)
 
 
@@ -138,8 +141,10 @@ def gelu(x: np.ndarray) -> np.ndarray:
 
 def softmax_rows(S: np.ndarray) -> np.ndarray:
     """Row softmax with the row maximum subtracted first."""
-    E = np.exp(S - S.max(axis=1, keepdims=True))
-    return E / E.sum(axis=1, keepdims=True)
+    E = S - S.max(axis=1, keepdims=True)
+    np.exp(E, out=E)
+    E /= E.sum(axis=1, keepdims=True)
+    return E
 
 
 def attention(Q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, n_heads: int) -> np.ndarray:

@@ -173,7 +173,7 @@ int check_dims(const char* fn, const wamc_dims* d) {
   if (!std::isfinite(d->w_attn) || !std::isfinite(d->w_surprise))
     return fail(WAMC_ERR_ARG, "%s: score weights must be finite", fn);
   const long long rows = static_cast<long long>(d->batch) * d->n_tokens;
-  if (rows > (1ll << 30) || static_cast<long long>(d->d_ffn) > (1 << 24) ||
+  if (rows > (1ll << 30) || static_cast<long long>(d->d_ffn) > (1 << 22) ||
       static_cast<long long>(d->d_model) > (1 << 20) || rows * d->d_model > (1ll << 40))
     return fail(WAMC_ERR_ARG, "%s: sizes exceed the supported range", fn);
   if (d->d_model % 8 || d->d_ffn % 8)

@@ -579,9 +579,11 @@ void gemm_bf16_dtl_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   const int half = lane >> 5, col = lane & 31;
-  const bf16_t* A = static_cast<const bf16_t*>(g.a);
-  const bf16_t* W = static_cast<const bf16_t*>(g.w);
   const int K = g.K;
+  // 64-bit tile bases; the per-thread offsets inside a tile stay 32-bit
+  // (at most BM rows of K <= 2^22 elements)
+  const bf16_t* A = static_cast<const bf16_t*>(g.a) + static_cast<size_t>(m0) * K;
+  const bf16_t* W = static_cast<const bf16_t*>(g.w) + static_cast<size_t>(n0) * K;
 
   // load i of this thread fills LDS chunk c = (il*4 + wid)*64 + lane of its
   // operand (il = i for A, i - LOADS_A for W); it fetches the element chunk
@@ -593,8 +595,8 @@ void gemm_bf16_dtl_kernel(GemmArgs g) {
     const int c = (il * 4 + wid) * 64 + lane;
     const int row = c / CPR;
     const int kc = swz_kc<CPR>(row, c % CPR);   // the XOR key is its own inverse
-    if (i < LOADS_A) goff[i] = min(m0 + row, g.M - 1) * K + kc * 8;
-    else goff[i] = min(n0 + row, g.Nout - 1) * K + kc * 8;
+    if (i < LOADS_A) goff[i] = (min(m0 + row, g.M - 1) - m0) * K + kc * 8;
+    else goff[i] = (min(n0 + row, g.Nout - 1) - n0) * K + kc * 8;
   }
   auto issue = [&](int kt, int stage) {
 #pragma unroll
@@ -697,9 +699,11 @@ __global__ __launch_bounds__(kKs2Threads, 1) void gemm_bf16_dtl_ks2_kernel(GemmA
   const int grp = wid >> 2, gw = wid & 3;
   const int wm = gw >> 1, wn = gw & 1;
   const int half = lane >> 5, col = lane & 31;
-  const bf16_t* A = static_cast<const bf16_t*>(g.a);
-  const bf16_t* W = static_cast<const bf16_t*>(g.w);
   const int K = g.K;
+  // 64-bit tile bases; the per-thread offsets inside a tile stay 32-bit
+  // (at most BM rows of K <= 2^22 elements)
+  const bf16_t* A = static_cast<const bf16_t*>(g.a) + static_cast<size_t>(m0) * K;
+  const bf16_t* W = static_cast<const bf16_t*>(g.w) + static_cast<size_t>(n0) * K;
 
   int goff[LOADS];
 #pragma unroll
@@ -708,8 +712,8 @@ __global__ __launch_bounds__(kKs2Threads, 1) void gemm_bf16_dtl_ks2_kernel(GemmA
     const int c = (il * 4 + gw) * 64 + lane;
     const int row = c / CPR;
     const int kc = swz_kc<CPR>(row, c % CPR);
-    if (i < LOADS_A) goff[i] = min(m0 + row, g.M - 1) * K + kc * 8;
-    else goff[i] = min(n0 + row, g.Nout - 1) * K + kc * 8;
+    if (i < LOADS_A) goff[i] = (min(m0 + row, g.M - 1) - m0) * K + kc * 8;
+    else goff[i] = (min(n0 + row, g.Nout - 1) - n0) * K + kc * 8;
   }
   const int nk = K / BK;
   const int iters = (nk + 1) / 2;
@@ -979,13 +983,17 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
       const int c = (il * NW + wid) * 64 + lane;
       const int row = c / CPR;
       const int kc = swz_kc<CPR>(row, c % CPR);
-      if (i < LOADS_A) goff[i] = min(tl.m0 + row, g.M - 1) * K + kc * 8 + kk0 * BK;
-      else goff[i] = min(tl.n0 + row, g.Nout - 1) * K + kc * 8 + kk0 * BK;
+      if (i < LOADS_A) goff[i] = (min(tl.m0 + row, g.M - 1) - tl.m0) * K + kc * 8 + kk0 * BK;
+      else goff[i] = (min(tl.n0 + row, g.Nout - 1) - tl.n0) * K + kc * 8 + kk0 * BK;
     }
+    // 64-bit tile bases; the per-thread offsets inside a tile stay 32-bit
+    // (at most BM rows of K <= 2^22 elements)
+    const bf16_t* At = A + static_cast<size_t>(tl.m0) * K;
+    const bf16_t* Wtt = Wt + static_cast<size_t>(tl.n0) * K;
     auto issue = [&](int kt, int stage) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const bf16_t* src = (i < LOADS_A ? A : Wt) + goff[i] + kt * BK;
+        const bf16_t* src = (i < LOADS_A ? At : Wtt) + goff[i] + kt * BK;
         const int il = i < LOADS_A ? i : i - LOADS_A;
         uint4* dst = &lds[stage][(i < LOADS_A ? 0 : CHUNKS_A) + (il * NW + wid) * 64];
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);

@@ -51,6 +51,8 @@ def test_workspace_bytes_grows_with_rows():
     ("dtype", 7, 1),
     ("ln_eps", 0.0, 1),
     ("head_dim", 64, 1),        # 2 * 64 != 256
+    ("d_ffn", (1 << 22) + 8, 1),   # beyond the GEMMs' 32-bit in-tile offsets
+    ("n_tokens", (1 << 30) + 1, 1),
 ])
 def test_bad_dims(field, value, code):
     d = _dims(**{field: value})
@@ -58,6 +60,12 @@ def test_bad_dims(field, value, code):
     st = wamc.lib().wamc_workspace_bytes(ctypes.byref(d), 1, ctypes.byref(out))
     assert st == code, wamc.lib().wamc_last_error()
     assert wamc.lib().wamc_last_error() != b""
+
+
+def test_largest_ffn_accepted():
+    d = _dims(d_ffn=1 << 22)
+    out = ctypes.c_size_t()
+    assert wamc.lib().wamc_workspace_bytes(ctypes.byref(d), 1, ctypes.byref(out)) == 0, wamc.lib().wamc_last_error()
 
 
 def test_unsupported_head_dim_bf16():
