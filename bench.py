@@ -1,21 +1,26 @@
 """Benchmark of the sparse KV-refresh prefill on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2_layer]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3_stack]
 
 A step is one refresh chunk: token scores (attention mass + surprise),
 selection with the age bound, gather, then every layer on the refreshed rows
-(WAM-Cache, paperpeel 2610.11401, §4).  The default workload is the single
-bf16 layer with d=1536, 12 heads, FFN 8960, N=4096 visual tokens and k=2458
-(60 % refresh), 64 action queries, age bound 3.  Inputs are seeded synthetic
-data already resident in HBM; the state after the dense chunk carries random
-ages U{0..3} so some tokens are forced.
+(WAM-Cache, paperpeel 2610.11401, §4).  The default workload is the 30-layer
+bf16 stack with d=1536, 12 heads, FFN 8960, N=4680 visual tokens (3 views of
+30x52) and k=2808 (60 % refresh), 64 action queries, age bound 3, on a
+16-chunk rollout of two moving blobs over a static scene.  Inputs are seeded
+synthetic data already resident in HBM.  The steps walk the rollout's refresh
+chunks in turn; the state after the dense chunk 0 is restored before each
+pass over the rollout.
 
-Printed as one JSON line: ms per refresh chunk (the metric), the library's own
-dense prefill of the same chunk, the speedup and its k_eff/N bound, refreshed
-tokens/s, the roofline of the dominant kernel (a second pass of the same K
-steps in which every launch carries HIP events stamped with that kernel's own
-start and end), and the CPU oracle timed on a bounded sample of the same
-workload.  Every timed loop starts once the GPU clocks are up (clock_warm).
+Printed as one JSON line: ms per refresh chunk (the metric: the mean, with
+the median and p10/p90 of the per-chunk times), the library's own dense
+prefill of the same chunks' latents, the speedup (mean ratio, paired median
+and its bootstrap 95 % interval) and its k_eff/N bound, refreshed tokens/s,
+the roofline of the dominant kernel (a further pass of the same K steps in
+which every launch carries HIP events stamped with that kernel's own start
+and end), and the CPU oracle timed on a bounded sample of the same workload.
+Every timed loop starts behind a clock warm-up (clock_warm, reported as
+clock_warm_chunks) and then W untimed warm-up steps.
 """
 from __future__ import annotations
 
@@ -41,9 +46,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warm-up steps before each timed loop; default: as many as fill %.2f s "
-                         "(at least 5), enough for the GPU clocks to ramp up after idle" % WARM_SECONDS)
-    ap.add_argument("--config", default="c2_layer")
+                    help="untimed warm-up steps before each timed loop (default 5), after a clock warm-up of "
+                         "at least %.2f s of the same work (the GPU clocks ramp up after idle)" % WARM_SECONDS)
+    ap.add_argument("--config", default="c3_stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--profile-steps", action="store_true",
@@ -251,6 +256,16 @@ def run_sweep(args):
         del eng
 
 
+def budget_rows(fraction: float, n_tokens: int) -> int:
+    """Token count of a refresh budget given as a fraction of the tokens:
+    ceil(fraction * n_tokens), taken on the decimal value (0.4 of 4680 is
+    1872, where binary floating point would give 1873).  The library takes
+    the counts; turning the pages' budget fractions into counts is the
+    caller's part."""
+    from fractions import Fraction
+    return min(n_tokens, -(-Fraction(repr(float(fraction))) * n_tokens // 1))
+
+
 def run_union(args):
     """The union refresh rule (top ceil(b_a N) by attention mass, top
     ceil(b_s N) by surprise, forced tokens; WAM-Cache §1, §4.3, §4.4) on the
@@ -272,7 +287,7 @@ def run_union(args):
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * T)]
     eng = wamc.Engine(wamc.dims_for(base), weights, N, dev)
     for b_a, b_s in ((0.4, 0.1), (0.6, 0.1)):
-        na, ns = wamc.budget_rows(b_a, N), wamc.budget_rows(b_s, N)
+        na, ns = budget_rows(b_a, N), budget_rows(b_s, N)
         clock_warm(lambda: eng.dense(zs[0]))
         keffs = []
         for t in range(1, T):
@@ -429,7 +444,8 @@ def run_capacity(args):
         k_fill = plateau_capacity(rows, curve, k, tol=0.02)
         res = {}
         for name, kk in (("k", k), ("fill", k_fill)):
-            eng = wamc.Engine(wamc.dims_for(wl), weights, kk, dev)
+            # the smallest capacity the library accepts: N - k tokens may be forced
+            eng = wamc.Engine(wamc.dims_for(wl), weights, max(kk, wl.n_tokens - kk), dev)
             eng.dense(z0)
 
             def chunk_from_zero_ages():
@@ -518,6 +534,14 @@ def run_plateau(args):
                       "ms_per_layer": curves, "kernel_rows": kernel_rows, "kernel_us": per_kernel}), flush=True)
 
 
+def bootstrap_ci(values, stat=np.median, reps: int = 2000, seed: int = 0):
+    """95 % percentile-bootstrap interval of `stat` over the values."""
+    v = np.asarray(values, dtype=np.float64)
+    rng = np.random.default_rng(seed)
+    boots = [stat(v[rng.integers(0, len(v), len(v))]) for _ in range(reps)]
+    return [float(np.percentile(boots, 2.5)), float(np.percentile(boots, 97.5))]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -544,7 +568,10 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     adt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    r = W.make_rollout(wl, chunks=2)
+    # the rollout: a dense chunk 0, then refresh chunks 1..T-1, every chunk's
+    # latents and action queries resident in HBM before anything is timed
+    T = max(2, wl.chunks)
+    r = W.make_rollout(wl, chunks=T)
     dims = wamc.dims_for(wl)
     weights = wamc.Engine.upload_weights(r.weights, adt, dev)
     rows_cap = wl.k if wl.k >= (wl.n_tokens + 1) // 2 else wl.n_tokens
@@ -553,49 +580,79 @@ def main():
         # the instruction's keys/values, once per episode (outside the timed steps)
         eng.text_kv(torch.from_numpy(np.stack(r.text)).to(dev, adt).contiguous())
 
-    def bz(t):
-        return torch.from_numpy(np.stack([r.z[e][t] for e in range(wl.batch)])).to(dev, adt).contiguous()
-
-    z0, z1 = bz(0), bz(1)
-    qa = torch.from_numpy(np.stack([r.qa[e][1] for e in range(wl.batch)], axis=1)).to(dev, adt).contiguous()
+    zs = [torch.from_numpy(np.stack([r.z[e][t] for e in range(wl.batch)])).to(dev, adt).contiguous()
+          for t in range(T)]
+    qs = [None] + [torch.from_numpy(np.stack([r.qa[e][t] for e in range(wl.batch)], axis=1)).to(dev, adt)
+                   .contiguous() for t in range(1, T)]
+    ages0 = torch.from_numpy(np.stack(r.ages0)).to(dev)
     stream = torch.cuda.current_stream()
 
     if not args.profile_steps:
         # profiled runs skip the dense chunk so every traced launch is a refresh launch
-        eng.dense(z0)
-    eng.age.copy_(torch.from_numpy(np.stack(r.ages0)).to(dev))
+        eng.dense(zs[0])
+    eng.age.copy_(ages0)
     torch.cuda.synchronize()
+    start = eng.snapshot()       # the state after chunk 0; every pass over the rollout starts here
 
-    def refresh_step():
-        eng.chunk(z1, qa, wl.k, stream=stream)
+    def chunk_of(i):
+        return 1 + i % (T - 1)
 
-    def dense_step():
-        eng.dense(z1, stream=stream)
+    def before_step(i):
+        # a new pass over the rollout restores the state after chunk 0
+        # (outside the chunk's own events)
+        if i > 0 and chunk_of(i) == 1:
+            eng.restore(start)
 
-    def warm(fn, warmup):
-        if warmup is None:
-            return clock_warm(fn, 5)
-        for _ in range(warmup):
-            fn()
+    def refresh_step(i):
+        t = chunk_of(i)
+        eng.chunk(zs[t], qs[t], wl.k, stream=stream)
+
+    def dense_step(i):
+        eng.dense(zs[chunk_of(i)], stream=stream)
+
+    def run(step, n, events=None, on_step=None):
+        for i in range(n):
+            before_step(i)
+            if events is not None:
+                events[i][0].record(stream)
+            step(i)
+            if events is not None:
+                events[i][1].record(stream)
+            if on_step is not None:
+                on_step(i)
+
+    def warm(step, warmup):
+        """Clock warm-up (at least 0.15 s of this work: the clocks ramp for
+        ~40 ms after idle), then the requested warm-up steps; the state is
+        restored after it."""
+        calls = [0]
+
+        def one():
+            before_step(calls[0])
+            step(calls[0])
+            calls[0] += 1
+        n_clock = clock_warm(one, 1)
+        run(step, warmup)
         torch.cuda.synchronize()
-        return warmup
+        eng.restore(start)
+        return n_clock
 
-    def timed(fn, steps, warmup):
-        w = warm(fn, warmup)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def timed(step, steps, warmup, on_step=None):
+        n_clock = warm(step, warmup)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        a.record(stream)
-        for _ in range(steps):
-            fn()
-        b.record(stream)
+        run(step, steps, ev, on_step)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return a.elapsed_time(b) / steps, 1e3 * wall / steps, w
+        per = np.array([a.elapsed_time(b) for a, b in ev])
+        return per, 1e3 * wall / steps, n_clock
 
+    warmup = 5 if args.warmup is None else args.warmup
     if args.profile_steps:
         if args.profile_events:
             wamc.timing_enable(True)
-        ms, _, w = timed(refresh_step, args.steps, args.warmup)
+        per, _, n_clock = timed(refresh_step, args.steps, warmup)
         if args.profile_events:
             kt = wamc.timing_read()
             wamc.timing_enable(False)
@@ -606,22 +663,24 @@ def main():
             for _ in range(3):
                 dst.copy_(src)
             torch.cuda.synchronize()
-        print(json.dumps({"profile_steps": args.steps, "warmup": w, "ms_per_step": ms}))
+        print(json.dumps({"profile_steps": args.steps, "warmup": warmup, "clock_warm_chunks": n_clock,
+                          "ms_per_step": float(per.mean())}))
         return
 
-    ms_refresh, wall_refresh, warm_refresh = timed(refresh_step, args.steps, args.warmup)
-    k_eff = eng.k_eff.cpu().numpy().astype(np.int64)
-    k_total = int(k_eff.sum())
-    ms_dense, _, _ = timed(dense_step, args.steps, args.warmup)
-    # restore a refresh-ready state (the dense steps reset every age to 0)
-    eng.dense(z0)
-    eng.age.copy_(torch.from_numpy(np.stack(r.ages0)).to(dev))
-    warm(refresh_step, args.warmup)
+    # refresh chunks, each timed by its own event pair; k_eff of every step kept
+    keff_log = torch.zeros((args.steps, wl.batch), dtype=torch.int32, device=dev)
+    per_refresh, wall_refresh, clock_refresh = timed(refresh_step, args.steps, warmup,
+                                                     on_step=lambda i: keff_log[i].copy_(eng.k_eff))
+    keff_steps = keff_log.cpu().numpy().astype(np.int64)
+    k_total = float(keff_steps.sum(axis=1).mean())        # refreshed rows per chunk, all episodes
+    # the library's dense prefill of the same chunks' latents, step for step
+    per_dense, _, _ = timed(dense_step, args.steps, warmup)
+    eng.restore(start)
 
-    # per-kernel pass: HIP events around every launch, same K steps
+    # per-kernel pass: HIP events carried by every launch, same K steps
+    warm(refresh_step, warmup)
     wamc.timing_enable(True)
-    for _ in range(args.steps):
-        refresh_step()
+    run(refresh_step, args.steps)
     torch.cuda.synchronize()
     kt = wamc.timing_read()
     wamc.timing_enable(False)
@@ -657,14 +716,18 @@ def main():
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_seconds)
 
-    bound = wl.n_tokens * wl.batch / max(k_total, 1)
+    ms_refresh = float(per_refresh.mean())
+    ratio = per_dense / per_refresh                      # paired: the same chunk's latents
+    bound = wl.n_tokens * wl.batch / max(k_total, 1.0)
+    pct = lambda a, q: float(np.percentile(a, q))
     line = {
         "metric": "refresh-prefill ms/chunk & speedup vs dense at 60% refresh; MFMA/HBM % peak",
         "value": ms_refresh,
         "unit": "ms/chunk",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": warm_refresh,
+        "warmup": warmup,
+        "clock_warm_chunks": clock_refresh,
         "ms_per_step": ms_refresh,
         "higher_is_better": False,
         "scaling": "weak",
@@ -672,18 +735,29 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "n_layers": wl.n_layers, "d_model": wl.d_model, "n_heads": wl.n_heads,
-                   "d_ffn": wl.d_ffn, "n_tokens": wl.n_tokens, "k": wl.k, "k_eff": k_eff.tolist(),
+                   "d_ffn": wl.d_ffn, "n_tokens": wl.n_tokens, "k": wl.k, "k_eff_mean": k_total / wl.batch,
                    "n_action": wl.n_action, "age_bound": wl.age_bound, "batch": wl.batch,
-                   "rows_cap": rows_cap, "parallelism": "single GPU"},
-        "dense_ms_per_chunk": ms_dense,
-        "speedup_vs_dense": ms_dense / ms_refresh,
+                   "rollout_chunks": T, "rows_cap": rows_cap, "parallelism": "single GPU"},
+        "ms_per_chunk_median": float(np.median(per_refresh)),
+        "ms_per_chunk_p10_p90": [pct(per_refresh, 10), pct(per_refresh, 90)],
+        "dense_ms_per_chunk": float(per_dense.mean()),
+        "dense_ms_median": float(np.median(per_dense)),
+        "dense_ms_p10_p90": [pct(per_dense, 10), pct(per_dense, 90)],
+        "speedup_vs_dense": float(per_dense.mean()) / ms_refresh,
+        "speedup_median_paired": float(np.median(ratio)),
+        "speedup_ci95_bootstrap": bootstrap_ci(ratio),
         "speedup_bound": bound,
-        "speedup_frac_of_bound": (ms_dense / ms_refresh) / bound,
+        "speedup_frac_of_bound": (float(per_dense.mean()) / ms_refresh) / bound,
         "refreshed_tokens_per_s": k_total / (ms_refresh / 1e3),
         "wall_ms_per_step": wall_refresh,
+        "timing": (f"each step is one refresh chunk of a {T}-chunk rollout (chunks 1..{T - 1} in turn; the state "
+                   "after the dense chunk 0 is restored before each pass, outside the chunk's events) timed by "
+                   "its own HIP event pair; dense steps run the library's dense prefill on the same chunks' "
+                   "latents, step for step, and the speedup CI resamples those pairs; before each timed loop "
+                   "the clocks are warmed by clock_warm_chunks chunks (>= 0.15 s), then `warmup` more"),
         "roofline": roof,
         "kernels": kernels,
-        "kernel_timing": "second pass of the same steps; every launch carries HIP events stamped with the "
+        "kernel_timing": "third pass of the same steps; every launch carries HIP events stamped with the "
                          "kernel's own start and end on the launch stream (hipExtLaunchKernel)",
         "cpu_baseline": cpu,
     }

@@ -202,7 +202,16 @@ int wamc_refresh_layer(const wamc_dims* dims, int32_t layer, const wamc_layer_w*
  * scoring/selection; ages are then updated from it (score_out untouched).
  * Outputs: idx_out [B,N] i32 and k_eff_out [B] i32 (required); score_out
  * (nullable) [B,N] f32; layer_out (nullable) [L,B,rows_cap,d] f32: every
- * layer's output rows in idx order.  rows_cap in [k, N] bounds k_eff. */
+ * layer's output rows in idx order.
+ * rows_cap (<= N) bounds k_eff.  When the library selects it must be at
+ * least max(k, N - k), and N when G = 0 (WAMC_ERR_ARG otherwise): a token
+ * forced at this chunk was not refreshed in the previous one, which
+ * refreshed at least k tokens, so with ages that came from this library's
+ * chunks at this k (or from a dense prefill) at most N - k tokens are forced
+ * and the refresh set always fits, keeping every age <= G.  Ages supplied
+ * from elsewhere can force more; the set is then cut to rows_cap by rank and
+ * the forced tokens left out keep aging past G (wamc_select reports the
+ * forced count).  With idx_override, rows_cap must hold the given set. */
 int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const void* z, void* zref,
                        const void* q_act, const float* mass_in, void* k_cache, void* v_cache,
                        int32_t* age, int32_t k, const int32_t* idx_override,

@@ -634,6 +634,16 @@ int wamc_prefill_chunk(const wamc_dims* dims, const wamc_layer_w* layers, const 
   if (k < 0 || k > dims->n_tokens) return fail(WAMC_ERR_ARG, "%s: k (%d) must be in [0, N=%d]", fn, k, dims->n_tokens);
   if ((st = check_rows_cap(fn, dims, rows_cap))) return st;
   if (rows_cap < k) return fail(WAMC_ERR_ARG, "%s: rows_cap (%d) < k (%d)", fn, rows_cap, k);
+  if (!idx_override) {
+    // With G >= 1 a forced token was not refreshed in the previous chunk,
+    // which refreshed at least k tokens, so at most N - k are forced (all N
+    // when G = 0).  A smaller capacity could leave forced tokens out.
+    const int forced_max = dims->age_bound == 0 ? dims->n_tokens : dims->n_tokens - k;
+    if (rows_cap < forced_max)
+      return fail(WAMC_ERR_ARG,
+                  "%s: rows_cap (%d) < %d, the most tokens the age bound can force (N - k, or N when G = 0): "
+                  "forced tokens would be left out", fn, rows_cap, forced_max);
+  }
   if (idx_override) {
     OPT_PTR(idx_override);
     if (!k_eff_override) return fail(WAMC_ERR_ARG, "%s: idx_override needs k_eff_override", fn);

@@ -201,13 +201,6 @@ def prefill_chunk(dims, layers: Sequence[dict], z, zref, q_act, k_cache, v_cache
                                     _ptr(layer_out), rows_cap, _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def budget_rows(fraction: float, n_tokens: int) -> int:
-    """Token count of a refresh budget given as a fraction of the tokens:
-    ceil(fraction * n_tokens), taken on the decimal value (0.1 of 30 is 3)."""
-    from fractions import Fraction
-    return min(n_tokens, -(-Fraction(repr(float(fraction))) * n_tokens // 1))
-
-
 def select_union(dims, mass, surprise, age, n_attn, n_surprise, idx, k_eff, n_forced=None, stream=None):
     _check(lib().wamc_select_union(ctypes.byref(dims), _ptr(mass), _ptr(surprise), _ptr(age), n_attn, n_surprise,
                                    _ptr(idx), _ptr(k_eff), _ptr(n_forced), _stream(stream)))

@@ -169,3 +169,23 @@ def test_text_cross_attention_validates():
     assert L.wamc_text_kv(ctypes.byref(d), arr, None, FAKE, ws, None) == 1
     d.n_text = -1
     assert L.wamc_workspace_bytes(ctypes.byref(d), 10, ctypes.byref(ctypes.c_size_t())) == 1
+
+
+def test_prefill_chunk_refuses_a_capacity_the_forced_tokens_may_overflow():
+    """With the library selecting, rows_cap must hold the N - k tokens the
+    age bound can force (N when G = 0), so no forced token is left out."""
+    L = wamc.lib()
+    d = _dims()
+    N = d.n_tokens
+    lw = wamc.LayerW(*([FAKE] * 9))
+    arr = (wamc.LayerW * d.n_layers)(*([lw] * d.n_layers))
+    ws = wamc.workspace_bytes(d, N)
+
+    def call(dims, k, rows_cap):
+        return L.wamc_prefill_chunk(ctypes.byref(dims), arr, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, k, None,
+                                    None, FAKE, FAKE, None, None, rows_cap, FAKE, ws, None)
+    k = N // 4
+    assert call(d, k, k) == 1 and b"force" in L.wamc_last_error()
+    assert call(d, k, N - k - 1) == 1
+    d0 = _dims(age_bound=0)
+    assert call(d0, N - 10, N - 1) == 1
