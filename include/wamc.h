@@ -263,6 +263,27 @@ int wamc_dense_prefill(const wamc_dims* dims, const wamc_layer_w* layers, const 
                        void* k_cache, void* v_cache, int32_t* age, float* layer_out, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* wamc_prefill_chunk for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same chunk, with the workspace taken from a static scratch
+ * array of WAMC_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends (its address is looked up once per device on
+ * the first call).  Returns WAMC_ERR_WORKSPACE, with nothing enqueued, when
+ * wamc_workspace_bytes(dims, rows_cap) exceeds that size (the 30-layer
+ * d=1536 chunk at rows_cap = 2808 needs about 250 MiB; the d=3072 four-episode
+ * chunk does not fit).  Calls no allocating routine.  Every call on one GPU
+ * shares that GPU's array and leaves its contents behind; the kernels clear
+ * what must start at zero, but calls that overlap on one GPU (other streams,
+ * other threads) race on it and must be serialised by the caller.  Other
+ * arguments, validation and errors as in wamc_prefill_chunk (whose name the
+ * argument messages carry). */
+#define WAMC_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int wamc_prefill_chunk_noalloc(const wamc_dims* dims, const wamc_layer_w* layers, const void* z, void* zref,
+                               const void* q_act, const float* mass_in, void* k_cache, void* v_cache,
+                               int32_t* age, int32_t k, const int32_t* idx_override,
+                               const int32_t* k_eff_override, int32_t* idx_out, int32_t* k_eff_out,
+                               float* score_out, float* layer_out, int32_t rows_cap, void* stream);
+
 /* Optional per-kernel timing, off by default.  While on, every kernel launch
  * carries a pair of HIP events (hipExtLaunchKernel) that the runtime stamps
  * with that kernel's own start and end on the launch stream; a step made of

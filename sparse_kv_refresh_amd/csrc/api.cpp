@@ -480,6 +480,14 @@ hipError_t run_refresh_rows(const wamc_dims* dims, const wamc_layer_w* layers, c
 
 }  // namespace
 
+namespace wamc {
+// The thread's error detail for entry points defined in other files.
+int api_fail(int code, const char* msg) {
+  g_last_error = msg;
+  return code;
+}
+}  // namespace wamc
+
 // ===========================================================================
 // exported API
 // ===========================================================================

@@ -62,6 +62,8 @@ _SIGNATURES = {
     "wamc_refresh_layer": ([_DP, _I, _LP, _P, _P, _P, _I, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "wamc_prefill_chunk": ([_DP, _LP, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P],
                            ctypes.c_int),
+    "wamc_prefill_chunk_noalloc": ([_DP, _LP, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _P],
+                                   ctypes.c_int),
     "wamc_select_union": ([_DP, _P, _P, _P, _I, _I, _P, _P, _P, _P], ctypes.c_int),
     "wamc_prefill_chunk_union": ([_DP, _LP, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _SZ, _P],
                                  ctypes.c_int),
@@ -199,6 +201,26 @@ def prefill_chunk(dims, layers: Sequence[dict], z, zref, q_act, k_cache, v_cache
                                     _ptr(k_cache), _ptr(v_cache), _ptr(age), k, _ptr(idx_override),
                                     _ptr(k_eff_override), _ptr(idx_out), _ptr(k_eff_out), _ptr(score_out),
                                     _ptr(layer_out), rows_cap, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def prefill_chunk_noalloc(dims, layers: Sequence[dict], z, zref, q_act, k_cache, v_cache, age, k, idx_out,
+                          k_eff_out, rows_cap, mass_in=None, idx_override=None, k_eff_override=None,
+                          score_out=None, layer_out=None, stream=None, _layer_array=None):
+    """prefill_chunk with the library's static scratch in place of a
+    workspace (for callers that cannot allocate device memory)."""
+    arr = _layer_array if _layer_array is not None else _layers(layers)
+    _check(lib().wamc_prefill_chunk_noalloc(ctypes.byref(dims), arr, _ptr(z), _ptr(zref), _ptr(q_act),
+                                            _ptr(mass_in), _ptr(k_cache), _ptr(v_cache), _ptr(age), k,
+                                            _ptr(idx_override), _ptr(k_eff_override), _ptr(idx_out),
+                                            _ptr(k_eff_out), _ptr(score_out), _ptr(layer_out), rows_cap,
+                                            _stream(stream)))
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the static scratch behind prefill_chunk_noalloc (from the header)."""
+    with open(HEADER) as f:
+        m = re.search(r"#define\s+WAMC_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", f.read())
+    return int(m.group(1)) << int(m.group(2))
 
 
 def select_union(dims, mass, surprise, age, n_attn, n_surprise, idx, k_eff, n_forced=None, stream=None):

@@ -171,6 +171,23 @@ def test_text_cross_attention_validates():
     assert L.wamc_workspace_bytes(ctypes.byref(d), 10, ctypes.byref(ctypes.c_size_t())) == 1
 
 
+def test_noalloc_refuses_chunks_beyond_its_scratch():
+    """The four-episode d=3072 chunk needs more workspace than the static
+    scratch holds: refused on the host, before any device call."""
+    L = wamc.lib()
+    d = wamc.dims_for(W.preset("c5_large"))
+    need = wamc.workspace_bytes(d, 4096)
+    assert need > wamc.noalloc_scratch_bytes() == 256 << 20
+    layers = (wamc.LayerW * d.n_layers)()
+    P = ctypes.c_void_p(FAKE)
+    st = L.wamc_prefill_chunk_noalloc(ctypes.byref(d), layers, P, P, P, None, P, P, P, 4096, None, None, P, P,
+                                      None, None, 4096, None)
+    assert st == 3
+    assert b"static scratch" in L.wamc_last_error()
+    # the 30-layer d=1536 chunk at the benchmark's row capacity fits
+    assert wamc.workspace_bytes(wamc.dims_for(W.preset("c3_stack")), 2808) <= wamc.noalloc_scratch_bytes()
+
+
 def test_prefill_chunk_refuses_a_capacity_the_forced_tokens_may_overflow():
     """With the library selecting, rows_cap must hold the N - k tokens the
     age bound can force (N when G = 0), so no forced token is left out."""
