@@ -84,6 +84,36 @@ def copy_factor(vals: dict, counter: str) -> float:
     return COPY_BYTES / (big * 1024.0)
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
+
+
+def mfma_summary(db: str, chunks: int, last: int, simds: int, xcds: int):
+    """Per kernel kind, from one `--pmc SQ_VALU_MFMA_BUSY_CYCLES
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE` run of `chunks` steps: the
+    mean of each counter per launch over the launches of the last `last`
+    steps, the MFMA busy share and the bf16 MFMA flops executed (MOPS x 512).
+    As stored per dispatch, the MFMA busy cycles are summed over all SIMDs
+    and GRBM_GUI_ACTIVE over the XCDs (divided by the XCD count it matches
+    the traced kernel duration at 2.4 GHz), so the busy share is
+    busy / (active / xcds * simds)."""
+    vals = {c: counters(db, c) for c in MFMA_COUNTERS}
+    out = {}
+    for kind, pat in KIND_PATTERNS.items():
+        per = {cname: [v for kn, vs in table.items() if re.search(pat, kn) for v in vs]
+               for cname, table in vals.items()}
+        n = min(len(v) for v in per.values())
+        if n == 0 or n % chunks:
+            continue
+        drop = n - (n // chunks) * last
+        mean = {c: sum(v[drop:n]) / (n - drop) for c, v in per.items()}
+        busy, mops, active = (mean[c] for c in MFMA_COUNTERS)
+        out[kind] = {"launches": n - drop, "mfma_busy_cycles": busy, "gpu_active_cycles_per_xcd": active / xcds,
+                     "mfma_util": busy / (active / xcds * simds) if active > 0 else None,
+                     "bf16_mfma_flops": mops * 512.0, "source_file": KERNEL_SOURCE[kind],
+                     "source_sha256_16": source_hash(KERNEL_SOURCE[kind])}
+    return {"counters": list(MFMA_COUNTERS), "simds": simds, "xcds": xcds, "kernels": out}
+
+
 def source_hash(fname: str) -> str:
     """Hash of a kernel's source file together with the shared headers it
     includes (every csrc/*.h, in name order), so that a change to either
@@ -113,7 +143,25 @@ def main(argv=None):
                    help="for kernels launched more than once per step: which launch of each step")
     b.add_argument("--per-step", type=int, default=1, help="launches of this kernel per step")
     b.add_argument("--out")
+    c = sub.add_parser("mfma")
+    c.add_argument("db")
+    c.add_argument("--config", default="c3_stack")
+    c.add_argument("--chunks", type=int, required=True, help="steps the run made (warm-up included)")
+    c.add_argument("--last", type=int, required=True, help="steps summarised: the last ones of the run")
+    c.add_argument("--simds", type=int, default=1024, help="SIMDs of the chip (256 CUs x 4)")
+    c.add_argument("--xcds", type=int, default=8, help="instances GRBM_GUI_ACTIVE is summed over")
+    c.add_argument("--out")
     args = ap.parse_args(argv)
+
+    if args.cmd == "mfma":
+        rec = mfma_summary(args.db, args.chunks, args.last, args.simds, args.xcds)
+        rec["config"] = args.config
+        text = json.dumps(rec, indent=1)
+        if args.out:
+            with open(args.out, "w") as fh:
+                fh.write(text + "\n")
+        print(text)
+        return
 
     if args.cmd == "stats":
         # the rocpd top_kernels view reports durations in microseconds
