@@ -66,7 +66,7 @@ def parse():
                     help="30-layer d=1536 stack at 120 / 480 / 1080 tokens with k = 0.584 N, eager and HIP-graph "
                          "replay (one JSON line each)")
     ap.add_argument("--capacity", action="store_true",
-                    help="capacity filling on the 30-layer stack: measured per-layer plateau, then chunks at k and "
+                    help="capacity filling on the 30-layer stack: chunk latency measured from k upward, then chunks at k and "
                          "at the plateau's upper end (one JSON line per k)")
     ap.add_argument("--union", action="store_true",
                     help="the pages' union rule on the 30-layer stack at budgets (b_a, b_s) = (0.4, 0.1) and "
@@ -390,83 +390,55 @@ def run_small_n(args):
 
 
 def run_capacity(args):
-    """Capacity filling (RealtimeWAM §3): the per-layer latency of the d=1536
-    layer over N=4680 tokens is measured every 32 rows with launches sized for
-    the rows; for each requested k the plateau's upper end k_fill (2 %
-    tolerance) is taken, and whole 30-layer chunks are timed at k and k_fill
-    (ages reset before each chunk, so exactly k resp. k_fill rows refresh)."""
+    """Capacity filling (RealtimeWAM §3: the upper end of the latency plateau
+    holding the required token count is the execution capacity; the spare
+    slots are filled with the next-ranked tokens).  The curve is measured on
+    whole 30-layer chunks: for each requested k the chunk is timed at
+    k, k + 32, ..., k + 512 rows (one engine sized for every token, ages reset
+    before each chunk so exactly that many rows refresh), and k_fill is the
+    largest count whose latency stays within 1 % of the latency at k.  Each
+    line reports the curve, k_fill and the chunk latency at k and at k_fill."""
     import torch
     from sparse_kv_refresh_amd import inputs as W
     from sparse_kv_refresh_amd import wamc
     from sparse_kv_refresh_amd.capacity import plateau_capacity
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # per-layer curve
-    wl1 = W.preset("c3_stack", n_layers=1)
-    r1 = W.make_rollout(wl1, chunks=1)
-    dims1 = wamc.dims_for(wl1)
-    w1 = wamc.Engine.upload_weights(r1.weights, torch.bfloat16, dev)[0]
-    N, d = wl1.n_tokens, wl1.d_model
-    g = torch.Generator(device=dev)
-    g.manual_seed(7)
-    kc = torch.randn((1, N, d), device=dev, generator=g).to(torch.bfloat16)
-    vc = torch.randn((1, N, d), device=dev, generator=g).to(torch.bfloat16)
-    x0 = torch.randn((1, N, d), device=dev, generator=g)
-    idx = torch.arange(N, dtype=torch.int32, device=dev)[None].contiguous()
-    ws = torch.empty(wamc.workspace_bytes(dims1, N), dtype=torch.uint8, device=dev)
-    rows = list(range(32, N + 1, 32)) + ([N] if N % 32 else [])
-    keff_n = torch.tensor([N], dtype=torch.int32, device=dev)
-    xw = x0.clone()  # the call updates its rows in place
-    clock_warm(lambda: wamc.refresh_layer(dims1, 0, w1, xw, idx, keff_n, N, kc, vc, ws, stream=stream))
-    del xw
-    curve = []
-    for m in rows:
-        keff = torch.tensor([m], dtype=torch.int32, device=dev)
-        x = x0[:, :m].contiguous()
-        for _ in range(2):
-            wamc.refresh_layer(dims1, 0, w1, x, idx, keff, m, kc, vc, ws, stream=stream)
-        a.record(stream)
-        for _ in range(5):
-            wamc.refresh_layer(dims1, 0, w1, x, idx, keff, m, kc, vc, ws, stream=stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        curve.append(a.elapsed_time(b) / 5)
-    del kc, vc, x0, ws
-    # whole chunks at k and at the capacity
     wl = W.preset("c3_stack", n_layers=args.sweep_layers)
+    N = wl.n_tokens
     r = W.make_rollout(wl, chunks=2)
     weights = wamc.Engine.upload_weights(r.weights, torch.bfloat16, dev)
     z0 = torch.from_numpy(r.z[0][0]).to(dev, torch.bfloat16)[None].contiguous()
     z1 = torch.from_numpy(r.z[0][1]).to(dev, torch.bfloat16)[None].contiguous()
     q1 = torch.from_numpy(r.qa[0][1]).to(dev, torch.bfloat16)[:, None].contiguous()
-    for k in (468, 1170, 2340, 2458, 2808):
-        k_fill = plateau_capacity(rows, curve, k, tol=0.02)
-        res = {}
-        for name, kk in (("k", k), ("fill", k_fill)):
-            # the smallest capacity the library accepts: N - k tokens may be forced
-            eng = wamc.Engine(wamc.dims_for(wl), weights, max(kk, wl.n_tokens - kk), dev)
-            eng.dense(z0)
+    eng = wamc.Engine(wamc.dims_for(wl), weights, N, dev)
+    eng.dense(z0)
+    start = eng.snapshot()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(8)]
 
-            def chunk_from_zero_ages():
-                eng.age.zero_()
-                eng.chunk(z1, q1, kk, stream=stream)
-            clock_warm(chunk_from_zero_ages)
-            ts = []
-            for _ in range(6):
-                eng.age.zero_()
-                a.record(stream)
-                eng.chunk(z1, q1, kk, stream=stream)
-                b.record(stream)
-                torch.cuda.synchronize()
-                ts.append(a.elapsed_time(b))
-            res[name] = float(np.median(ts[1:]))
-            del eng
-        print(json.dumps({"capacity": {"k": k, "k_fill": k_fill, "extra_tokens": k_fill - k},
-                          "layers": wl.n_layers, "n_tokens": N, "ms_at_k": res["k"], "ms_at_fill": res["fill"],
-                          "latency_change": res["fill"] / res["k"] - 1.0,
-                          "layer_ms_at_k": float(np.interp(k, rows, curve)),
-                          "layer_ms_at_fill": float(np.interp(k_fill, rows, curve))}), flush=True)
+    def chunk_ms(kk, reps=7):
+        eng.restore(start)
+        for i in range(reps):
+            eng.age.zero_()
+            ev[i][0].record(stream)
+            eng.chunk(z1, q1, kk, stream=stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([x.elapsed_time(y) for x, y in ev[1:reps]]))
+
+    def one_chunk():
+        eng.age.zero_()
+        eng.chunk(z1, q1, 2808, stream=stream)
+    clock_warm(one_chunk)
+    for k in (468, 1170, 2340, 2458, 2808):
+        rows = [k + 32 * j for j in range(17) if k + 32 * j <= N]
+        curve = [chunk_ms(kk) for kk in rows]
+        k_fill = plateau_capacity(rows, curve, k, tol=0.01)
+        at_k, at_fill = chunk_ms(k), chunk_ms(k_fill)
+        print(json.dumps({"capacity": {"k": k, "k_fill": k_fill, "extra_tokens": k_fill - k, "tolerance": 0.01},
+                          "layers": wl.n_layers, "n_tokens": N, "curve_rows": rows, "curve_ms": curve,
+                          "ms_at_k": at_k, "ms_at_fill": at_fill, "latency_change": at_fill / at_k - 1.0}),
+              flush=True)
 
 
 def run_plateau(args):

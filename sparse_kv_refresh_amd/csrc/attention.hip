@@ -65,15 +65,20 @@ __device__ __forceinline__ int vs_chunk(int row, int c) { return row * 16 + (c ^
 typedef short attn_v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) attn_v4i16_t lds_v4i16_t;
 
-// Key-split of the last round: with P workgroups resident (one per CU) and T
-// active (query tile, head, episode) units -- only tiles holding refreshed
-// rows count, read from k_eff on the device -- the first floor(T/P)*P units
-// take one workgroup each over all N keys; each of the r remaining units is
-// cut into C key ranges, C chosen from a cost model (rounds of the r*C pieces
-// x (fixed piece cost + key tiles per piece) + merge cost per piece) within
-// the grid's spare workgroups.  A split unit is completed by the last of its
-// pieces to arrive: it merges the C partial (o, max, sum) in key order, so
-// the result does not depend on arrival order.
+// Schedule (stream-K over the key tiles).  The active (query tile, head,
+// episode) units -- only tiles holding refreshed rows count, read from k_eff
+// on the device -- each have `ntiles` 64-key tiles; the T * ntiles (unit,
+// key tile) steps, in unit order, are cut into G equal contiguous ranges,
+// one per workgroup.  With at least P = 256 units (one round of the CUs),
+// G = P, so every CU gets the same number of tile steps whatever T is; a
+// range holds whole units and at most two partial ones (its first and its
+// last).  With fewer units, G = T * C: every unit is cut into C equal key
+// ranges, C from a cost model (rounds of the T*C pieces x (fixed piece cost
+// + key tiles per piece) + merge cost per piece).  A unit covered by several
+// ranges is completed by the last of its pieces to arrive, which merges the
+// partial (o, max, sum) of the pieces in key order, so the result does not
+// depend on arrival order.  Without scratch for partials, G = T (one unit
+// per workgroup).
 #ifndef WAMC_ATTN_MAX_SPLIT
 #define WAMC_ATTN_MAX_SPLIT 16
 #endif
@@ -83,31 +88,39 @@ typedef __attribute__((address_space(3))) attn_v4i16_t lds_v4i16_t;
 #ifndef WAMC_ATTN_MERGE_COST
 #define WAMC_ATTN_MERGE_COST 2
 #endif
+#ifndef WAMC_ATTN_STREAMK
+#define WAMC_ATTN_STREAMK 1
+#endif
 constexpr int kAttnP = 256;                      // resident workgroups (one per CU)
 constexpr int kAttnMinTiles = 4;                 // fewest key tiles per piece
 constexpr int kAttnMaxSplit = WAMC_ATTN_MAX_SPLIT;
 constexpr int kAttnPieceCost = WAMC_ATTN_PIECE_COST;   // in key tiles
 constexpr int kAttnMergeCost = WAMC_ATTN_MERGE_COST;   // in key tiles, per merged piece
 
+// First workgroup whose range [beg(v), beg(v+1)), beg(v) = v*S/G, holds
+// step x: the largest v with v*S/G <= x.
+__device__ __forceinline__ int attn_range_of(long long x, long long S, int G) {
+  return static_cast<int>(((x + 1) * G + S - 1) / S) - 1;
+}
+
 __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a, float scale2) {
   int T = 0;
   for (int bb = 0; bb < a.B; ++bb) T += (rows_of(a.k_eff, bb, a.rows_cap) + kAttnQ - 1) / kAttnQ;
   T *= a.H;
+  if (T == 0) return;
   const int ntiles = (a.N + kAttnKeys - 1) / kAttnKeys;
-  const int ndp = (T / kAttnP) * kAttnP;
-  const int hw = blockIdx.x;
-  int unit, C = 1, piece = 0, c = 0;
-  if (hw < ndp) {
-    unit = xcd_remap(hw, ndp);
-  } else {
-    const int r = T - ndp;
-    if (r == 0) return;
-    if (a.part) {
-      const int room = min(static_cast<int>(gridDim.x) - ndp, a.slots);
-      const int cmax = max(1, min(min(kAttnMaxSplit, ntiles / kAttnMinTiles), room / r));
-      float best = static_cast<float>((r + kAttnP - 1) / kAttnP) * static_cast<float>(kAttnPieceCost + ntiles);
+  int G = T;
+  if (a.part) {
+    if (WAMC_ATTN_STREAMK && T >= kAttnP && a.slots >= 2 * kAttnP) {
+      G = kAttnP;
+    } else if (T < kAttnP) {
+      // C pieces per unit within the grid and the partial slots (two per range)
+      const int room = min(static_cast<int>(gridDim.x), a.slots / 2);
+      const int cmax = max(1, min(min(kAttnMaxSplit, ntiles / kAttnMinTiles), room / T));
+      float best = static_cast<float>(kAttnPieceCost + ntiles);
+      int C = 1;
       for (int cc = 2; cc <= cmax; ++cc) {
-        const float cost = static_cast<float>((r * cc + kAttnP - 1) / kAttnP) *
+        const float cost = static_cast<float>((T * cc + kAttnP - 1) / kAttnP) *
                                (static_cast<float>(kAttnPieceCost) + static_cast<float>(ntiles) / cc) +
                            static_cast<float>(kAttnMergeCost * cc);
         if (cost < best) {
@@ -115,12 +128,39 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
           C = cc;
         }
       }
+      G = T * C;
     }
-    if (hw - ndp >= r * C) return;
-    piece = xcd_remap(hw - ndp, r * C);
-    unit = ndp + piece / C;
-    c = piece % C;
   }
+  if (static_cast<int>(blockIdx.x) >= G) return;
+  // consecutive ranges on one XCD: the units of one head share its K/V in that L2
+  const int v = xcd_remap(blockIdx.x, G);
+  const long long S_all = static_cast<long long>(T) * ntiles;
+  const long long beg = v * S_all / G, end = (v + 1) * S_all / G;
+
+  // per group and stage: a K tile, then a V tile, filled by direct-to-LDS
+  // loads.  One LDS object only: with a second one the compiler cannot tell
+  // the direct-to-LDS writes in flight from the reads and waits for the
+  // prefetch before every tile.
+  constexpr int kTileChunks = kKsBytes / 16, kStageChunks = 2 * kTileChunks;
+  __shared__ uint4 kv_all[kGroups][2][kStageChunks];
+
+  // the wave index is uniform: keep it (and what derives from it) in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wid >> 2, gw = wid & 3;
+  const int half = lane >> 5, col = lane & 31;
+  const int N = a.N, d = a.d;
+  uint4* Ks0 = &kv_all[grp][0][0];
+  uint4* Vs0 = Ks0 + kTileChunks;
+
+  for (long long pos = beg; pos < end;) {
+  if (pos != beg) __syncthreads();   // the previous unit's exchange area is read
+  const int unit_all = static_cast<int>(pos / ntiles);
+  const long long ubeg = static_cast<long long>(unit_all) * ntiles, uend = ubeg + ntiles;
+  const int kt0 = static_cast<int>(pos - ubeg);
+  const int kt1 = static_cast<int>(min(end, uend) - ubeg);
+  const bool first_seg = pos == beg;
+  pos = min(end, uend);
+  int unit = unit_all;
   // unit -> (episode, head, query tile), query tile fastest: the tiles of one
   // head run on one XCD and share its K/V in that L2
   int b = 0, rt = 1;
@@ -136,21 +176,6 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   const int h = unit / rt, qt = unit - h * rt;
   const int rows = rows_of(a.k_eff, b, a.rows_cap);
   const int q0 = qt * kAttnQ;
-  const int kt0 = c * ntiles / C, kt1 = (c + 1) * ntiles / C;   // this piece's key tiles
-
-  // per group and stage: a K tile, then a V tile, filled by direct-to-LDS
-  // loads.  One LDS object only: with a second one the compiler cannot tell
-  // the direct-to-LDS writes in flight from the reads and waits for the
-  // prefetch before every tile.
-  constexpr int kTileChunks = kKsBytes / 16, kStageChunks = 2 * kTileChunks;
-  __shared__ uint4 kv_all[kGroups][2][kStageChunks];
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int grp = wid >> 2, gw = wid & 3;
-  const int half = lane >> 5, col = lane & 31;
-  const int N = a.N, d = a.d;
-  uint4* Ks0 = &kv_all[grp][0][0];
-  uint4* Vs0 = Ks0 + kTileChunks;
   const bf16_t* Kc = static_cast<const bf16_t*>(a.k_cache) + static_cast<size_t>(b) * N * d + h * kDh;
   const bf16_t* Vc = static_cast<const bf16_t*>(a.v_cache) + static_cast<size_t>(b) * N * d + h * kDh;
 
@@ -399,44 +424,47 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
     l = lsum + __shfl_xor(lsum, 32, kWave);
   }
   bf16_t* Op = static_cast<bf16_t*>(a.o) + (static_cast<size_t>(b) * a.rows_cap + qrow) * d + h * kDh;
-  if (C == 1) {
-    if (grp == 1 || qrow >= rows) return;
-    const float inv = 1.0f / l;
+  if (kt0 == 0 && kt1 == ntiles) {
+    // the whole unit in this range: normalise and store
+    if (grp == 0 && qrow < rows) {
+      const float inv = 1.0f / l;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        // elements v = g4*4 .. g4*4+3: dh rows db*32 + g4*8 + half*4 + 0..3
-        float r[4];
+        for (int g4 = 0; g4 < 4; ++g4) {
+          // elements v = g4*4 .. g4*4+3: dh rows db*32 + g4*8 + half*4 + 0..3
+          float r[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = g4 * 4 + e;
-          r[e] = (o[db][v] * e0 + src[(db * 16 + v) * 64] * e1) * inv;
+          for (int e = 0; e < 4; ++e) {
+            const int vv = g4 * 4 + e;
+            r[e] = (o[db][vv] * e0 + src[(db * 16 + vv) * 64] * e1) * inv;
+          }
+          uint2 w;
+          w.x = pack_bf16x2(r[0], r[1]);
+          w.y = pack_bf16x2(r[2], r[3]);
+          *reinterpret_cast<uint2*>(Op + db * 32 + g4 * 8 + half * 4) = w;
         }
-        uint2 w;
-        w.x = pack_bf16x2(r[0], r[1]);
-        w.y = pack_bf16x2(r[2], r[3]);
-        *reinterpret_cast<uint2*>(Op + db * 32 + g4 * 8 + half * 4) = w;
-      }
-    return;
+    }
+    continue;
   }
 
-  // split unit: group 0 writes this piece's (o relative to m, m, l) to its
-  // scratch slot as relaxed system-scope atomics (coherent between the XCDs'
-  // caches without cache-wide maintenance), then the arrival is counted
+  // part of the unit: group 0 writes this piece's (o relative to m, m, l) to
+  // the range's slot (2v for its first piece, 2v + 1 for its last) as relaxed
+  // system-scope atomics (coherent between the XCDs' caches without
+  // cache-wide maintenance), then the arrival is counted
   const int gl = gw * 64 + lane;   // lane of group 0 holding the same queries
   float* slot_base = a.part;
   if (grp == 0) {
-    float* dst = slot_base + static_cast<size_t>(piece) * kAttnPartFloats;
+    float* dst = slot_base + static_cast<size_t>(2 * v + (first_seg ? 0 : 1)) * kAttnPartFloats;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
-          const int v = g4 * 4 + e;
-          const float x0 = o[db][v] * e0 + src[(db * 16 + v) * 64] * e1;
-          const float x1 = o[db][v + 1] * e0 + src[(db * 16 + v + 1) * 64] * e1;
+          const int vv = g4 * 4 + e;
+          const float x0 = o[db][vv] * e0 + src[(db * 16 + vv) * 64] * e1;
+          const float x1 = o[db][vv + 1] * e0 + src[(db * 16 + vv + 1) * 64] * e1;
           const unsigned long long w = (static_cast<unsigned long long>(__float_as_uint(x1)) << 32) | __float_as_uint(x0);
           __hip_atomic_store(reinterpret_cast<unsigned long long*>(dst) + ((db * 4 + g4) * 2 + e / 2) * 256 + gl, w,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -446,30 +474,37 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   }
   __builtin_amdgcn_s_waitcnt(0);   // the stores have reached the coherence point
   __syncthreads();
+  // the ranges holding this unit: v_first .. v_last, in key order
+  const int v_first = attn_range_of(ubeg, S_all, G);
+  const int v_last = attn_range_of(uend - 1, S_all, G);
+  const int npieces = v_last - v_first + 1;
   int* flag = reinterpret_cast<int*>(xml) + 1024;   // past the exchanged m, l
-  const int uid = piece / C + ndp;
   if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(&a.counters[uid], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    const int last = old == C - 1 ? 1 : 0;
-    if (last) __hip_atomic_store(&a.counters[uid], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int old = __hip_atomic_fetch_add(&a.counters[unit_all], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int last = old == npieces - 1 ? 1 : 0;
+    if (last) __hip_atomic_store(&a.counters[unit_all], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     *flag = last;
   }
   __syncthreads();
-  if (!*flag || qrow >= rows) return;
-  // last piece: merge the C partials in key order; group g finishes dh blocks 2g, 2g+1
-  const float* first = slot_base + static_cast<size_t>(piece - c) * kAttnPartFloats;
+  if (!*flag || qrow >= rows) continue;
+  // last piece: merge the partials in key order; group g finishes dh blocks 2g, 2g+1.
+  // A range that starts inside the unit holds it as its first piece (slot
+  // 2v), one that starts before it as its last (slot 2v + 1).
   float mt = -INFINITY;
-  for (int cc = 0; cc < C; ++cc)
-    mt = fmaxf(mt, __hip_atomic_load(first + static_cast<size_t>(cc) * kAttnPartFloats + 128 * 128 + gl,
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
+  for (int vc = v_first; vc <= v_last; ++vc) {
+    const long long bc = vc * S_all / G;
+    const float* pp = slot_base + static_cast<size_t>(2 * vc + (bc >= ubeg ? 0 : 1)) * kAttnPartFloats;
+    mt = fmaxf(mt, __hip_atomic_load(pp + 128 * 128 + gl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
+  }
   float acc[2][16];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+    for (int vv = 0; vv < 16; ++vv) acc[i][vv] = 0.f;
   float lt = 0.f;
-  for (int cc = 0; cc < C; ++cc) {
-    const float* pp = first + static_cast<size_t>(cc) * kAttnPartFloats;
+  for (int vc = v_first; vc <= v_last; ++vc) {
+    const long long bc = vc * S_all / G;
+    const float* pp = slot_base + static_cast<size_t>(2 * vc + (bc >= ubeg ? 0 : 1)) * kAttnPartFloats;
     const float mc = __hip_atomic_load(pp + 128 * 128 + gl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     const float lc = __hip_atomic_load(pp + 128 * 128 + 256 + gl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     const float sc = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mc - mt) * scale2);
@@ -500,6 +535,7 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
       w.y = pack_bf16x2(acc[i][g4 * 4 + 2] * inv, acc[i][g4 * 4 + 3] * inv);
       *reinterpret_cast<uint2*>(Op + (2 * grp + i) * 32 + g4 * 8 + half * 4) = w;
     }
+  }   // ranges of this workgroup
 }
 
 // ---------------------------------------------------------------------------
@@ -557,12 +593,12 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s, KernelT
   TimedLaunch t(timer, "attention", s);
   const float scale2 = kLog2e / sqrtf(static_cast<float>(a.dh));
   if (bf16) {
-    // one workgroup per unit at rows_cap rows; room for the pieces of split
-    // units: a full round when the units overflow one round, else the round
-    // itself (unused workgroups exit at once)
+    // with partial scratch: one round of workgroups (the kernel derives its
+    // ranges from k_eff and exits the ones it does not need); without: one
+    // workgroup per unit at rows_cap rows
     const long long units = static_cast<long long>((a.rows_cap + kAttnQ - 1) / kAttnQ) * a.H * a.B;
-    const long long spare = units > kAttnP ? units + kAttnP : kAttnP;
-    const unsigned grid = static_cast<unsigned>(a.part ? spare : units);
+    const long long with_part = WAMC_ATTN_STREAMK ? kAttnP : std::max<long long>(units, kAttnP);
+    const unsigned grid = static_cast<unsigned>(a.part ? with_part : units);
     launch(attn_bf16_kernel, grid, kAttnThreads2, 0, s, a, scale2);
   } else {
     const dim3 grid((a.rows_cap + 3) / 4, a.H, a.B);

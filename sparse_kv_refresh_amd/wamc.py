@@ -15,7 +15,9 @@ from typing import List, Optional, Sequence
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libwamc.so")
+# WAMC_LIB names another build of the library (for A/B measurements of build
+# options); the in-tree libwamc.so otherwise
+LIB_PATH = os.environ.get("WAMC_LIB") or os.path.join(PKG, "libwamc.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "wamc.h")
 
 WAMC_FP32, WAMC_BF16 = 0, 1

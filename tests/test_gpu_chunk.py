@@ -272,3 +272,82 @@ def test_union_rule_rollout(name):
         _compare_chunk(wl, eng, states, res, lo, t)
         assert int(eng.age.max()) <= wl.age_bound
     assert min(keffs) >= max(na, ns)
+
+
+def test_capacity_filled_chunk():
+    """A capacity-filled refresh (RealtimeWAM §3: the plateau's upper end is
+    the execution capacity, filled with the next-ranked tokens): the chunk's
+    latency is measured on the GPU from k upward, the fill count taken by the
+    capacity policy, and the chunk at that count compared with the oracle on
+    the same refresh set; then the same at a fixed ragged fill (k + 56)."""
+    from sparse_kv_refresh_amd.capacity import plateau_capacity
+    wl = W.preset("t_bf16_small")
+    r = W.make_rollout(wl, chunks=2)
+    prec = O.Precision(wl.dtype)
+    N, k = wl.n_tokens, wl.k
+    eng = engine(wl, r)                       # rows_cap = N
+    eng.dense(batch_z(wl, r, 0))
+    snap = eng.snapshot()
+    z1, q1 = batch_z(wl, r, 1), batch_q(wl, r, 1)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    rows = [k + 32 * j for j in range(9) if k + 32 * j <= N]
+    curve = []
+    for kk in rows:
+        for i in range(5):
+            eng.restore(snap)
+            ev[i][0].record(stream)
+            eng.chunk(z1, q1, kk, stream=stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        curve.append(float(np.median([a.elapsed_time(b) for a, b in ev[1:]])))
+    k_fill = plateau_capacity(rows, curve, k, tol=0.01)
+    assert k <= k_fill <= N
+    for kf in sorted({k_fill, k + 56}):
+        eng.restore(snap)
+        st = _oracle_states(wl, r, prec)[0]
+        res = O.refresh_chunk(st, r.z[0][1], r.qa[0][1], r.weights, kf, wl.age_bound, wl.n_heads, wl.ln_eps,
+                              wl.w_attn, wl.w_surprise, prec)
+        assert res.k_eff == kf
+        ov = np.full((1, N), -1, dtype=np.int32)
+        ov[0, :kf] = res.idx
+        lo = torch.zeros((wl.n_layers, 1, N, wl.d_model), dtype=torch.float32, device=DEV)
+        eng.chunk(z1, q1, kf, idx_override=to_dev(ov), k_eff_override=to_dev(np.array([kf], dtype=np.int32)),
+                  layer_out=lo)
+        torch.cuda.synchronize()
+        _compare_chunk(wl, eng, [st], [res], lo, 1)
+        # with its own selection the library fills by rank: the oracle's rule on the GPU's scores
+        eng.restore(snap)
+        eng.chunk(z1, q1, kf, layer_out=lo)
+        torch.cuda.synchronize()
+        sel, ke, _, _ = O.select(to_np(eng.score[0]), np.zeros(N, dtype=np.int64), kf, wl.age_bound)
+        assert int(eng.k_eff[0]) == ke == kf
+        assert np.array_equal(to_np(eng.idx[0])[:ke], sel)
+
+
+@pytest.mark.parametrize("rows,cols", [(12, 10), (36, 30)])
+def test_small_token_stack(rows, cols):
+    """The small-context regime of the pages' latency experiment (WAM-Cache
+    §5.2: the refresh ratio 0.584 of the native 120 visual tokens, here at 120
+    and 1080 tokens) on three layers of the d=1536 stack, G = 2, in the
+    launch configuration the small-N benchmark uses (rows_cap = k): three
+    refresh chunks driven by the oracle's refresh sets."""
+    N = rows * cols
+    k = int(round(0.584 * N))
+    wl = W.preset("c3_stack", n_layers=3, views=1, rows=rows, cols=cols, k=k, age_bound=2, chunks=4)
+    r = W.make_rollout(wl, chunks=wl.chunks)
+    prec = O.Precision(wl.dtype)
+    states = _oracle_states(wl, r, prec)
+    eng = engine(wl, r, rows_cap=k)
+    eng.dense(batch_z(wl, r, 0))
+    lo = torch.zeros((wl.n_layers, 1, k, wl.d_model), dtype=torch.float32, device=DEV)
+    for t in range(1, wl.chunks):
+        res = [O.refresh_chunk(states[0], r.z[0][t], r.qa[0][t], r.weights, k, wl.age_bound, wl.n_heads,
+                               wl.ln_eps, wl.w_attn, wl.w_surprise, prec)]
+        assert res[0].k_eff == k          # k >= N/2: the forced tokens always fit in k
+        ov = np.full((1, N), -1, dtype=np.int32)
+        ov[0, :k] = res[0].idx
+        eng.chunk(batch_z(wl, r, t), batch_q(wl, r, t), k, idx_override=to_dev(ov),
+                  k_eff_override=to_dev(np.array([k], dtype=np.int32)), layer_out=lo)
+        torch.cuda.synchronize()
+        _compare_chunk(wl, eng, states, res, lo, t)
