@@ -43,7 +43,15 @@ constexpr int kDh = 128;
 // more than 2^kLazy in probability (log2 units), so most tiles skip the
 // rescale of the output accumulators; exp2 arguments stay <= kLazy.
 constexpr float kLazy = 8.0f;
-constexpr int kGroups = 2;                      // key-split groups of 4 waves
+#ifndef WAMC_ATTN_GROUPS
+#define WAMC_ATTN_GROUPS 2
+#endif
+// key-split groups of 4 waves per workgroup: 2 (one 8-wave workgroup per CU,
+// the groups take alternate key tiles and merge) or 1 (two independent
+// 4-wave workgroups per CU)
+constexpr int kGroups = WAMC_ATTN_GROUPS;
+static_assert(kGroups == 1 || kGroups == 2, "one or two key groups");
+constexpr int kAttnPerCu = 2 / kGroups;         // resident workgroups per CU
 constexpr int kAttnThreads2 = kAttnThreads * kGroups;
 constexpr int kKsBytes = kAttnKeys * kDh * 2;   // one K or V tile, 256-byte rows, XOR-swizzled chunks
 
@@ -91,7 +99,8 @@ typedef __attribute__((address_space(3))) attn_v4i16_t lds_v4i16_t;
 #ifndef WAMC_ATTN_STREAMK
 #define WAMC_ATTN_STREAMK 1
 #endif
-constexpr int kAttnP = 256;                      // resident workgroups (one per CU)
+constexpr int kAttnP = 256 * kAttnPerCu;        // resident workgroups
+constexpr int kAttnStreamUnits = 256;            // from one unit per CU on: stream-K over all P workgroups
 constexpr int kAttnMinTiles = 4;                 // fewest key tiles per piece
 constexpr int kAttnMaxSplit = WAMC_ATTN_MAX_SPLIT;
 constexpr int kAttnPieceCost = WAMC_ATTN_PIECE_COST;   // in key tiles
@@ -103,7 +112,7 @@ __device__ __forceinline__ int attn_range_of(long long x, long long S, int G) {
   return static_cast<int>(((x + 1) * G + S - 1) / S) - 1;
 }
 
-__global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a, float scale2) {
+__global__ __launch_bounds__(kAttnThreads2, kAttnPerCu) void attn_bf16_kernel(AttnArgs a, float scale2) {
   int T = 0;
   for (int bb = 0; bb < a.B; ++bb) T += (rows_of(a.k_eff, bb, a.rows_cap) + kAttnQ - 1) / kAttnQ;
   T *= a.H;
@@ -111,9 +120,9 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   const int ntiles = (a.N + kAttnKeys - 1) / kAttnKeys;
   int G = T;
   if (a.part) {
-    if (WAMC_ATTN_STREAMK && T >= kAttnP && a.slots >= 2 * kAttnP) {
+    if (WAMC_ATTN_STREAMK && T >= kAttnStreamUnits && a.slots >= 2 * kAttnP) {
       G = kAttnP;
-    } else if (T < kAttnP) {
+    } else if (T < kAttnStreamUnits) {
       // C pieces per unit within the grid and the partial slots (two per range)
       const int room = min(static_cast<int>(gridDim.x), a.slots / 2);
       const int cmax = max(1, min(min(kAttnMaxSplit, ntiles / kAttnMinTiles), room / T));
@@ -402,27 +411,36 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   __syncthreads();
   float* xo = reinterpret_cast<float*>(&kv_all[0][0][0]);
   float* xml = xo + 4 * 64 * 64;
-  static_assert(4 * 64 * 64 * 4 + 4 * 2 * 64 * 4 + 16 <= sizeof(kv_all), "exchange of o, m, l and the flag fits the tile buffers");
-  if (grp == 1) {
-    float* dst = xo + static_cast<size_t>(gw) * 64 * 64 + lane;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) dst[(db * 16 + v) * 64] = o[db][v];
-    xml[(gw * 2 + 0) * 64 + lane] = m_run;
-    xml[(gw * 2 + 1) * 64 + lane] = l_run;
-  }
-  __syncthreads();
-  const float* src = xo + static_cast<size_t>(gw) * 64 * 64 + lane;
   float m = 0.f, e0 = 0.f, e1 = 0.f, l = 0.f;
-  if (grp == 0) {
-    const float m1 = xml[(gw * 2 + 0) * 64 + lane], l1 = xml[(gw * 2 + 1) * 64 + lane];
-    m = fmaxf(m_run, m1);
-    e0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m) * scale2);
-    e1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * scale2);
-    const float lsum = l_run * e0 + l1 * e1;
-    l = lsum + __shfl_xor(lsum, 32, kWave);
+  if constexpr (kGroups == 2) {
+    static_assert(kGroups != 2 || 4 * 64 * 64 * 4 + 4 * 2 * 64 * 4 + 16 <= sizeof(kv_all),
+                  "exchange of o, m, l and the flag fits the tile buffers");
+    if (grp == 1) {
+      float* dst = xo + static_cast<size_t>(gw) * 64 * 64 + lane;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[(db * 16 + v) * 64] = o[db][v];
+      xml[(gw * 2 + 0) * 64 + lane] = m_run;
+      xml[(gw * 2 + 1) * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const float m1 = xml[(gw * 2 + 0) * 64 + lane], l1 = xml[(gw * 2 + 1) * 64 + lane];
+      m = fmaxf(m_run, m1);
+      e0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m) * scale2);
+      e1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * scale2);
+      const float lsum = l_run * e0 + l1 * e1;
+      l = lsum + __shfl_xor(lsum, 32, kWave);
+    }
+  } else {
+    m = m_run;
+    e0 = 1.f;
+    l = l_run + __shfl_xor(l_run, 32, kWave);
   }
+  // group 1's contribution to element (db, v) of this lane (none with one group)
+  const float* src = xo + static_cast<size_t>(gw) * 64 * 64 + lane;
+  auto other = [&](int db, int vv) { return kGroups == 2 ? src[(db * 16 + vv) * 64] * e1 : 0.f; };
   bf16_t* Op = static_cast<bf16_t*>(a.o) + (static_cast<size_t>(b) * a.rows_cap + qrow) * d + h * kDh;
   if (kt0 == 0 && kt1 == ntiles) {
     // the whole unit in this range: normalise and store
@@ -437,7 +455,7 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int vv = g4 * 4 + e;
-            r[e] = (o[db][vv] * e0 + src[(db * 16 + vv) * 64] * e1) * inv;
+            r[e] = (o[db][vv] * e0 + other(db, vv)) * inv;
           }
           uint2 w;
           w.x = pack_bf16x2(r[0], r[1]);
@@ -463,8 +481,8 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
           const int vv = g4 * 4 + e;
-          const float x0 = o[db][vv] * e0 + src[(db * 16 + vv) * 64] * e1;
-          const float x1 = o[db][vv + 1] * e0 + src[(db * 16 + vv + 1) * 64] * e1;
+          const float x0 = o[db][vv] * e0 + other(db, vv);
+          const float x1 = o[db][vv + 1] * e0 + other(db, vv + 1);
           const unsigned long long w = (static_cast<unsigned long long>(__float_as_uint(x1)) << 32) | __float_as_uint(x0);
           __hip_atomic_store(reinterpret_cast<unsigned long long*>(dst) + ((db * 4 + g4) * 2 + e / 2) * 256 + gl, w,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -478,7 +496,8 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   const int v_first = attn_range_of(ubeg, S_all, G);
   const int v_last = attn_range_of(uend - 1, S_all, G);
   const int npieces = v_last - v_first + 1;
-  int* flag = reinterpret_cast<int*>(xml) + 1024;   // past the exchanged m, l
+  // past the exchanged m, l (with one group the tile buffers are free)
+  int* flag = kGroups == 2 ? reinterpret_cast<int*>(xml) + 1024 : reinterpret_cast<int*>(xo);
   if (tid == 0) {
     const int old = __hip_atomic_fetch_add(&a.counters[unit_all], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     const int last = old == npieces - 1 ? 1 : 0;
@@ -487,7 +506,9 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
   }
   __syncthreads();
   if (!*flag || qrow >= rows) continue;
-  // last piece: merge the partials in key order; group g finishes dh blocks 2g, 2g+1.
+  // last piece: merge the partials in key order; with two groups group g
+  // finishes dh blocks 2g, 2g+1, with one group the group does all four, two
+  // blocks at a time.
   // A range that starts inside the unit holds it as its first piece (slot
   // 2v), one that starts before it as its last (slot 2v + 1).
   float mt = -INFINITY;
@@ -496,6 +517,7 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
     const float* pp = slot_base + static_cast<size_t>(2 * vc + (bc >= ubeg ? 0 : 1)) * kAttnPartFloats;
     mt = fmaxf(mt, __hip_atomic_load(pp + 128 * 128 + gl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
   }
+  for (int blk0 = 2 * grp; blk0 < 4; blk0 += 2 * kGroups) {
   float acc[2][16];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -515,7 +537,7 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         w[i * 8 + q] = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(pp) +
-                                             (((2 * grp + i) * 4 + q / 2) * 2 + q % 2) * 256 + gl,
+                                             (((blk0 + i) * 4 + q / 2) * 2 + q % 2) * 256 + gl,
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -533,8 +555,9 @@ __global__ __launch_bounds__(kAttnThreads2, 1) void attn_bf16_kernel(AttnArgs a,
       uint2 w;
       w.x = pack_bf16x2(acc[i][g4 * 4 + 0] * inv, acc[i][g4 * 4 + 1] * inv);
       w.y = pack_bf16x2(acc[i][g4 * 4 + 2] * inv, acc[i][g4 * 4 + 3] * inv);
-      *reinterpret_cast<uint2*>(Op + (2 * grp + i) * 32 + g4 * 8 + half * 4) = w;
+      *reinterpret_cast<uint2*>(Op + (blk0 + i) * 32 + g4 * 8 + half * 4) = w;
     }
+  }   // dh block pairs
   }   // ranges of this workgroup
 }
 

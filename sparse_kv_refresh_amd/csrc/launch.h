@@ -205,7 +205,12 @@ struct AttnArgs {
 hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s, KernelTimer* timer);
 
 // Scratch of the key-split attention for B episodes of rows_cap rows and H heads.
-constexpr int kAttnSlotsMax = 512;
+#ifndef WAMC_ATTN_GROUPS
+#define WAMC_ATTN_GROUPS 2
+#endif
+// two partial slots per resident workgroup (256 per CU-round with 8-wave
+// workgroups, 512 with 4-wave ones)
+constexpr int kAttnSlotsMax = 512 * (WAMC_ATTN_GROUPS == 1 ? 2 : 1);
 constexpr int kAttnPartFloats = 128 * 128 + 2 * 256;   // o (128 queries x 128 dh) + m, l per lane
 struct AttnScratch {
   size_t part_bytes, counter_bytes;
