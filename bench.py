@@ -385,6 +385,16 @@ def run_small_n(args):
         out["speedup_eager"] = out["dense_ms_eager"] / out["refresh_ms_eager"]
         out["speedup_graph"] = out["dense_ms_graph"] / out["refresh_ms_graph"]
         out["speedup_bound"] = N / k
+        # per-kernel split of one layer's time, refresh and dense (eager calls, kernel timer)
+        for name, fn in (("refresh", refresh), ("dense", dense)):
+            eng.restore(snap)
+            wamc.timing_enable(True)
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            kt = wamc.timing_read()
+            wamc.timing_enable(False)
+            out[f"{name}_kernel_us_per_chunk"] = {kk: 1e3 * tot / 5 for kk, (n, tot) in kt.items()}
         print(json.dumps(out), flush=True)
         del eng
 
