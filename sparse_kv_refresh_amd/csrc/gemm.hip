@@ -839,7 +839,10 @@ constexpr int kSkMaxSplit = WAMC_SK_MAX_SPLIT;   // most pieces per tile
 // fixed cost of one piece (pipeline fill, partial store, arrival, fix-up), in k-tiles
 constexpr int kSkPieceCost = WAMC_SK_PIECE_COST;
 // k-tiles from which the launch grid makes room for a split tail
-constexpr int kSkLongK = 64;
+#ifndef WAMC_SK_LONG_K
+#define WAMC_SK_LONG_K 64
+#endif
+constexpr int kSkLongK = WAMC_SK_LONG_K;
 
 // Pieces per tile for r tail tiles of nk k-tiles each, P resident
 // workgroups and room for `room` pieces: S minimises (rounds of r*S pieces)
@@ -1094,6 +1097,218 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-K pieces with a separate reduction (few output tiles)
+//
+// With a few hundred rows the projections have a few dozen 128x128 tiles, and
+// a kernel that gives each tile one workgroup waits one load round trip per
+// k-tile on a handful of CUs.  Here every 64x128 or 128x128 tile is cut
+// along K into S pieces, one workgroup each, so the tiles x S workgroups fill
+// the CUs; each
+// piece stores its raw f32 accumulators to its own plane of the scratch,
+// [S][M][Nout], valid rows only.  A second kernel sums the S planes of each
+// element in piece order (so the result does not depend on which piece ran
+// first) and applies the epilogue, spread over every CU.  Measured at
+// d = 1536 with 70 to 1080 rows this beats both the one-tile-per-workgroup
+// kernels and the work-balanced kernel's split, whose last piece reads all
+// S partial tiles itself, one round trip to the coherence point per piece.
+// ---------------------------------------------------------------------------
+#ifndef WAMC_GEMM_PARTS
+#define WAMC_GEMM_PARTS 1
+#endif
+#ifndef WAMC_PARTS_RESIDENT
+#define WAMC_PARTS_RESIDENT 512
+#endif
+#ifndef WAMC_PARTS_MIN_ITERS
+#define WAMC_PARTS_MIN_ITERS 6
+#endif
+#ifndef WAMC_PARTS_MAX_SPLIT
+#define WAMC_PARTS_MAX_SPLIT 16
+#endif
+constexpr int kPartsBN = 128, kPartsBK = 64;
+constexpr int kPartsTallRows = 384;   // rows from which a long-K split takes 128-row tiles
+constexpr int kPartsResident = WAMC_PARTS_RESIDENT;   // two 4-wave workgroups (48 or 64 KiB LDS each) per CU
+constexpr int kPartsMinIters = WAMC_PARTS_MIN_ITERS;  // fewest k-tiles per piece
+constexpr int kPartsMaxSplit = WAMC_PARTS_MAX_SPLIT;
+
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_parts_kernel(GemmArgs g) {
+  constexpr int NT = 64 * WGM * WGN, NW = NT / 64;
+  constexpr int CPR = BK / 8;
+  constexpr int CHUNKS_A = BM * CPR, CHUNKS_B = BN * CPR;
+  constexpr int LOADS_A = CHUNKS_A / NT;
+  constexpr int LOADS_B = CHUNKS_B / NT;
+  constexpr int LOADS = LOADS_A + LOADS_B;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TI = WTM / 32, TJ = WTN / 32;
+  static_assert(LOADS_A * NT == CHUNKS_A && LOADS_B * NT == CHUNKS_B, "tile/threads");
+  static_assert(TI * 32 == WTM && TJ * 32 == WTN, "wave tile");
+
+  const int S = g.parts;
+  const int B = g.M / g.rows_cap;
+  int tiles_m = 0;
+  for (int b = 0; b < B; ++b) tiles_m += (rows_of(g.k_eff, b, g.rows_cap) + BM - 1) / BM;
+  const int tiles_n = (g.Nout + BN - 1) / BN;
+  const int tiles = tiles_m * tiles_n;
+  const int items = tiles * S;   // the grid is sized for rows_cap rows: the rest exit
+  if (static_cast<int>(blockIdx.x) >= items) return;
+  // item v = piece sp of tile t; consecutive items (one XCD) share a W panel and K range
+  const int v = xcd_remap(blockIdx.x, items);
+  const int sp = v / tiles;
+  const SkTile tl = sk_tile<BM, BN>(g, v - sp * tiles, tiles_m, tiles_n);
+  const int nk_all = g.K / BK;
+  const int kk0 = sp * nk_all / S, n = (sp + 1) * nk_all / S - kk0;
+
+  __shared__ uint4 lds[STAGES][CHUNKS_A + CHUNKS_B];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WGN, wn = wid % WGN;
+  const int half = lane >> 5, col = lane & 31;
+  const int K = g.K;
+  int goff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int il = i < LOADS_A ? i : i - LOADS_A;
+    const int c = (il * NW + wid) * 64 + lane;
+    const int row = c / CPR;
+    const int kc = swz_kc<CPR>(row, c % CPR);
+    if (i < LOADS_A) goff[i] = (min(tl.m0 + row, g.M - 1) - tl.m0) * K + kc * 8 + kk0 * BK;
+    else goff[i] = (min(tl.n0 + row, g.Nout - 1) - tl.n0) * K + kc * 8 + kk0 * BK;
+  }
+  const bf16_t* At = static_cast<const bf16_t*>(g.a) + static_cast<size_t>(tl.m0) * K;
+  const bf16_t* Wtt = static_cast<const bf16_t*>(g.w) + static_cast<size_t>(tl.n0) * K;
+  auto issue = [&](int kt, int stage) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const bf16_t* src = (i < LOADS_A ? At : Wtt) + goff[i] + kt * BK;
+      const int il = i < LOADS_A ? i : i - LOADS_A;
+      uint4* dst = &lds[stage][(i < LOADS_A ? 0 : CHUNKS_A) + (il * NW + wid) * 64];
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
+    }
+  };
+  f32x16_t acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
+  const int ra = wm * WTM + col, rb = wn * WTN + col;
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < n) issue(p, p);
+  for (int q = 0; q < n; ++q) {
+    wait_tiles_ahead<LOADS, STAGES - 2>(min(STAGES - 2, n - 1 - q));
+    __builtin_amdgcn_s_barrier();
+    if (q + STAGES - 1 < n) issue(q + STAGES - 1, (q + STAGES - 1) % STAGES);
+    const uint4* as = lds[q % STAGES];
+    mma_stage<BK, TI, TJ, CPR>(as, as + CHUNKS_A, ra, rb, half, acc);
+  }
+  // lane (half, col) of block (i, j) holds row wm*WTM + 32i + col, columns
+  // wn*WTN + 32j + 8gg + 4half + (0..3) (the operands are issued W first)
+  float* plane = g.sk_partial + static_cast<size_t>(sp) * g.M * g.Nout;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int m = tl.m0 + wm * WTM + 32 * i + col;
+    if (m >= tl.mend) continue;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int c = tl.n0 + wn * WTN + 32 * j + 8 * gg + 4 * half;
+        if (c < g.Nout)
+          *reinterpret_cast<float4*>(plane + static_cast<size_t>(m) * g.Nout + c) =
+              make_float4(acc[i][j][4 * gg], acc[i][j][4 * gg + 1], acc[i][j][4 * gg + 2], acc[i][j][4 * gg + 3]);
+      }
+  }
+}
+
+// Sum of the S planes in piece order, then the epilogue of the tile kernels
+// (v = acc + bias; act(v), or resid + gate * v as one fma), four columns a
+// thread (Nout % 4 == 0, so a group lies in one of Q | K | V).
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_parts_epilogue_kernel(GemmArgs g) {
+  const int S = g.parts;
+  const int groups = g.Nout / 4;
+  const long long total = static_cast<long long>(g.M) * groups;
+  const size_t plane = static_cast<size_t>(g.M) * g.Nout;
+  const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
+  for (long long q = blockIdx.x * 256LL + threadIdx.x; q < total; q += static_cast<long long>(gridDim.x) * 256) {
+    const int m = static_cast<int>(q / groups);
+    const int c = static_cast<int>(q - static_cast<long long>(m) * groups) * 4;
+    const RowInfo ri = row_info(g, m);
+    if (!ri.valid) continue;
+    const float* src = g.sk_partial + static_cast<size_t>(m) * g.Nout + c;
+    float4 a = *reinterpret_cast<const float4*>(src);
+    for (int p = 1; p < S; ++p) {
+      const float4 x = *reinterpret_cast<const float4*>(src + p * plane);
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+    }
+    const uint2 bb = *reinterpret_cast<const uint2*>(bias + c);
+    float y[4] = {a.x + __uint_as_float(bb.x << 16), a.y + __uint_as_float(bb.x & 0xffff0000u),
+                  a.z + __uint_as_float(bb.y << 16), a.w + __uint_as_float(bb.y & 0xffff0000u)};
+    if constexpr (EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN || EPI == EPI_RESID_PLAIN) {
+      uint2 gt = make_uint2(0x3f803f80u, 0x3f803f80u);   // 1.0 in bf16: ungated
+      if constexpr (EPI != EPI_RESID_PLAIN) gt = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(g.gate) + c);
+      const size_t o = static_cast<size_t>(m) * g.Nout + c;
+      const float4 xin = *reinterpret_cast<const float4*>(g.resid_in + o);
+      float4 xo;
+      xo.x = fmaf(__uint_as_float(gt.x << 16), y[0], xin.x);
+      xo.y = fmaf(__uint_as_float(gt.x & 0xffff0000u), y[1], xin.y);
+      xo.z = fmaf(__uint_as_float(gt.y << 16), y[2], xin.z);
+      xo.w = fmaf(__uint_as_float(gt.y & 0xffff0000u), y[3], xin.w);
+      *reinterpret_cast<float4*>(g.resid_out + o) = xo;
+    } else {
+      if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = gelu_erf_fast(y[e]);
+      }
+      uint2 w;
+      w.x = pack_bf16x2(y[0], y[1]);
+      w.y = pack_bf16x2(y[2], y[3]);
+      if constexpr (EPI == EPI_QKV || EPI == EPI_KV) {
+        const int d = g.d_model;
+        const int wr = c / d, cc = c - wr * d;
+        const int which = wr + (EPI == EPI_KV ? 1 : 0);
+        int r = m;
+        if (which != 0) {
+          const int tok = g.idx ? g.idx[static_cast<size_t>(ri.b) * g.n_tokens + ri.r] : ri.r;
+          r = (tok >= 0 && tok < g.n_tokens) ? ri.b * g.n_tokens + tok : -1;
+        }
+        bf16_t* dst = static_cast<bf16_t*>(which == 0 ? g.q_out : (which == 1 ? g.k_cache : g.v_cache));
+        if (r >= 0) *reinterpret_cast<uint2*>(dst + static_cast<size_t>(r) * d + cc) = w;
+      } else {
+        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.g_out) + static_cast<size_t>(m) * g.Nout + c) = w;
+      }
+    }
+  }
+}
+
+// Pieces per tile (S = 1: the path is not taken) and the tile height of the
+// split-K path.  S is as large as keeps the tiles x S workgroups within one
+// round of the resident workgroups, with at least kPartsMinIters k-tiles per
+// piece and the S planes within the scratch.  Measured at d = 1536, 70 to
+// 1080 rows: with a long K (the MLP down projection) any split pays, and from
+// a few hundred rows on 128-row tiles, which read A and W half as often, beat
+// 64-row ones (1080 rows: 55 against 69 us); with a short K a two-piece split
+// loses to the in-workgroup split-K kernel (QKV at 280 rows: 24 against 20 us),
+// so it takes three pieces or more.
+struct PartsPlan {
+  int S, bm;
+};
+static PartsPlan parts_plan(const GemmArgs& g) {
+  PartsPlan p{1, 64};
+  if (!WAMC_GEMM_PARTS || !g.sk_partial || g.K % kPartsBK != 0 || g.Nout % 4 != 0) return p;
+  const int nk = g.K / kPartsBK;
+  const bool long_k = nk >= kSkLongK;
+  p.bm = long_k && g.M >= kPartsTallRows ? 128 : 64;
+  const long long tiles = static_cast<long long>(g.M / g.rows_cap) * ((g.rows_cap + p.bm - 1) / p.bm) *
+                          ((g.Nout + kPartsBN - 1) / kPartsBN);
+  const long long plane = static_cast<long long>(g.M) * g.Nout * 4;
+  long long S = std::min<long long>(kPartsResident / tiles, nk / kPartsMinIters);
+  S = std::min<long long>(S, kPartsMaxSplit);
+  S = std::min<long long>(S, static_cast<long long>(g.sk_partial_bytes) / plane);
+  p.S = S >= (long_k ? 2 : 3) ? static_cast<int>(S) : 1;
+  return p;
+}
+
 #ifndef WAMC_GEMM_BIG
 #define WAMC_GEMM_BIG 1
 #endif
@@ -1282,7 +1497,9 @@ static bool wide_tiles_pay(const GemmArgs& g, long long rows_known) {
 
 hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer) {
   if (g.M <= 0 || g.Nout <= 0) return hipSuccess;
-  TimedLaunch t(timer, gemm_name(g, epi), s);
+  const bool dtl_ok = bf16 && g.K % 64 == 0 && !kForceGeneric;
+  const PartsPlan pp = dtl_ok ? parts_plan(g) : PartsPlan{1, 64};
+  TimedLaunch t(timer, gemm_name(g, epi), s, pp.S > 1);   // the split-K path launches two kernels
   // Kernel choice from the tile count at rows_cap rows (measured on the d=1536
   // shapes).  When those 128x128 tiles fit the 256 CUs in one round, the
   // in-workgroup split-K kernel gives every SIMD two waves without a trip
@@ -1290,7 +1507,6 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   // work-balanced kernel, which splits K over more workgroups, is faster.
   // Otherwise the work-balanced kernel sizes its work from k_eff on the device.
   const long long t128 = static_cast<long long>((g.M + 127) / 128) * ((g.Nout + 127) / 128);
-  const bool dtl_ok = bf16 && g.K % 64 == 0 && !kForceGeneric;
   const bool use_ks2 = dtl_ok && kSplitK && WAMC_GEMM_KS2 && t128 <= 256 && g.K >= 2 * 64 &&
                        (g.K < 4096 || t128 > 128);
   const bool use_sk = dtl_ok && WAMC_GEMM_SK && g.sk_partial && g.sk_counters &&
@@ -1302,7 +1518,18 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   const long long t256 = static_cast<long long>(g.M / g.rows_cap) * ((rows_known + 255) / 256) *
                          ((g.Nout + 255) / 256);
   const bool big = kGemmBig && g.d_model >= 256 && g.sk_partial_bytes >= SkBig::kTileBytes && t256 >= 2 * SkBig::kP;
-  if (!use_ks2 && use_sk && big) {
+  if (pp.S > 1) {
+    GemmArgs gp = g;
+    gp.parts = pp.S;
+    const long long tiles = static_cast<long long>(g.M / g.rows_cap) * ((g.rows_cap + pp.bm - 1) / pp.bm) *
+                            ((g.Nout + kPartsBN - 1) / kPartsBN);
+    const unsigned grid = static_cast<unsigned>(tiles * pp.S);
+    if (pp.bm == 128) launch(gemm_bf16_parts_kernel<128, kPartsBN, kPartsBK, 2, 2, 2>, grid, 256, 0, s, gp);
+    else launch(gemm_bf16_parts_kernel<64, kPartsBN, kPartsBK, 2, 2, 2>, grid, 256, 0, s, gp);
+    const long long groups = static_cast<long long>(g.M) * (g.Nout / 4);
+    const unsigned eg = static_cast<unsigned>(std::min<long long>((groups + 255) / 256, 2048));
+    WAMC_EPI_DISPATCH(epi, (launch(gemm_parts_epilogue_kernel<E>, eg, 256, 0, s, gp)));
+  } else if (!use_ks2 && use_sk && big) {
     launch_sk<256, 256, 32, 4, 2, 4>(epi, g, s);
   } else if (!use_ks2 && use_sk && (epi == EPI_QKV || epi == EPI_GELU) && wide_tiles_pay(g, rows_known)) {
     launch_sk<128, 192, 64, 2, 2, 2>(epi, g, s);

@@ -179,6 +179,7 @@ struct GemmArgs {
   float* sk_partial;        // f32 partial tiles of split output tiles
   size_t sk_partial_bytes;  // its size (bounds the number of pieces)
   int* sk_counters;         // per-tile arrival counters, zero between launches
+  int parts;                // pieces per tile of the split-K path with a separate reduction (set by launch_gemm)
 };
 hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer);
 

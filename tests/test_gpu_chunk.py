@@ -325,21 +325,30 @@ def test_capacity_filled_chunk():
         assert np.array_equal(to_np(eng.idx[0])[:ke], sel)
 
 
-@pytest.mark.parametrize("rows,cols", [(12, 10), (36, 30)])
-def test_small_token_stack(rows, cols):
+@pytest.mark.parametrize("name,rows,cols", [("c3_stack", 12, 10), ("c3_stack", 36, 30), ("c3_text", 12, 10)])
+def test_small_token_stack(name, rows, cols):
     """The small-context regime of the pages' latency experiment (WAM-Cache
     §5.2: the refresh ratio 0.584 of the native 120 visual tokens, here at 120
     and 1080 tokens) on three layers of the d=1536 stack, G = 2, in the
-    launch configuration the small-N benchmark uses (rows_cap = k): three
-    refresh chunks driven by the oracle's refresh sets."""
+    launch configuration the small-N benchmark uses (rows_cap = k): the dense
+    chunk's K/V caches, then three refresh chunks driven by the oracle's
+    refresh sets.  With a few hundred rows the projections take the split-K
+    path with a separate reduction (4 to 16 pieces per 64x128 tile at 70
+    rows, 2 at 1080); with the module's text cross-attention (128 text
+    tokens) its K/V, query and output projections take it too (WAM-Cache §3)."""
     N = rows * cols
     k = int(round(0.584 * N))
-    wl = W.preset("c3_stack", n_layers=3, views=1, rows=rows, cols=cols, k=k, age_bound=2, chunks=4)
+    wl = W.preset(name, n_layers=3, views=1, rows=rows, cols=cols, k=k, age_bound=2, chunks=4)
     r = W.make_rollout(wl, chunks=wl.chunks)
     prec = O.Precision(wl.dtype)
     states = _oracle_states(wl, r, prec)
     eng = engine(wl, r, rows_cap=k)
     eng.dense(batch_z(wl, r, 0))
+    torch.cuda.synchronize()
+    for l in range(wl.n_layers):
+        for nm, g, o in (("K", eng.k_cache[l, 0], states[0].K[l]), ("V", eng.v_cache[l, 0], states[0].V[l])):
+            ok, err = close(wl, to_np(g), o)
+            assert ok, f"dense chunk {nm} layer {l}: error {err}"
     lo = torch.zeros((wl.n_layers, 1, k, wl.d_model), dtype=torch.float32, device=DEV)
     for t in range(1, wl.chunks):
         res = [O.refresh_chunk(states[0], r.z[0][t], r.qa[0][t], r.weights, k, wl.age_bound, wl.n_heads,
