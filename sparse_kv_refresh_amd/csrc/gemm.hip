@@ -833,6 +833,10 @@ __global__ __launch_bounds__(kKs2Threads, 1) void gemm_bf16_dtl_ks2_kernel(GemmA
 #endif
 constexpr int kSkMinIters = WAMC_SK_MIN_ITERS;   // fewest k-tiles per split range
 constexpr int kSkMaxSplit = WAMC_SK_MAX_SPLIT;   // most pieces per tile
+#ifndef WAMC_SK_SLOT_ROUNDS
+#define WAMC_SK_SLOT_ROUNDS 2
+#endif
+constexpr int kSkSlotRounds = WAMC_SK_SLOT_ROUNDS;   // partial-tile slots, in resident workgroups
 #ifndef WAMC_SK_PIECE_COST
 #define WAMC_SK_PIECE_COST 16
 #endif
@@ -937,7 +941,7 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   const int tiles_n = (g.Nout + BN - 1) / BN;
   const int tiles = tiles_m * tiles_n;
   constexpr int P = Cfg::kP;
-  const int slots = static_cast<int>(min(g.sk_partial_bytes / Cfg::kTileBytes, static_cast<size_t>(2 * P)));
+  const int slots = static_cast<int>(min(g.sk_partial_bytes / Cfg::kTileBytes, static_cast<size_t>(kSkSlotRounds * P)));
   const int ndp = (tiles / P) * P;        // tiles done one per workgroup
   const int r = tiles - ndp;              // tail tiles, split along K
   const int nk = g.K / BK;
@@ -1353,10 +1357,10 @@ GemmScratch gemm_scratch(int B, int rows_cap, int d, int F) {
   s.counter_bytes = static_cast<size_t>(s.counters) * sizeof(int);
   // partial tiles: at most two rounds of resident workgroups' worth of pieces
   // (fewer for small shapes: tiles x the most pieces per tile)
-  const size_t small = std::min<size_t>(2 * SkSmall::kP, static_cast<size_t>(s.counters) * kSkMaxSplit) *
+  const size_t small = std::min<size_t>(kSkSlotRounds * SkSmall::kP, static_cast<size_t>(s.counters) * kSkMaxSplit) *
                        SkSmall::kTileBytes;
   const size_t tiles_big = static_cast<size_t>(B) * ((rows_cap + 255) / 256) * ((widest + 255) / 256);
-  const size_t big = kGemmBig ? std::min<size_t>(2 * SkBig::kP, tiles_big * kSkMaxSplit) * SkBig::kTileBytes : 0;
+  const size_t big = kGemmBig ? std::min<size_t>(kSkSlotRounds * SkBig::kP, tiles_big * kSkMaxSplit) * SkBig::kTileBytes : 0;
   s.partial_bytes = std::max(small, big);
   return s;
 }
@@ -1378,7 +1382,7 @@ static void launch_sk(GemmEpi epi, const GemmArgs& g, hipStream_t s) {
   constexpr long long P = Cfg::kP;
   const long long cap = static_cast<long long>(WAMC_SK_GRID_ROUNDS) * P;
   const long long ndp = tiles_cap / P * P, r = tiles_cap - ndp;
-  const long long slots = std::min<long long>(static_cast<long long>(g.sk_partial_bytes / Cfg::kTileBytes), 2 * P);
+  const long long slots = std::min<long long>(static_cast<long long>(g.sk_partial_bytes / Cfg::kTileBytes), kSkSlotRounds * P);
   const long long room = std::max<long long>(std::min(cap - ndp, slots), 0);
   const int nk = g.K / BK;
   const int S = nk >= kSkLongK && r > 0 && r <= room
