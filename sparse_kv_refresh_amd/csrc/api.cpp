@@ -327,10 +327,16 @@ ZeroJob counter_clear(void* ws, const WsLayout& L) {
 // x_out (may alias x_in).
 // rows_lo: a lower bound on every k_eff[b] known on the host (0 when unknown),
 // from which the GEMM tile shape is chosen.
+// h1_ready: the layer's first modulated LayerNorm is already in the h buffer.
+// next_shift1 / next_scale1 (nullable): the next layer's first modulation;
+// when the MLP down projection can produce that LayerNorm in its own pass it
+// does, and *next_h1_ready says so.
 hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_in, float* x_out,
                      const int32_t* idx, const int32_t* k_eff, int32_t rows_cap, int32_t rows_lo, void* kc,
                      void* vc, void* ws, const WsLayout& L, hipStream_t s, bool h1_ready = false,
-                     const ZeroJob& zj = ZeroJob{}) {
+                     const ZeroJob& zj = ZeroJob{}, const void* next_shift1 = nullptr,
+                     const void* next_scale1 = nullptr, bool* next_h1_ready = nullptr) {
+  if (next_h1_ready) *next_h1_ready = false;
   const bool bf16 = d->dtype == WAMC_BF16;
   const size_t es = act_size(d);
   const int D = d->d_model, F = d->d_ffn, B = d->batch;
@@ -383,15 +389,25 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
   e = launch_attention(bf16, at_, s, tm);
   if (e != hipSuccess) return e;
 
+  // The LayerNorm after each residual projection (the text query's plain one,
+  // or adaLN-2) comes from the projection's own pass where its schedule holds
+  // whole rows (ln_done), else from the LayerNorm kernel.
   g.a = hbuf; g.w = w->w_o; g.bias = w->b_o; g.Nout = D; g.K = D;
   g.resid_in = x_in; g.resid_out = x_out; g.gate = gate1;
-  e = launch_gemm(bf16, EPI_RESID_OUT, g, s, tm);
+  g.ln_out = hbuf; g.ln_eps = d->ln_eps;
+  g.ln_shift = d->n_text > 0 ? nullptr : shift2;
+  g.ln_scale = d->n_text > 0 ? nullptr : scale2;
+  bool ln_done = false;
+  e = launch_gemm(bf16, EPI_RESID_OUT, g, s, tm, &ln_done);
+  g.ln_out = nullptr;
   if (e != hipSuccess) return e;
 
   if (d->n_text > 0) {
     // text cross-attention: Qc = LN(x) W_qc^T + b_qc; x += attn(Qc, K_t, V_t) W_oc^T + b_oc
-    e = launch_ln_mod(bf16, x_out, nullptr, nullptr, B, rows_cap, k_eff, D, d->ln_eps, hbuf, ZeroJob{}, s, tm);
-    if (e != hipSuccess) return e;
+    if (!ln_done) {
+      e = launch_ln_mod(bf16, x_out, nullptr, nullptr, B, rows_cap, k_eff, D, d->ln_eps, hbuf, ZeroJob{}, s, tm);
+      if (e != hipSuccess) return e;
+    }
     g.a = hbuf; g.w = w->w_qc; g.bias = w->b_qc; g.Nout = D; g.K = D; g.g_out = qbuf;
     e = launch_gemm(bf16, EPI_STORE, g, s, tm);
     if (e != hipSuccess) return e;
@@ -401,12 +417,16 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
     if (e != hipSuccess) return e;
     g.a = hbuf; g.w = w->w_oc; g.bias = w->b_oc; g.Nout = D; g.K = D;
     g.resid_in = x_out; g.resid_out = x_out; g.gate = nullptr;
-    e = launch_gemm(bf16, EPI_RESID_PLAIN, g, s, tm);
+    g.ln_out = hbuf; g.ln_shift = shift2; g.ln_scale = scale2;
+    e = launch_gemm(bf16, EPI_RESID_PLAIN, g, s, tm, &ln_done);
+    g.ln_out = nullptr;
     if (e != hipSuccess) return e;
   }
 
-  e = launch_ln_mod(bf16, x_out, shift2, scale2, B, rows_cap, k_eff, D, d->ln_eps, hbuf, ZeroJob{}, s, tm);
-  if (e != hipSuccess) return e;
+  if (!ln_done) {
+    e = launch_ln_mod(bf16, x_out, shift2, scale2, B, rows_cap, k_eff, D, d->ln_eps, hbuf, ZeroJob{}, s, tm);
+    if (e != hipSuccess) return e;
+  }
 
   g.a = hbuf; g.w = w->w_1; g.bias = w->b_1; g.Nout = F; g.K = D; g.g_out = gbuf;
   e = launch_gemm(bf16, EPI_GELU, g, s, tm);
@@ -414,7 +434,10 @@ hipError_t run_layer(const wamc_dims* d, const wamc_layer_w* w, const float* x_i
 
   g.a = gbuf; g.w = w->w_2; g.bias = w->b_2; g.Nout = D; g.K = F;
   g.resid_in = x_out; g.resid_out = x_out; g.gate = gate2;
-  return launch_gemm(bf16, EPI_RESID_DOWN, g, s, tm);
+  if (next_shift1) {
+    g.ln_out = hbuf; g.ln_shift = next_shift1; g.ln_scale = next_scale1;
+  }
+  return launch_gemm(bf16, EPI_RESID_DOWN, g, s, tm, next_h1_ready);
 }
 
 // Attention mass (unless supplied) and the per-token P, U partials.
@@ -468,12 +491,16 @@ hipError_t run_refresh_rows(const wamc_dims* dims, const wamc_layer_w* layers, c
     e = launch_gather(bf16, z, zref, idx, k_eff, B, N, D, rows_cap, x, nullptr, counter_clear(ws, L), s, tm);
   const size_t layer_elems = static_cast<size_t>(B) * N * D;
   const size_t out_elems = static_cast<size_t>(B) * rows_cap * D;
+  bool h1 = fuse_ln;
   for (int l = 0; l < dims->n_layers && e == hipSuccess; ++l) {
     const float* xin = (layer_out && l > 0) ? layer_out + (l - 1) * out_elems : x;
     float* xout = layer_out ? layer_out + l * out_elems : x;
     void* kc = static_cast<char*>(k_cache) + l * layer_elems * es;
     void* vc = static_cast<char*>(v_cache) + l * layer_elems * es;
-    e = run_layer(dims, &layers[l], xin, xout, idx, k_eff, rows_cap, rows_lo, kc, vc, ws, L, s, l == 0 && fuse_ln);
+    const bool next = l + 1 < dims->n_layers;
+    e = run_layer(dims, &layers[l], xin, xout, idx, k_eff, rows_cap, rows_lo, kc, vc, ws, L, s, h1, ZeroJob{},
+                  next ? offset(layers[l + 1].mod, 0, es) : nullptr, next ? offset(layers[l + 1].mod, D, es) : nullptr,
+                  &h1);
   }
   return e;
 }
@@ -836,12 +863,16 @@ int wamc_dense_prefill(const wamc_dims* dims, const wamc_layer_w* layers, const 
   else
     e = launch_gather(bf16, z, zref, nullptr, nullptr, B, N, D, N, x, age, counter_clear(ws, L), s, tm);
   const size_t layer_elems = static_cast<size_t>(B) * N * D;
+  bool h1 = fuse_ln;
   for (int l = 0; l < dims->n_layers && e == hipSuccess; ++l) {
     const float* xin = (layer_out && l > 0) ? layer_out + (l - 1) * layer_elems : x;
     float* xout = layer_out ? layer_out + l * layer_elems : x;
     void* kc = static_cast<char*>(k_cache) + l * layer_elems * es;
     void* vc = static_cast<char*>(v_cache) + l * layer_elems * es;
-    e = run_layer(dims, &layers[l], xin, xout, nullptr, nullptr, N, N, kc, vc, ws, L, s, l == 0 && fuse_ln);
+    const bool next = l + 1 < dims->n_layers;
+    e = run_layer(dims, &layers[l], xin, xout, nullptr, nullptr, N, N, kc, vc, ws, L, s, h1, ZeroJob{},
+                  next ? offset(layers[l + 1].mod, 0, es) : nullptr, next ? offset(layers[l + 1].mod, D, es) : nullptr,
+                  &h1);
   }
   return hip_status(fn, e, s);
 }

@@ -28,6 +28,7 @@
 // fp32 workloads).
 #include "common.h"
 #include "launch.h"
+#include "rowops.h"
 
 #include <algorithm>
 
@@ -1241,7 +1242,19 @@ __global__ __launch_bounds__(256) void gemm_parts_epilogue_kernel(GemmArgs g) {
     if (!ri.valid) continue;
     const float* src = g.sk_partial + static_cast<size_t>(m) * g.Nout + c;
     float4 a = *reinterpret_cast<const float4*>(src);
-    for (int p = 1; p < S; ++p) {
+    // planes 1.. in batches of four whose loads are in flight together; the
+    // additions stay in plane order
+    int p = 1;
+    for (; p + 4 <= S; p += 4) {
+      float4 x[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = *reinterpret_cast<const float4*>(src + (p + q) * plane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a.x += x[q].x; a.y += x[q].y; a.z += x[q].z; a.w += x[q].w;
+      }
+    }
+    for (; p < S; ++p) {
       const float4 x = *reinterpret_cast<const float4*>(src + p * plane);
       a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
     }
@@ -1283,6 +1296,80 @@ __global__ __launch_bounds__(256) void gemm_parts_epilogue_kernel(GemmArgs g) {
       }
     }
   }
+}
+
+// The reduction of a residual projection (Nout = d) fused with the
+// LayerNorm that follows it: one wavefront per row (4 rows a block), lane
+// chunks as in the row kernels, so the row's x is bitwise that of the
+// reduction above and its h that of the LayerNorm kernel, and one launch
+// replaces two.
+template <int NC, int EPI, bool MOD>
+__global__ __launch_bounds__(256) void gemm_parts_resid_ln_kernel(GemmArgs g) {
+  static_assert(EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN || EPI == EPI_RESID_PLAIN, "residual epilogues");
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int m = blockIdx.x * 4 + wid;
+  if (m >= g.M || !row_info(g, m).valid) return;
+  const int d = g.Nout, S = g.parts;
+  const size_t plane = static_cast<size_t>(g.M) * d;
+  const float* src = g.sk_partial + static_cast<size_t>(m) * d;
+  float v[NC][4];
+  load_row<NC>(src, d, lane, v);
+  // planes 1.. in pairs whose loads are in flight together, added in plane order
+  int p = 1;
+  for (; p + 2 <= S; p += 2) {
+    float t[2][NC][4];
+    load_row<NC>(src + p * plane, d, lane, t[0]);
+    load_row<NC>(src + (p + 1) * plane, d, lane, t[1]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int j = 0; j < NC; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[j][i] += t[q][j][i];
+  }
+  if (p < S) {
+    float t[NC][4];
+    load_row<NC>(src + p * plane, d, lane, t);
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[j][i] += t[j][i];
+  }
+  float bs[NC][4], gt[NC][4], xin[NC][4];
+  load_row<NC>(static_cast<const bf16_t*>(g.bias), d, lane, bs);
+  if constexpr (EPI != EPI_RESID_PLAIN) {
+    load_row<NC>(static_cast<const bf16_t*>(g.gate), d, lane, gt);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gt[j][i] = 1.0f;
+  }
+  load_row<NC>(g.resid_in + static_cast<size_t>(m) * d, d, lane, xin);
+  RowMod<NC, bf16_t, MOD> md;
+  md.load(static_cast<const bf16_t*>(g.ln_shift), static_cast<const bf16_t*>(g.ln_scale), d, lane);
+  float* xo = g.resid_out + static_cast<size_t>(m) * d;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    if (j * 256 >= d) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[j][i] = fmaf(gt[j][i], v[j][i] + bs[j][i], xin[j][i]);
+    const int c = lane * 4 + j * 256;
+    if (c < d) *reinterpret_cast<float4*>(xo + c) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+  }
+  float mean, rstd;
+  row_stats(v, d, lane, g.ln_eps, mean, rstd);
+  row_norm_store<NC, bf16_t, MOD>(v, d, lane, mean, rstd, md, static_cast<bf16_t*>(g.ln_out) + static_cast<size_t>(m) * d);
+}
+
+template <int EPI>
+static void launch_parts_resid_ln(const GemmArgs& gp, int nc, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>((gp.M + 3) / 4);
+  const bool mod = gp.ln_shift != nullptr;
+  WAMC_ROW_NC_DISPATCH(nc, if constexpr (NC > 0) {
+    if (mod) launch(gemm_parts_resid_ln_kernel<NC, EPI, true>, grid, 256, 0, s, gp);
+    else launch(gemm_parts_resid_ln_kernel<NC, EPI, false>, grid, 256, 0, s, gp);
+  })
 }
 
 // Pieces per tile (S = 1: the path is not taken) and the tile height of the
@@ -1499,7 +1586,8 @@ static bool wide_tiles_pay(const GemmArgs& g, long long rows_known) {
   return g.sk_partial_bytes >= SkConfig<128, 192, 64, 2, 2, 2>::kTileBytes && 3 * r192 < 2 * r128;
 }
 
-hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer) {
+hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer, bool* ln_done) {
+  if (ln_done) *ln_done = false;
   if (g.M <= 0 || g.Nout <= 0) return hipSuccess;
   const bool dtl_ok = bf16 && g.K % 64 == 0 && !kForceGeneric;
   const PartsPlan pp = dtl_ok ? parts_plan(g) : PartsPlan{1, 64};
@@ -1530,9 +1618,18 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
     const unsigned grid = static_cast<unsigned>(tiles * pp.S);
     if (pp.bm == 128) launch(gemm_bf16_parts_kernel<128, kPartsBN, kPartsBK, 2, 2, 2>, grid, 256, 0, s, gp);
     else launch(gemm_bf16_parts_kernel<64, kPartsBN, kPartsBK, 2, 2, 2>, grid, 256, 0, s, gp);
-    const long long groups = static_cast<long long>(g.M) * (g.Nout / 4);
-    const unsigned eg = static_cast<unsigned>(std::min<long long>((groups + 255) / 256, 2048));
-    WAMC_EPI_DISPATCH(epi, (launch(gemm_parts_epilogue_kernel<E>, eg, 256, 0, s, gp)));
+    const bool resid = epi == EPI_RESID_OUT || epi == EPI_RESID_DOWN || epi == EPI_RESID_PLAIN;
+    const int nc = g.Nout == g.d_model ? row_chunks(g.d_model) : 0;
+    if (g.ln_out && resid && nc > 0) {
+      if (epi == EPI_RESID_OUT) launch_parts_resid_ln<EPI_RESID_OUT>(gp, nc, s);
+      else if (epi == EPI_RESID_DOWN) launch_parts_resid_ln<EPI_RESID_DOWN>(gp, nc, s);
+      else launch_parts_resid_ln<EPI_RESID_PLAIN>(gp, nc, s);
+      if (ln_done) *ln_done = true;
+    } else {
+      const long long groups = static_cast<long long>(g.M) * (g.Nout / 4);
+      const unsigned eg = static_cast<unsigned>(std::min<long long>((groups + 255) / 256, 2048));
+      WAMC_EPI_DISPATCH(epi, (launch(gemm_parts_epilogue_kernel<E>, eg, 256, 0, s, gp)));
+    }
   } else if (!use_ks2 && use_sk && big) {
     launch_sk<256, 256, 32, 4, 2, 4>(epi, g, s);
   } else if (!use_ks2 && use_sk && (epi == EPI_QKV || epi == EPI_GELU) && wide_tiles_pay(g, rows_known)) {

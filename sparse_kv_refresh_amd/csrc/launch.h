@@ -180,8 +180,16 @@ struct GemmArgs {
   size_t sk_partial_bytes;  // its size (bounds the number of pieces)
   int* sk_counters;         // per-tile arrival counters, zero between launches
   int parts;                // pieces per tile of the split-K path with a separate reduction (set by launch_gemm)
+  // EPI_RESID_* (optional): the LayerNorm that follows, h = act(LN(out)(1 + scale) + shift) (no
+  // modulation when shift is null), done in the same pass where the schedule holds whole rows
+  void* ln_out;             // [M, d] act; null: no LayerNorm here
+  const void* ln_shift;     // [d] act, nullable
+  const void* ln_scale;     // [d] act
+  float ln_eps;
 };
-hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer);
+// *ln_done (nullable) tells whether the LayerNorm asked for in g.ln_out was done.
+hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer,
+                       bool* ln_done = nullptr);
 
 // Scratch of the work-balanced bf16 GEMM for one layer's four projections.
 struct GemmScratch {
