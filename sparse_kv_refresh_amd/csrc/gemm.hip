@@ -1380,11 +1380,17 @@ static void launch_parts_resid_ln(const GemmArgs& gp, int nc, hipStream_t s) {
 // a few hundred rows on 128-row tiles, which read A and W half as often, beat
 // 64-row ones (1080 rows: 55 against 69 us); with a short K a two-piece split
 // loses to the in-workgroup split-K kernel (QKV at 280 rows: 24 against 20 us),
-// so it takes three pieces or more.
+// so it takes three pieces or more, or two where the reduction also does the
+// LayerNorm that follows (a launch of its own otherwise).
 struct PartsPlan {
   int S, bm;
 };
-static PartsPlan parts_plan(const GemmArgs& g) {
+// whether the split-K reduction of this launch can do the LayerNorm after it
+static bool parts_ln_fuses(GemmEpi epi, const GemmArgs& g) {
+  const bool resid = epi == EPI_RESID_OUT || epi == EPI_RESID_DOWN || epi == EPI_RESID_PLAIN;
+  return resid && g.ln_out != nullptr && g.Nout == g.d_model && row_chunks(g.d_model) > 0;
+}
+static PartsPlan parts_plan(GemmEpi epi, const GemmArgs& g) {
   PartsPlan p{1, 64};
   if (!WAMC_GEMM_PARTS || !g.sk_partial || g.K % kPartsBK != 0 || g.Nout % 4 != 0) return p;
   const int nk = g.K / kPartsBK;
@@ -1396,7 +1402,7 @@ static PartsPlan parts_plan(const GemmArgs& g) {
   long long S = std::min<long long>(kPartsResident / tiles, nk / kPartsMinIters);
   S = std::min<long long>(S, kPartsMaxSplit);
   S = std::min<long long>(S, static_cast<long long>(g.sk_partial_bytes) / plane);
-  p.S = S >= (long_k ? 2 : 3) ? static_cast<int>(S) : 1;
+  p.S = S >= (long_k || parts_ln_fuses(epi, g) ? 2 : 3) ? static_cast<int>(S) : 1;
   return p;
 }
 
@@ -1590,7 +1596,7 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   if (ln_done) *ln_done = false;
   if (g.M <= 0 || g.Nout <= 0) return hipSuccess;
   const bool dtl_ok = bf16 && g.K % 64 == 0 && !kForceGeneric;
-  const PartsPlan pp = dtl_ok ? parts_plan(g) : PartsPlan{1, 64};
+  const PartsPlan pp = dtl_ok ? parts_plan(epi, g) : PartsPlan{1, 64};
   TimedLaunch t(timer, gemm_name(g, epi), s, pp.S > 1);   // the split-K path launches two kernels
   // Kernel choice from the tile count at rows_cap rows (measured on the d=1536
   // shapes).  When those 128x128 tiles fit the 256 CUs in one round, the
@@ -1618,9 +1624,8 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
     const unsigned grid = static_cast<unsigned>(tiles * pp.S);
     if (pp.bm == 128) launch(gemm_bf16_parts_kernel<128, kPartsBN, kPartsBK, 2, 2, 2>, grid, 256, 0, s, gp);
     else launch(gemm_bf16_parts_kernel<64, kPartsBN, kPartsBK, 2, 2, 2>, grid, 256, 0, s, gp);
-    const bool resid = epi == EPI_RESID_OUT || epi == EPI_RESID_DOWN || epi == EPI_RESID_PLAIN;
-    const int nc = g.Nout == g.d_model ? row_chunks(g.d_model) : 0;
-    if (g.ln_out && resid && nc > 0) {
+    if (parts_ln_fuses(epi, g)) {
+      const int nc = row_chunks(g.d_model);
       if (epi == EPI_RESID_OUT) launch_parts_resid_ln<EPI_RESID_OUT>(gp, nc, s);
       else if (epi == EPI_RESID_DOWN) launch_parts_resid_ln<EPI_RESID_DOWN>(gp, nc, s);
       else launch_parts_resid_ln<EPI_RESID_PLAIN>(gp, nc, s);
