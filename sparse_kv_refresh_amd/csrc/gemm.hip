@@ -1379,9 +1379,11 @@ static void launch_parts_resid_ln(const GemmArgs& gp, int nc, hipStream_t s) {
 // 1080 rows: with a long K (the MLP down projection) any split pays, and from
 // a few hundred rows on 128-row tiles, which read A and W half as often, beat
 // 64-row ones (1080 rows: 55 against 69 us); with a short K a two-piece split
-// loses to the in-workgroup split-K kernel (QKV at 280 rows: 24 against 20 us),
-// so it takes three pieces or more, or two where the reduction also does the
-// LayerNorm that follows (a launch of its own otherwise).
+// loses to the in-workgroup split-K kernel (QKV at 280 rows: 24 against 20 us;
+// the long-K down projection at 2458 rows: 94 against 86 us), so wherever that
+// kernel would run the path takes three pieces or more, or two where the
+// reduction also does the LayerNorm that follows (a launch of its own
+// otherwise).
 struct PartsPlan {
   int S, bm;
 };
@@ -1390,7 +1392,7 @@ static bool parts_ln_fuses(GemmEpi epi, const GemmArgs& g) {
   const bool resid = epi == EPI_RESID_OUT || epi == EPI_RESID_DOWN || epi == EPI_RESID_PLAIN;
   return resid && g.ln_out != nullptr && g.Nout == g.d_model && row_chunks(g.d_model) > 0;
 }
-static PartsPlan parts_plan(GemmEpi epi, const GemmArgs& g) {
+static PartsPlan parts_plan(GemmEpi epi, const GemmArgs& g, bool ks2_runs) {
   PartsPlan p{1, 64};
   if (!WAMC_GEMM_PARTS || !g.sk_partial || g.K % kPartsBK != 0 || g.Nout % 4 != 0) return p;
   const int nk = g.K / kPartsBK;
@@ -1402,7 +1404,7 @@ static PartsPlan parts_plan(GemmEpi epi, const GemmArgs& g) {
   long long S = std::min<long long>(kPartsResident / tiles, nk / kPartsMinIters);
   S = std::min<long long>(S, kPartsMaxSplit);
   S = std::min<long long>(S, static_cast<long long>(g.sk_partial_bytes) / plane);
-  p.S = S >= (long_k || parts_ln_fuses(epi, g) ? 2 : 3) ? static_cast<int>(S) : 1;
+  p.S = S >= ((long_k && !ks2_runs) || parts_ln_fuses(epi, g) ? 2 : 3) ? static_cast<int>(S) : 1;
   return p;
 }
 
@@ -1595,18 +1597,19 @@ static bool wide_tiles_pay(const GemmArgs& g, long long rows_known) {
 hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s, KernelTimer* timer, bool* ln_done) {
   if (ln_done) *ln_done = false;
   if (g.M <= 0 || g.Nout <= 0) return hipSuccess;
-  const bool dtl_ok = bf16 && g.K % 64 == 0 && !kForceGeneric;
-  const PartsPlan pp = dtl_ok ? parts_plan(epi, g) : PartsPlan{1, 64};
-  TimedLaunch t(timer, gemm_name(g, epi), s, pp.S > 1);   // the split-K path launches two kernels
   // Kernel choice from the tile count at rows_cap rows (measured on the d=1536
-  // shapes).  When those 128x128 tiles fit the 256 CUs in one round, the
+  // shapes).  With few tiles, the split-K path with a separate reduction
+  // (parts_plan).  When the 128x128 tiles fit the 256 CUs in one round, the
   // in-workgroup split-K kernel gives every SIMD two waves without a trip
   // through memory; with a long K and at most half the CUs' worth of tiles the
   // work-balanced kernel, which splits K over more workgroups, is faster.
   // Otherwise the work-balanced kernel sizes its work from k_eff on the device.
+  const bool dtl_ok = bf16 && g.K % 64 == 0 && !kForceGeneric;
   const long long t128 = static_cast<long long>((g.M + 127) / 128) * ((g.Nout + 127) / 128);
   const bool use_ks2 = dtl_ok && kSplitK && WAMC_GEMM_KS2 && t128 <= 256 && g.K >= 2 * 64 &&
                        (g.K < 4096 || t128 > 128);
+  const PartsPlan pp = dtl_ok ? parts_plan(epi, g, use_ks2) : PartsPlan{1, 64};
+  TimedLaunch t(timer, gemm_name(g, epi), s, pp.S > 1);   // the split-K path launches two kernels
   const bool use_sk = dtl_ok && WAMC_GEMM_SK && g.sk_partial && g.sk_counters &&
                       g.sk_partial_bytes >= SkSmall::kTileBytes;
   // 256-wide tiles need d >= 256 (a QKV tile crosses at most one of the Q|K|V edges).  They are

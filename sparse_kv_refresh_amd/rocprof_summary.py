@@ -27,10 +27,10 @@ import sys
 COPY_BYTES = 1 << 30
 
 KIND_PATTERNS = {
-    "gemm_qkv": r"gemm_bf16_\w*kernel<\(?wamc::GemmEpi\)?0|gemm_bf16_\w*kernel<0",
-    "gemm_out_resid": r"gemm_bf16_\w*kernel<\(?wamc::GemmEpi\)?1|gemm_bf16_\w*kernel<1",
-    "gemm_down_resid": r"gemm_bf16_\w*kernel<\(?wamc::GemmEpi\)?3|gemm_bf16_\w*kernel<3",
-    "gemm_up_gelu": r"gemm_bf16_\w*kernel<\(?wamc::GemmEpi\)?2|gemm_bf16_\w*kernel<2",
+    "gemm_qkv": r"gemm_bf16_\w*kernel<(\(wamc::GemmEpi\))?0[,>]",
+    "gemm_out_resid": r"gemm_bf16_\w*kernel<(\(wamc::GemmEpi\))?1[,>]",
+    "gemm_down_resid": r"gemm_bf16_\w*kernel<(\(wamc::GemmEpi\))?3[,>]",
+    "gemm_up_gelu": r"gemm_bf16_\w*kernel<(\(wamc::GemmEpi\))?2[,>]",
     "attention": "attn_bf16_kernel",
     "score_pass1": "score_pass1_bf16",
     "score_pass2": "score_pass2_bf16",
