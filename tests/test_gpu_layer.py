@@ -95,6 +95,52 @@ def test_refresh_layer_wide(m, spare):
     _check_refresh_layer(W.preset("c2_layer"), m, spare, seed=m)
 
 
+def test_refresh_layer_batch_split():
+    """Three episodes of the d=1536, FFN 8960 layer over N=4096 cached tokens
+    with 37, 100 and 0 refreshed rows (rows_cap = 100, k_eff read on the
+    device): with this few rows the out-projection and the MLP down
+    projection take the split-K path with a separate reduction (4 and 7
+    pieces per 64x128 tile), its tiles derived from each episode's k_eff, and
+    the out-projection's reduction also does adaLN-2.  Every episode against
+    the oracle's block; the empty episode's caches and the rows past k_eff
+    stay untouched (WAM-Cache §4.4)."""
+    wl = W.preset("c2_layer", batch=3)
+    weights = W.make_weights(wl)
+    prec = O.Precision(wl.dtype)
+    N, d, B = wl.n_tokens, wl.d_model, wl.batch
+    rows_cap, ms = 100, [37, 100, 0]
+    rng = np.random.default_rng(11)
+    x = torch.full((B, rows_cap, d), 77.0, dtype=torch.float32, device=DEV)
+    idx_full = np.full((B, N), -1, dtype=np.int32)
+    Kcs, Vcs, wants, Kos, Vos = [], [], [], [], []
+    for e, m in enumerate(ms):
+        idx = np.sort(rng.choice(N, size=m, replace=False)).astype(np.int32)
+        Kc = prec.store(rng.standard_normal((N, d)).astype(np.float32) * 0.5)
+        Vc = prec.store(rng.standard_normal((N, d)).astype(np.float32) * 0.5)
+        X = rng.standard_normal((m, d)).astype(np.float32)
+        Ko, Vo = Kc.astype(prec.acc).copy(), Vc.astype(prec.acc).copy()
+        wants.append(O.block(X.astype(prec.acc), idx, weights[0], Ko, Vo, wl.n_heads, wl.ln_eps, prec) if m else None)
+        Kcs.append(Kc); Vcs.append(Vc); Kos.append(Ko); Vos.append(Vo)
+        x[e, :m] = torch.from_numpy(X).to(DEV)
+        idx_full[e, :m] = idx
+    dims = wamc.dims_for(wl)
+    w = wamc.Engine.upload_weights(weights, act(wl), DEV)[0]
+    kc = to_dev(np.stack(Kcs), act(wl)).contiguous()
+    vc = to_dev(np.stack(Vcs), act(wl)).contiguous()
+    keff = torch.tensor(ms, dtype=torch.int32, device=DEV)
+    ws = torch.empty(wamc.workspace_bytes(dims, rows_cap), dtype=torch.uint8, device=DEV)
+    wamc.refresh_layer(dims, 0, w, x, to_dev(idx_full), keff, rows_cap, kc, vc, ws)
+    torch.cuda.synchronize()
+    for e, m in enumerate(ms):
+        if m:
+            for nm, g, o in (("X", to_np(x[e, :m]), wants[e]), ("K", to_np(kc[e]), Kos[e]), ("V", to_np(vc[e]), Vos[e])):
+                ok, err = close(wl, g, o)
+                assert ok, f"episode {e} {nm}: {err}"
+        else:
+            assert np.array_equal(to_np(kc[e]), Kcs[e]) and np.array_equal(to_np(vc[e]), Vcs[e])
+        assert (x[e, m:] == 77.0).all(), f"episode {e}: rows past k_eff"
+
+
 @pytest.mark.parametrize("n", [33, 65, 130, 257, 1000, 4000, 4095])
 def test_refresh_layer_key_tiles(n):
     """The attention's key-tile paths, on a d=256 layer (two heads of 128)
