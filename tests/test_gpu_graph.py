@@ -15,10 +15,15 @@ from gpu_util import DEV, batch_q, batch_z, engine, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,rule", [("t_bf16_small", "fixed"), ("t_bf16_batch", "fixed"),
-                                       ("t_bf16_small", "union")])
-def test_chunk_graph_replay_bitwise(name, rule):
-    wl = W.preset(name)
+# the d=1536 stack at 120 tokens: its projections take the split-K path with
+# a separate reduction and the fused LayerNorms
+SMALL_STACK = dict(n_layers=2, views=1, rows=12, cols=10, k=70, age_bound=2, chunks=3)
+
+
+@pytest.mark.parametrize("name,rule,over", [("t_bf16_small", "fixed", {}), ("t_bf16_batch", "fixed", {}),
+                                            ("t_bf16_small", "union", {}), ("c3_stack", "fixed", SMALL_STACK)])
+def test_chunk_graph_replay_bitwise(name, rule, over):
+    wl = W.preset(name, **over)
     r = W.make_rollout(wl, chunks=3)
     eng = engine(wl, r)
     L, B, N, d = wl.n_layers, wl.batch, wl.n_tokens, wl.d_model
