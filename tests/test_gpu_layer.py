@@ -95,6 +95,16 @@ def test_refresh_layer_wide(m, spare):
     _check_refresh_layer(W.preset("c2_layer"), m, spare, seed=m)
 
 
+def test_refresh_layer_ragged_columns():
+    """A d=1152 layer (9 heads of 128) with an FFN of 3000 and 40 refreshed
+    rows: the QKV, out- and MLP up projections take the split-K path with
+    three pieces per tile, the up projection's last column tile holding 56 of
+    its 128 columns (3000 = 23 x 128 + 56); the down projection (K = 3000,
+    not a multiple of 64) takes the generic kernel."""
+    wl = W.preset("c2_layer", d_model=1152, n_heads=9, d_ffn=3000, k=40)
+    _check_refresh_layer(wl, wl.k, False, seed=40)
+
+
 def test_refresh_layer_batch_split():
     """Three episodes of the d=1536, FFN 8960 layer over N=4096 cached tokens
     with 37, 100 and 0 refreshed rows (rows_cap = 100, k_eff read on the
