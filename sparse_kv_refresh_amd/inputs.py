@@ -90,6 +90,10 @@ PRESETS: Dict[str, Workload] = {
     # instruction tokens
     "c3_text": Workload("c3_text", 30, 1536, 12, 8960, 3, 30, 52, 64, 2808, 3, "bf16",
                         chunks=16, latent="stack", n_text=128),
+    # the 30-layer stack at the small context of the latency experiment: one
+    # view of 36x30 = 1080 tokens, k = 631 (the 0.584 refresh ratio), G = 2
+    "c3_ctx1080": Workload("c3_ctx1080", 30, 1536, 12, 8960, 1, 36, 30, 64, 631, 2, "bf16",
+                           chunks=16, latent="stack"),
     # 20-layer d=3072 bf16, 2 views x 64x64 = 8192 tokens, 4 episodes, k = 50 %.
     "c5_large": Workload("c5_large", 20, 3072, 24, 12288, 2, 64, 64, 128, 4096, 4, "bf16",
                          batch=4, chunks=8, latent="episodes"),
