@@ -157,11 +157,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_pass1_bf16(
       if (q >= QB) break;
       f32x16_t acc = {};
       const bf16_t* qrow = sq + (q * 32 + col) * kQaStride + half * 64;
+      // the block's query fragments in one batch of LDS reads ahead of the
+      // MFMAs (read one by one, each MFMA waited for its own read)
+      uint4 qf[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const uint4 qf = *reinterpret_cast<const uint4*>(qrow + s * 8);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s]), as_bf16x8(qf), acc, 0, 0, 0);
-      }
+      for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const uint4*>(qrow + s * 8);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s]), as_bf16x8(qf[s]), acc, 0, 0, 0);
       // acc[v]: key kb + (v/4)*8 + half*4 + v%4, query q*32 + col
       float tmax = -INFINITY;
       float sv[16];
@@ -234,11 +238,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_pass2_bf16(
       if (q >= QB) break;
       f32x16_t acc = {};
       const bf16_t* qrow = sq + (q * 32 + col) * kQaStride + half * 64;
+      uint4 qf[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const uint4 qf = *reinterpret_cast<const uint4*>(qrow + s * 8);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qf), as_bf16x8(kf[s]), acc, 0, 0, 0);
-      }
+      for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const uint4*>(qrow + s * 8);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qf[s]), as_bf16x8(kf[s]), acc, 0, 0, 0);
       // acc[v]: query q*32 + (v/4)*8 + half*4 + v%4, key kb + col
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
