@@ -190,9 +190,42 @@ __device__ __forceinline__ void tile_epilogue_staged(const GemmArgs& g, const f3
   constexpr int CPR = BN / EPC;            // chunks per row
   constexpr int PER = SROWS * CPR / NT;    // chunks per thread per step
   static_assert(PER * NT == SROWS * CPR && PER >= 1, "epilogue chunks / threads");
+  // When NT % CPR == 0 a thread's chunks q = tid + p*NT all sit in column
+  // chunk tid % CPR, and its bias and gate are loaded once for the tile;
+  // otherwise per chunk, as it is stored.
+  constexpr bool FIXC = NT % CPR == 0;
   const int tid = threadIdx.x;
-  const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
   const int d = g.d_model;
+  const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
+  auto chunk_cols = [&](int q, int& nc, bool& nok, float (&bsv)[EPC], float (&gt)[4]) {
+    const int n = n0 + (q % CPR) * EPC;
+    nok = n < g.Nout;   // Nout % 8 == 0: a chunk lies wholly inside or outside
+    nc = nok ? n : 0;
+    if constexpr (EPC == 8) {
+      const uint4 bb = *reinterpret_cast<const uint4*>(bias + nc);
+      const uint32_t w[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bsv[2 * e] = __uint_as_float(w[e] << 16);
+        bsv[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    } else {
+      const uint2 bb = *reinterpret_cast<const uint2*>(bias + nc);
+      bsv[0] = __uint_as_float(bb.x << 16); bsv[1] = __uint_as_float(bb.x & 0xffff0000u);
+      bsv[2] = __uint_as_float(bb.y << 16); bsv[3] = __uint_as_float(bb.y & 0xffff0000u);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gt[e] = 1.f;   // EPI_RESID_PLAIN: ungated
+    if constexpr (EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN) {
+      const uint2 gg = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(g.gate) + nc);
+      gt[0] = __uint_as_float(gg.x << 16); gt[1] = __uint_as_float(gg.x & 0xffff0000u);
+      gt[2] = __uint_as_float(gg.y << 16); gt[3] = __uint_as_float(gg.y & 0xffff0000u);
+    }
+  };
+  int nc0 = 0;
+  bool nok0 = false;
+  float bsv0[EPC], gt0[4];
+  if constexpr (FIXC) chunk_cols(tid, nc0, nok0, bsv0, gt0);
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
     // phase 1: raw accumulators of rows wm*WTM + i*32 + col -> staging row wm*32 + col
@@ -206,59 +239,52 @@ __device__ __forceinline__ void tile_epilogue_staged(const GemmArgs& g, const f3
               make_float4(acc[i][j][4 * gg + 0], acc[i][j][4 * gg + 1], acc[i][j][4 * gg + 2], acc[i][j][4 * gg + 3]);
     }
     __syncthreads();
-    // phase 2: chunk q -> staging row sr = q / CPR, columns (q % CPR)*EPC ..
+    // phase 2: chunk q = tid + p*NT -> staging row sr = q / CPR.  Every load
+    // of the step (staged values, row table, residual rows) is issued before
+    // the first store: a store to an output that may alias them would
+    // otherwise hold each chunk's loads behind the previous chunk's store.
     float v[PER][EPC];
-    int rr[PER], nn[PER];
+    int rr[PER], rq[PER];
+    float4 xin[F32OUT ? PER : 1];
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int q = tid + p * NT;
-      const int sr = q / CPR, cc = q % CPR;
-      const int lr = (sr / 32) * WTM + i * 32 + (sr % 32);   // row within the tile
-      nn[p] = n0 + cc * EPC;
-      rr[p] = lr;
-      const float* sp = stage + sr * SSTRIDE + cc * EPC;
+      const int sr = (tid + p * NT) / CPR;
+      rr[p] = (sr / 32) * WTM + i * 32 + (sr % 32);   // row within the tile
+      rq[p] = tab[rr[p]];
+      const float* sp = stage + sr * SSTRIDE + ((tid + p * NT) % CPR) * EPC;
 #pragma unroll
       for (int e = 0; e < EPC; e += 4) {
         const float4 x = *reinterpret_cast<const float4*>(sp + e);
         v[p][e] = x.x; v[p][e + 1] = x.y; v[p][e + 2] = x.z; v[p][e + 3] = x.w;
       }
     }
+    if constexpr (F32OUT) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p)
+        xin[p] = *reinterpret_cast<const float4*>(g.resid_in + static_cast<size_t>(rq[p] < 0 ? 0 : rq[p]) * g.Nout +
+                                                  (FIXC ? nc0 : min(n0 + ((tid + p * NT) % CPR) * EPC, g.Nout - EPC)));
+    }
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int n = nn[p];
-      const bool nok = n < g.Nout;   // Nout % 8 == 0: a chunk lies wholly inside or outside
-      const int nc = nok ? n : 0;
-      const int rq = tab[rr[p]];
-      // bias (and gate) of the chunk's columns, then the element-wise step
-      float bsv[EPC];
-      if constexpr (EPC == 8) {
-        const uint4 bb = *reinterpret_cast<const uint4*>(bias + nc);
-        const uint32_t w[4] = {bb.x, bb.y, bb.z, bb.w};
+      int nc = nc0;
+      bool nok = nok0;
+      float bsv[EPC], gt[4];
+      if constexpr (FIXC) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bsv[2 * e] = __uint_as_float(w[e] << 16);
-          bsv[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-        }
+        for (int e = 0; e < EPC; ++e) bsv[e] = bsv0[e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gt[e] = gt0[e];
       } else {
-        const uint2 bb = *reinterpret_cast<const uint2*>(bias + nc);
-        bsv[0] = __uint_as_float(bb.x << 16); bsv[1] = __uint_as_float(bb.x & 0xffff0000u);
-        bsv[2] = __uint_as_float(bb.y << 16); bsv[3] = __uint_as_float(bb.y & 0xffff0000u);
+        chunk_cols(tid + p * NT, nc, nok, bsv, gt);
       }
       if constexpr (F32OUT) {
-        float gt[4] = {1.f, 1.f, 1.f, 1.f};   // EPI_RESID_PLAIN: ungated
-        if constexpr (EPI != EPI_RESID_PLAIN) {
-          const uint2 gg = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(g.gate) + nc);
-          gt[0] = __uint_as_float(gg.x << 16); gt[1] = __uint_as_float(gg.x & 0xffff0000u);
-          gt[2] = __uint_as_float(gg.y << 16); gt[3] = __uint_as_float(gg.y & 0xffff0000u);
-        }
-        const size_t o = static_cast<size_t>(rq < 0 ? 0 : rq) * g.Nout + nc;
-        const float4 xin = *reinterpret_cast<const float4*>(g.resid_in + o);
         float4 xo;
-        xo.x = fmaf(gt[0], v[p][0] + bsv[0], xin.x);
-        xo.y = fmaf(gt[1], v[p][1] + bsv[1], xin.y);
-        xo.z = fmaf(gt[2], v[p][2] + bsv[2], xin.z);
-        xo.w = fmaf(gt[3], v[p][3] + bsv[3], xin.w);
-        if (rq >= 0 && nok) *reinterpret_cast<float4*>(g.resid_out + o) = xo;
+        xo.x = fmaf(gt[0], v[p][0] + bsv[0], xin[p].x);
+        xo.y = fmaf(gt[1], v[p][1] + bsv[1], xin[p].y);
+        xo.z = fmaf(gt[2], v[p][2] + bsv[2], xin[p].z);
+        xo.w = fmaf(gt[3], v[p][3] + bsv[3], xin[p].w);
+        if (rq[p] >= 0 && nok)
+          *reinterpret_cast<float4*>(g.resid_out + static_cast<size_t>(rq[p]) * g.Nout + nc) = xo;
       } else {
         float y[8];
 #pragma unroll
@@ -275,11 +301,12 @@ __device__ __forceinline__ void tile_epilogue_staged(const GemmArgs& g, const f3
           // a chunk of 8 columns lies in one of Q | K | V (d % 8 == 0)
           const int wr = nc / d, c = nc - wr * d;
           const int which = wr + (EPI == EPI_KV ? 1 : 0);
-          const int r = which == 0 ? rq : tab[BM + rr[p]];
+          const int r = which == 0 ? rq[p] : tab[BM + rr[p]];
           bf16_t* dst = static_cast<bf16_t*>(which == 0 ? g.q_out : (which == 1 ? g.k_cache : g.v_cache));
           if (r >= 0 && nok) *reinterpret_cast<uint4*>(dst + static_cast<size_t>(r) * d + c) = w;
         } else {
-          if (rq >= 0 && nok) *reinterpret_cast<uint4*>(static_cast<bf16_t*>(g.g_out) + static_cast<size_t>(rq) * g.Nout + nc) = w;
+          if (rq[p] >= 0 && nok)
+            *reinterpret_cast<uint4*>(static_cast<bf16_t*>(g.g_out) + static_cast<size_t>(rq[p]) * g.Nout + nc) = w;
         }
       }
     }
@@ -556,6 +583,46 @@ __device__ __forceinline__ void mma_stage(const uint4* as, const uint4* ws, int 
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s & 1][j], af[s & 1][i], acc[i][j], 0, 0, 0);
+  }
+}
+
+// mma_stage with the next tile's loads spread over its first MFMAs: load l
+// (of LOADS) is issued right after MFMA (l * SPREAD) / LOADS.  Issued
+// together after the barrier, a tile's loads hold a wave at its issue for as
+// long as the CU's memory pipeline takes to accept them (about 500 cycles for
+// 32 KB, measured), with no MFMA running; between the MFMAs that time
+// overlaps the matrix work.
+template <int BK, int TI, int TJ, int CPR, int LOADS, int SPREAD, typename Issue>
+__device__ __forceinline__ void mma_stage_il(const uint4* as, const uint4* ws, int ra, int rb, int half,
+                                             f32x16_t (&acc)[TI][TJ], Issue issue_one) {
+  static_assert(SPREAD <= (BK / 16) * TI * TJ, "loads spread over more MFMAs than the stage has");
+  bf16x8_t af[2][TI], bfr[2][TJ];
+  auto load = [&](int s, int b) {
+    const int kc = 2 * s + half;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) af[b][i] = __builtin_bit_cast(bf16x8_t, as[swz<CPR>(ra + 32 * i, kc)]);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) bfr[b][j] = __builtin_bit_cast(bf16x8_t, ws[swz<CPR>(rb + 32 * j, kc)]);
+  };
+  load(0, 0);
+#pragma unroll
+  for (int s = 0; s < BK / 16; ++s) {
+    if (s + 1 < BK / 16) load(s + 1, (s + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s & 1][j], af[s & 1][i], acc[i][j], 0, 0, 0);
+        const int mi = (s * TI + i) * TJ + j;
+#pragma unroll
+        for (int l = 0; l < LOADS; ++l)
+          if ((l * SPREAD) / LOADS == mi) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(l);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
   }
 }
 
@@ -918,6 +985,7 @@ struct SkConfig {
                                                 : 1;
   static constexpr int kP = 256 * kPerCu;
   static constexpr size_t kTileBytes = static_cast<size_t>(BM) * BN * 4;
+  static constexpr bool kIl = BM == 256 && BN == 256 && kThreads == 256 && STAGES == 2;
 };
 
 template <int EPI, int BM, int BN, int BK, int STAGES, int WGM, int WGN>
@@ -935,6 +1003,9 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   constexpr int TI = WTM / 32, TJ = WTN / 32;
   static_assert(LOADS_A * NT == CHUNKS_A && LOADS_B * NT == CHUNKS_B, "tile/threads");
   static_assert(TI * 32 == WTM && TJ * 32 == WTN, "wave tile");
+  // one 4-wave workgroup per CU on 256x256 tiles (128x128 per wave): the next
+  // tile's loads go between the MFMAs of the first half of each stage
+  constexpr bool IL = Cfg::kIl;
 
   const int B = g.M / g.rows_cap;
   int tiles_m = 0;
@@ -943,8 +1014,12 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   const int tiles = tiles_m * tiles_n;
   constexpr int P = Cfg::kP;
   const int slots = static_cast<int>(min(g.sk_partial_bytes / Cfg::kTileBytes, static_cast<size_t>(kSkSlotRounds * P)));
-  const int ndp = (tiles / P) * P;        // tiles done one per workgroup
-  const int r = tiles - ndp;              // tail tiles, split along K
+  // planes (wide tiles only): every tile is cut into g.parts K-pieces that
+  // store raw f32 accumulators to plane [piece][M][Nout]; a second kernel sums
+  // the planes in piece order and applies the epilogue
+  const bool planes = IL && g.parts > 1;
+  const int ndp = planes ? 0 : (tiles / P) * P;   // tiles done one per workgroup
+  const int r = tiles - ndp;                       // tail tiles, split along K
   const int nk = g.K / BK;
   // Work items: the ndp tiles done whole, then the r*S pieces of the split
   // tail.  Workgroup h takes items h, h + G, h + 2G, ... (G = the grid, a
@@ -952,7 +1027,9 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   // belongs to).  The pieces fit the grid's spare workgroups and the partial
   // slots.
   const int G = static_cast<int>(gridDim.x);
-  const int S = sk_split(r, nk, P, min(max(G - ndp, 0), slots));
+  // (the wide tiles' grid of one workgroup per CU leaves room to split a few
+  // dozen short-K tiles, whose partial tiles cost more than the split saves)
+  const int S = planes ? g.parts : IL && nk < kSkLongK ? 1 : sk_split(r, nk, P, min(max(G - ndp, 0), slots));
   const int W = ndp + r * S;
 
   // one LDS object only: a second __shared__ variable makes the compiler wait
@@ -972,28 +1049,40 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
     // this item: tile tl, k-tiles [kk0, kk1); a piece of a split tile when split
     const bool split = w >= ndp && S > 1;
     SkTile tl;
-    int kk0 = 0, kk1 = nk, tt = 0, u = 0;
+    int kk0 = 0, kk1 = nk, tt = 0, u = 0, sp = 0;
     if (w < ndp) {
       tl = sk_tile<BM, BN>(g, xcd_remap(w, ndp), tiles_m, tiles_n);
     } else {
       u = xcd_remap(w - ndp, r * S);
-      tt = u / S;
-      const int sp = u - tt * S;   // split index
+      if (planes) {
+        // consecutive items (one XCD) share a K range and neighbouring tiles' panels
+        sp = u / r;
+        tt = u - sp * r;
+      } else {
+        tt = u / S;
+        sp = u - tt * S;   // split index
+      }
       tl = sk_tile<BM, BN>(g, ndp + tt, tiles_m, tiles_n);
       kk0 = sp * nk / S;
       kk1 = (sp + 1) * nk / S;
     }
 
-    int goff[LOADS];
+    int goff[IL ? 1 : LOADS];
+    if constexpr (!IL) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int il = i < LOADS_A ? i : i - LOADS_A;
-      const int c = (il * NW + wid) * 64 + lane;
-      const int row = c / CPR;
-      const int kc = swz_kc<CPR>(row, c % CPR);
-      if (i < LOADS_A) goff[i] = (min(tl.m0 + row, g.M - 1) - tl.m0) * K + kc * 8 + kk0 * BK;
-      else goff[i] = (min(tl.n0 + row, g.Nout - 1) - tl.n0) * K + kc * 8 + kk0 * BK;
+      for (int i = 0; i < LOADS; ++i) {
+        const int il = i < LOADS_A ? i : i - LOADS_A;
+        const int c = (il * NW + wid) * 64 + lane;
+        const int row = c / CPR;
+        const int kc = swz_kc<CPR>(row, c % CPR);
+        if (i < LOADS_A) goff[i] = (min(tl.m0 + row, g.M - 1) - tl.m0) * K + kc * 8 + kk0 * BK;
+        else goff[i] = (min(tl.n0 + row, g.Nout - 1) - tl.n0) * K + kc * 8 + kk0 * BK;
+      }
     }
+    // IL: load il of thread tid covers tile row r0 + 32 il at element column kcol
+    static_assert(!IL || (CPR == 8 && NT / CPR == 32), "interleaved loads: 32 rows per load");
+    const int r0 = tid / CPR, kcol = swz_kc<CPR>(r0, tid % CPR) * 8;
+    const int mlim = g.M - 1 - tl.m0, nlim = g.Nout - 1 - tl.n0;
     // 64-bit tile bases; the per-thread offsets inside a tile stay 32-bit
     // (at most BM rows of K <= 2^22 elements)
     const bf16_t* At = A + static_cast<size_t>(tl.m0) * K;
@@ -1001,8 +1090,11 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
     auto issue = [&](int kt, int stage) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const bf16_t* src = (i < LOADS_A ? At : Wtt) + goff[i] + kt * BK;
         const int il = i < LOADS_A ? i : i - LOADS_A;
+        int off;
+        if constexpr (IL) off = min(r0 + 32 * il, i < LOADS_A ? mlim : nlim) * K + kcol + (kk0 + kt) * BK;
+        else off = goff[i] + kt * BK;
+        const bf16_t* src = (i < LOADS_A ? At : Wtt) + off;
         uint4* dst = &lds[stage][(i < LOADS_A ? 0 : CHUNKS_A) + (il * NW + wid) * 64];
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
       }
@@ -1020,13 +1112,37 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
 #pragma unroll
     for (int p = 0; p < STAGES - 1; ++p)
       if (p < n) issue(p, p);
-    for (int q = 0; q < n; ++q) {
-      // tile q has landed once at most (tiles issued after it) x LOADS loads remain
-      wait_tiles_ahead<LOADS, STAGES - 2>(min(STAGES - 2, n - 1 - q));
-      __builtin_amdgcn_s_barrier();
-      if (q + STAGES - 1 < n) issue(q + STAGES - 1, (q + STAGES - 1) % STAGES);
-      const uint4* as = lds[q % STAGES];
-      mma_stage<BK, TI, TJ, CPR>(as, as + CHUNKS_A, ra, rb, half, acc);
+    if constexpr (IL) {
+      static_assert(STAGES == 2, "interleaved loads: two stages");
+      for (int q = 0; q < n; ++q) {
+        wait_vmcnt<0>();   // tile q has landed
+        __builtin_amdgcn_s_barrier();
+        // tile q + 1 into the other stage; past the last tile the last one is
+        // read again into the stage no later step reads (no branch among the MFMAs)
+        const int nt = min(q + 1, n - 1), ns = (q + 1) & 1;
+        const uint4* as = lds[q & 1];
+        const int kb = kcol + (kk0 + nt) * BK;
+        mma_stage_il<BK, TI, TJ, CPR, LOADS, (BK / 16) * TI * TJ / 2>(
+            as, as + CHUNKS_A, ra, rb, half, acc, [&](int i) {
+              // rows r0 + 32 il of the tile, clamped to the last valid row; the
+              // swizzle key is the same for every il (32 rows keep (row >> 1) & 7)
+              const int il = i < LOADS_A ? i : i - LOADS_A;
+              const int off = min(r0 + 32 * il, i < LOADS_A ? mlim : nlim) * K + kb;
+              const bf16_t* src = (i < LOADS_A ? At : Wtt) + off;
+              uint4* dst = &lds[ns][(i < LOADS_A ? 0 : CHUNKS_A) + (il * NW + wid) * 64];
+              __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
+            });
+      }
+      wait_vmcnt<0>();   // the last tile's extra loads land before the LDS is used again
+    } else {
+      for (int q = 0; q < n; ++q) {
+        // tile q has landed once at most (tiles issued after it) x LOADS loads remain
+        wait_tiles_ahead<LOADS, STAGES - 2>(min(STAGES - 2, n - 1 - q));
+        __builtin_amdgcn_s_barrier();
+        if (q + STAGES - 1 < n) issue(q + STAGES - 1, (q + STAGES - 1) % STAGES);
+        const uint4* as = lds[q % STAGES];
+        mma_stage<BK, TI, TJ, CPR>(as, as + CHUNKS_A, ra, rb, half, acc);
+      }
     }
 
     auto finish = [&]() {
@@ -1036,12 +1152,36 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
       __syncthreads();
       // staging after the row table, clear of the split flag at the end
       static_assert(2 * BM * 4 + epi_stage_bytes<BM, BN, WTM>() + 16 <= sizeof(lds), "epilogue staging fits the LDS");
-      tile_epilogue<EPI, BM, BN, TI, TJ, WTM, WTN, NT>(
-          g, acc, tl.m0, tl.n0, wm, wn, half, col, tab,
-          reinterpret_cast<float*>(reinterpret_cast<char*>(&lds[0][0]) + 2 * BM * 4), true);
+      float* stage = reinterpret_cast<float*>(reinterpret_cast<char*>(&lds[0][0]) + 2 * BM * 4);
+      if constexpr (IL) {
+        // staged for every epilogue: it stores the accumulators to LDS straight
+        // from their registers, where the direct one needs them all moved to
+        // the vector registers the 128x128 wave tile has no room for
+        tile_epilogue_staged<EPI, BM, BN, TI, TJ, WTM, WTN, NT>(g, acc, tl.n0, wm, wn, half, col, tab, stage, true);
+      } else {
+        tile_epilogue<EPI, BM, BN, TI, TJ, WTM, WTN, NT>(g, acc, tl.m0, tl.n0, wm, wn, half, col, tab, stage, true);
+      }
     };
     if (!split) {
       finish();
+    } else if (planes) {
+      // lane (half, col) of block (i, j) holds row wm*WTM + 32i + col, columns
+      // wn*WTN + 32j + 8gg + 4half + (0..3); valid rows and columns only
+      float* plane = g.sk_partial + static_cast<size_t>(sp) * g.M * g.Nout;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int m = tl.m0 + wm * WTM + 32 * i + col;
+        if (m >= tl.mend) continue;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            const int c = tl.n0 + wn * WTN + 32 * j + 8 * gg + 4 * half;
+            if (c < g.Nout)
+              *reinterpret_cast<float4*>(plane + static_cast<size_t>(m) * g.Nout + c) =
+                  make_float4(acc[i][j][4 * gg], acc[i][j][4 * gg + 1], acc[i][j][4 * gg + 2], acc[i][j][4 * gg + 3]);
+          }
+      }
     } else {
       // Partial tiles live in scratch slot u (piece u of the tail).  They are
       // written and read as relaxed system-scope atomics (sc0 sc1 accesses that go
@@ -1442,6 +1582,24 @@ constexpr bool kGemmBig = WAMC_GEMM_BIG != 0;
 // 2 stages, 2 independent 4-wave workgroups per CU)
 using SkSmall = SkConfig<WAMC_SK_BM, WAMC_SK_BN, WAMC_SK_BK, WAMC_SK_STAGES, WAMC_SK_WGM, WAMC_SK_WGN>;
 using SkBig = SkConfig<256, 256, 32, 4, 2, 4>;
+using SkWide = SkConfig<256, 256, 64, 2, 2, 2>;
+static_assert(SkWide::kIl && SkWide::kP == 256, "one 4-wave workgroup per CU with interleaved loads");
+// The 256x256 tiles run on one 4-wave workgroup per CU (128x128 per wave,
+// loads interleaved with the MFMAs) rather than 8 waves (measured at
+// d = 3072, 16k rows: QKV 916 -> 874 us, out-projection 395 -> 357, MLP up
+// 1289 -> 1211, MLP down 1270 -> 1114; at 2.5-2.8k rows they lose to the
+// 128x128 tiles, except as the pieces of a long-K split, below).
+#ifndef WAMC_GEMM_WIDE4
+#define WAMC_GEMM_WIDE4 1
+#endif
+// Long-K projections with few 256x256 tiles: each tile cut into S K-pieces
+// (S x tiles <= one workgroup per CU) that store f32 planes, reduced in piece
+// order by the split-K path's second kernel, which also does the LayerNorm
+// that follows where it can.  1: where the in-workgroup split-K kernel would
+// not run; 2: also in its place.
+#ifndef WAMC_GEMM_WIDE_PLANES
+#define WAMC_GEMM_WIDE_PLANES 1
+#endif
 
 GemmScratch gemm_scratch(int B, int rows_cap, int d, int F) {
   GemmScratch s{};
@@ -1609,7 +1767,6 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   const bool use_ks2 = dtl_ok && kSplitK && WAMC_GEMM_KS2 && t128 <= 256 && g.K >= 2 * 64 &&
                        (g.K < 4096 || t128 > 128);
   const PartsPlan pp = dtl_ok ? parts_plan(epi, g, use_ks2) : PartsPlan{1, 64};
-  TimedLaunch t(timer, gemm_name(g, epi), s, pp.S > 1);   // the split-K path launches two kernels
   const bool use_sk = dtl_ok && WAMC_GEMM_SK && g.sk_partial && g.sk_counters &&
                       g.sk_partial_bytes >= SkSmall::kTileBytes;
   // 256-wide tiles need d >= 256 (a QKV tile crosses at most one of the Q|K|V edges).  They are
@@ -1619,14 +1776,24 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   const long long t256 = static_cast<long long>(g.M / g.rows_cap) * ((rows_known + 255) / 256) *
                          ((g.Nout + 255) / 256);
   const bool big = kGemmBig && g.d_model >= 256 && g.sk_partial_bytes >= SkBig::kTileBytes && t256 >= 2 * SkBig::kP;
-  if (pp.S > 1) {
-    GemmArgs gp = g;
-    gp.parts = pp.S;
-    const long long tiles = static_cast<long long>(g.M / g.rows_cap) * ((g.rows_cap + pp.bm - 1) / pp.bm) *
-                            ((g.Nout + kPartsBN - 1) / kPartsBN);
-    const unsigned grid = static_cast<unsigned>(tiles * pp.S);
-    if (pp.bm == 128) launch(gemm_bf16_parts_kernel<128, kPartsBN, kPartsBK, 2, 2, 2>, grid, 256, 0, s, gp);
-    else launch(gemm_bf16_parts_kernel<64, kPartsBN, kPartsBK, 2, 2, 2>, grid, 256, 0, s, gp);
+  const bool wide4 = big && WAMC_GEMM_WIDE4;
+  // pieces per 256x256 tile of a long-K projection (1: no such split)
+  int wps = 1;
+  const long long t256_cap = static_cast<long long>(g.M / g.rows_cap) * ((g.rows_cap + 255) / 256) *
+                             ((g.Nout + 255) / 256);
+  if (WAMC_GEMM_WIDE_PLANES && use_sk && pp.S <= 1 && !big && g.d_model >= 256 && g.K / 64 >= kSkLongK &&
+      (!use_ks2 || WAMC_GEMM_WIDE_PLANES >= 2) && t256_cap > 0) {
+    const long long plane = static_cast<long long>(g.M) * g.Nout * 4;
+    long long S = SkWide::kP / t256_cap;
+    S = std::min<long long>(S, (g.K / 64) / kPartsMinIters);
+    S = std::min<long long>(S, kPartsMaxSplit);
+    S = std::min<long long>(S, static_cast<long long>(g.sk_partial_bytes) / plane);
+    if (S >= 2) wps = static_cast<int>(S);
+  }
+  TimedLaunch t(timer, gemm_name(g, epi), s, pp.S > 1 || wps > 1);   // the split-K paths launch two kernels
+  // second kernel of the split-K paths: planes summed in piece order, epilogue
+  // (and the LayerNorm after a residual, where it fuses)
+  auto reduce_parts = [&](const GemmArgs& gp) {
     if (parts_ln_fuses(epi, g)) {
       const int nc = row_chunks(g.d_model);
       if (epi == EPI_RESID_OUT) launch_parts_resid_ln<EPI_RESID_OUT>(gp, nc, s);
@@ -1638,6 +1805,24 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
       const unsigned eg = static_cast<unsigned>(std::min<long long>((groups + 255) / 256, 2048));
       WAMC_EPI_DISPATCH(epi, (launch(gemm_parts_epilogue_kernel<E>, eg, 256, 0, s, gp)));
     }
+  };
+  if (pp.S > 1) {
+    GemmArgs gp = g;
+    gp.parts = pp.S;
+    const long long tiles = static_cast<long long>(g.M / g.rows_cap) * ((g.rows_cap + pp.bm - 1) / pp.bm) *
+                            ((g.Nout + kPartsBN - 1) / kPartsBN);
+    const unsigned grid = static_cast<unsigned>(tiles * pp.S);
+    if (pp.bm == 128) launch(gemm_bf16_parts_kernel<128, kPartsBN, kPartsBK, 2, 2, 2>, grid, 256, 0, s, gp);
+    else launch(gemm_bf16_parts_kernel<64, kPartsBN, kPartsBK, 2, 2, 2>, grid, 256, 0, s, gp);
+    reduce_parts(gp);
+  } else if (wps > 1) {
+    GemmArgs gp = g;
+    gp.parts = wps;
+    const unsigned grid = static_cast<unsigned>((t256_cap * wps + 7) / 8 * 8);
+    WAMC_EPI_DISPATCH(epi, (launch(gemm_bf16_sk_kernel<E, 256, 256, 64, 2, 2, 2>, grid, 256, 0, s, gp)));
+    reduce_parts(gp);
+  } else if (!use_ks2 && use_sk && wide4) {
+    launch_sk<256, 256, 64, 2, 2, 2>(epi, g, s);
   } else if (!use_ks2 && use_sk && big) {
     launch_sk<256, 256, 32, 4, 2, 4>(epi, g, s);
   } else if (!use_ks2 && use_sk && (epi == EPI_QKV || epi == EPI_GELU) && wide_tiles_pay(g, rows_known)) {
