@@ -39,6 +39,15 @@ KIND_PATTERNS = {
     "gather_ln": "gather_ln_kernel",
     "ln_mod": "ln_mod_kernel",
 }
+# Split-K launches of a projection run a second kernel (the reduction of the
+# f32 planes, with the epilogue and, after a residual, the LayerNorm that
+# follows); a launch of the kind is the pair.
+SECOND_PATTERNS = {
+    "gemm_qkv": r"gemm_parts_(resid_ln_kernel<\d+, |epilogue_kernel<)(\(wamc::GemmEpi\))?0[,>]",
+    "gemm_out_resid": r"gemm_parts_(resid_ln_kernel<\d+, |epilogue_kernel<)(\(wamc::GemmEpi\))?1[,>]",
+    "gemm_up_gelu": r"gemm_parts_(resid_ln_kernel<\d+, |epilogue_kernel<)(\(wamc::GemmEpi\))?2[,>]",
+    "gemm_down_resid": r"gemm_parts_(resid_ln_kernel<\d+, |epilogue_kernel<)(\(wamc::GemmEpi\))?3[,>]",
+}
 KERNEL_SOURCE = {"gemm_qkv": "gemm.hip", "gemm_out_resid": "gemm.hip", "gemm_up_gelu": "gemm.hip",
                  "gemm_down_resid": "gemm.hip", "attention": "attention.hip", "score_pass1": "score.hip",
                  "score_pass2": "score.hip", "select": "select.hip", "gather": "rows.hip", "gather_ln": "rows.hip", "ln_mod": "rows.hip"}
@@ -106,8 +115,17 @@ def mfma_summary(db: str, chunks: int, last: int, simds: int, xcds: int):
             continue
         drop = n - (n // chunks) * last
         mean = {c: sum(v[drop:n]) / (n - drop) for c, v in per.items()}
+        launches = n - drop
+        if kind in SECOND_PATTERNS:
+            # the second kernel of a split-K launch, per name (see traffic)
+            for c, table in vals.items():
+                kept = [vs[len(vs) - len(vs) * last // chunks:] for kn, vs in table.items()
+                        if re.search(SECOND_PATTERNS[kind], kn) and len(vs) % chunks == 0]
+                n2 = sum(len(k) for k in kept)
+                if n2:
+                    mean[c] += sum(sum(k) for k in kept) / n2
         busy, mops, active = (mean[c] for c in MFMA_COUNTERS)
-        out[kind] = {"launches": n - drop, "mfma_busy_cycles": busy, "gpu_active_cycles_per_xcd": active / xcds,
+        out[kind] = {"launches": launches, "mfma_busy_cycles": busy, "gpu_active_cycles_per_xcd": active / xcds,
                      "mfma_util": busy / (active / xcds * simds) if active > 0 else None,
                      "bf16_mfma_flops": mops * 512.0, "source_file": KERNEL_SOURCE[kind],
                      "source_sha256_16": source_hash(KERNEL_SOURCE[kind])}
@@ -169,21 +187,47 @@ def main(argv=None):
         rows = kernel_stats_timed(args.db, args.steps, args.warmup) if args.steps > 0 else kernel_stats(args.db)
         for n, c, t, av in rows:
             print(f"{n[:90]:90s} {c:6d} {t:11.1f} {av:9.2f}")
+        # a projection launch that runs a split-K reduction too is the pair
+        pairs = []
+        for kind, pat in KIND_PATTERNS.items():
+            if kind not in SECOND_PATTERNS:
+                continue
+            first = [r for r in rows if re.search(pat, r[0])]
+            second = [r for r in rows if re.search(SECOND_PATTERNS[kind], r[0])]
+            if first and second:
+                calls = sum(r[1] for r in first)
+                pairs.append((kind, calls, sum(r[2] for r in first + second)))
+        if pairs:
+            print()
+            print("per launch of a projection whose split-K reduction is a second kernel (both kernels):")
+            for kind, calls, tot in pairs:
+                print(f"{kind:90s} {calls:6d} {tot:11.1f} {tot / calls:9.2f}")
         return
 
-    pat = KIND_PATTERNS[args.kernel]
+    pats = [KIND_PATTERNS[args.kernel]] + ([SECOND_PATTERNS[args.kernel]] if args.kernel in SECOND_PATTERNS else [])
     res = {}
     for key, db, cname in (("fetch", args.fetch_db, "FETCH_SIZE"), ("write", args.write_db, "WRITE_SIZE")):
         vals = counters(db, cname)
         f = copy_factor(vals, cname)
-        launches = [v for kn, vs in vals.items() if re.search(pat, kn) for v in vs]
-        launches = launches[args.skip_first * args.per_step:]
+        first = [v for kn, vs in vals.items() if re.search(pats[0], kn) for v in vs]
+        total = len(first)
+        launches = first[args.skip_first * args.per_step:]
         launches = launches[args.occurrence::args.per_step]
         if not launches:
-            raise SystemExit(f"no launches of {pat} in {db}")
-        kib = sum(launches) / len(launches)
+            raise SystemExit(f"no launches of {pats[0]} in {db}")
+        kib, n_launch, parts = sum(launches) / len(launches), len(launches), 1
+        if len(pats) > 1:
+            # the second kernel may be one of several (the reduction with the
+            # LayerNorm, or without it after the last layer): each name drops
+            # the warm-up share of its own launches, then the launch-weighted mean
+            frac = args.skip_first * args.per_step / total
+            kept = [vs[round(len(vs) * frac):] for kn, vs in vals.items() if re.search(pats[1], kn)]
+            n2 = sum(len(k) for k in kept)
+            if n2:
+                kib += sum(sum(k) for k in kept) / n2
+                parts += 1
         res[key] = {"raw_kib_per_launch": kib, "copy_factor": f, "bytes_per_launch": kib * 1024.0 * f,
-                    "launches": len(launches)}
+                    "launches": n_launch, "kernels_per_launch": parts}
     src = KERNEL_SOURCE[args.kernel]
     rec = {"kernel": args.kernel, "config": args.config, "counter_runs": res,
            "hbm_bytes_per_launch": res["fetch"]["bytes_per_launch"] + res["write"]["bytes_per_launch"],
