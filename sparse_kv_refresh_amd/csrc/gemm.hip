@@ -92,6 +92,31 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const RowInfo& ri, i
   }
 }
 
+// The Q / K / V output a chunk of columns goes to.  The three pointers pass
+// through an empty asm statement first: a per-thread select between fields of
+// the kernel argument block is otherwise compiled into a per-thread load of
+// the selected field, and every store then waits for that load and, since
+// stores share its counter, for all the stores before it.
+typedef __attribute__((address_space(1))) bf16_t gbf16_t;   // in global memory
+typedef unsigned u32x4_v __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) u32x4_v gu32x4_t;
+typedef __attribute__((address_space(1))) u32x2_v gu32x2_t;
+struct QkvDst {
+  gbf16_t *q, *k, *v;
+};
+__device__ __forceinline__ QkvDst qkv_dst(const GemmArgs& g) {
+  // typed as global pointers, so the stores stay global (not flat) stores
+  gbf16_t* q = (gbf16_t*)g.q_out;
+  gbf16_t* k = (gbf16_t*)g.k_cache;
+  gbf16_t* v = (gbf16_t*)g.v_cache;
+  asm("" : "+s"(q), "+s"(k), "+s"(v));
+  return {q, k, v};
+}
+__device__ __forceinline__ gbf16_t* qkv_pick(const QkvDst& p, int which) {
+  return which == 0 ? p.q : (which == 1 ? p.k : p.v);
+}
+
 // true when no row of [m0, m0 + rows) is valid (the whole tile can exit)
 __device__ __forceinline__ bool tile_empty(const GemmArgs& g, int m0, int rows) {
   if (m0 >= g.M) return true;
@@ -197,6 +222,7 @@ __device__ __forceinline__ void tile_epilogue_staged(const GemmArgs& g, const f3
   const int tid = threadIdx.x;
   const int d = g.d_model;
   const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
+  const QkvDst qd = qkv_dst(g);
   auto chunk_cols = [&](int q, int& nc, bool& nok, float (&bsv)[EPC], float (&gt)[4]) {
     const int n = n0 + (q % CPR) * EPC;
     nok = n < g.Nout;   // Nout % 8 == 0: a chunk lies wholly inside or outside
@@ -302,8 +328,8 @@ __device__ __forceinline__ void tile_epilogue_staged(const GemmArgs& g, const f3
           const int wr = nc / d, c = nc - wr * d;
           const int which = wr + (EPI == EPI_KV ? 1 : 0);
           const int r = which == 0 ? rq[p] : tab[BM + rr[p]];
-          bf16_t* dst = static_cast<bf16_t*>(which == 0 ? g.q_out : (which == 1 ? g.k_cache : g.v_cache));
-          if (r >= 0 && nok) *reinterpret_cast<uint4*>(dst + static_cast<size_t>(r) * d + c) = w;
+          gbf16_t* dst = qkv_pick(qd, which);
+          if (r >= 0 && nok) *reinterpret_cast<gu32x4_t*>(dst + static_cast<size_t>(r) * d + c) = __builtin_bit_cast(u32x4_v, w);
         } else {
           if (rq[p] >= 0 && nok)
             *reinterpret_cast<uint4*>(static_cast<bf16_t*>(g.g_out) + static_cast<size_t>(rq[p]) * g.Nout + nc) = w;
@@ -326,6 +352,7 @@ __device__ __forceinline__ void tile_epilogue_direct(const GemmArgs& g, const f3
   // loads are in flight together instead of one round trip per group.
   constexpr int NG = TJ * 4;
   const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
+  const QkvDst qd = qkv_dst(g);
   int ncol[NG];
   bool nok[NG];
   uint2 bb[NG];
@@ -372,8 +399,8 @@ __device__ __forceinline__ void tile_epilogue_direct(const GemmArgs& g, const f3
         uint2 w;
         w.x = pack_bf16x2(biased(i, jg, 0), biased(i, jg, 1));
         w.y = pack_bf16x2(biased(i, jg, 2), biased(i, jg, 3));
-        bf16_t* dst = static_cast<bf16_t*>(which == 0 ? g.q_out : (which == 1 ? g.k_cache : g.v_cache));
-        if (r >= 0 && nok[jg]) *reinterpret_cast<uint2*>(dst + static_cast<size_t>(r) * d + c) = w;
+        gbf16_t* dst = qkv_pick(qd, which);
+        if (r >= 0 && nok[jg]) *reinterpret_cast<gu32x2_t*>(dst + static_cast<size_t>(r) * d + c) = __builtin_bit_cast(u32x2_v, w);
       }
     } else if constexpr (EPI == EPI_RESID_OUT || EPI == EPI_RESID_DOWN || EPI == EPI_RESID_PLAIN) {
       const size_t rbase = static_cast<size_t>(rq < 0 ? 0 : rq) * g.Nout;
@@ -624,6 +651,49 @@ __device__ __forceinline__ void mma_stage_il(const uint4* as, const uint4* ws, i
           }
       }
   }
+}
+
+// One k-step of a wave's TI x TJ block of 32x32 tiles (fragments af, bfr)
+// with the next step's TI + TJ fragment reads and NL tile loads placed
+// between its MFMAs.  With a 128x128 wave tile (16 MFMAs a step) read r
+// follows MFMA r, so the reads go out in the first half of the step and land
+// under the second; with fewer MFMAs all reads follow the first MFMA.  Load l
+// follows MFMA (l * MFMAs) / NL + (MFMAs / NL - 1), i.e. the last MFMA of its
+// share.  The scheduling fences keep that order: the
+// compiler waits for every outstanding LDS read once a direct-to-LDS load is
+// in flight, so a read issued just before an MFMA that needs an older one
+// would be waited for too.
+template <int TI, int TJ, int NL, typename Read, typename Load>
+__device__ __forceinline__ void mma_step_pipe(const bf16x8_t (&af)[TI], const bf16x8_t (&bfr)[TJ],
+                                              f32x16_t (&acc)[TI][TJ], Read read_one, Load load_one) {
+  constexpr int NR = TI + TJ, MF = TI * TJ;
+  constexpr bool SPREAD_READS = MF >= 2 * NR;
+  static_assert(NL <= 2 * MF, "loads fit between the step's MFMAs");
+  constexpr int LOFF = NL > 0 && MF / NL > 1 ? MF / NL - 1 : 0;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int mi = i * TJ + j;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (SPREAD_READS) {
+        if (mi < NR) {
+          read_one(mi);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else if (mi == 0) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_one(r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int l = 0; l < NL; ++l)
+        if ((l * MF) / NL + LOFF == mi) {
+          load_one(l);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
 }
 
 template <int EPI, int BM, int BN, int BK, int STAGES>
@@ -974,6 +1044,18 @@ __device__ __forceinline__ SkTile sk_tile(const GemmArgs& g, int t, int tiles_m,
 #ifndef WAMC_SK_GRID_ROUNDS
 #define WAMC_SK_GRID_ROUNDS 3
 #endif
+// 256x256 tiles: 1 = fragment reads pipelined one k-step ahead across the
+// barrier (mma_step_pipe); 0 = two k-steps' reads after each barrier
+#ifndef WAMC_SK_IL_PIPE
+#define WAMC_SK_IL_PIPE 1
+#endif
+constexpr bool kIlPipe = WAMC_SK_IL_PIPE != 0;
+// the same loop for the 4-wave 128-row tiles of the work-balanced kernel
+#ifndef WAMC_SK_PIPE
+#define WAMC_SK_PIPE 0
+#endif
+constexpr bool kSkPipe = WAMC_SK_PIPE != 0;
+
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
 struct SkConfig {
   static constexpr int kThreads = 64 * WGM * WGN;
@@ -1006,6 +1088,8 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   // one 4-wave workgroup per CU on 256x256 tiles (128x128 per wave): the next
   // tile's loads go between the MFMAs of the first half of each stage
   constexpr bool IL = Cfg::kIl;
+  // the cross-barrier pipelined loop (256x256 tiles; 128x128 and 128x192 as a build option)
+  constexpr bool PIPE = IL ? kIlPipe : (kSkPipe && STAGES == 2 && BK == 64 && NT == 256);
 
   const int B = g.M / g.rows_cap;
   int tiles_m = 0;
@@ -1112,7 +1196,85 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
 #pragma unroll
     for (int p = 0; p < STAGES - 1; ++p)
       if (p < n) issue(p, p);
-    if constexpr (IL) {
+    if constexpr (PIPE) {
+      // Fragment reads one k-step ahead of the MFMAs, across the barrier.
+      // Per tile q (stage q&1): steps 0-2 each read the next step's fragments
+      // between their MFMAs; then every wave waits for its loads of tile q+1
+      // and its last reads of stage q&1, and one barrier makes both hold for
+      // the workgroup; step 3 then reads step 0 of tile q+1 from the other
+      // stage and starts tile q+2's loads into stage q&1.  The 256x256 tiles
+      // send a tile's loads out in two halves, during step 3 of the tile
+      // before and step 0 of their own, three to four k-steps before the
+      // barrier that needs them, with clamped tile indices past the last tile
+      // (the last tile loaded again into a stage no later step reads: no
+      // branch among the MFMAs); the 128x128 tiles send all of them during
+      // step 3, four k-steps ahead.
+      static_assert(STAGES == 2 && BK / 16 == 4 && LOADS % 2 == 0, "pipelined loop: two stages of four k-steps");
+      constexpr int LH = IL ? LOADS / 2 : LOADS;   // loads per issue window
+      bf16x8_t af0[TI], bf0[TJ], af1[TI], bf1[TJ];
+      // read r of step s (stage `st`) into (naf, nbf), in the order the MFMAs use them
+      auto reader = [&](bf16x8_t(&naf)[TI], bf16x8_t(&nbf)[TJ], const uint4* st, int s) {
+        const uint4* wst = st + CHUNKS_A;
+        const int kc = 2 * s + half;
+        return [&naf, &nbf, st, wst, kc, ra, rb](int r) {
+          if (r == 0) naf[0] = __builtin_bit_cast(bf16x8_t, st[swz<CPR>(ra, kc)]);
+          else if (r <= TJ) nbf[r - 1] = __builtin_bit_cast(bf16x8_t, wst[swz<CPR>(rb + 32 * (r - 1), kc)]);
+          else naf[r - TJ] = __builtin_bit_cast(bf16x8_t, st[swz<CPR>(ra + 32 * (r - TJ), kc)]);
+        };
+      };
+      // load l of window h of tile `tile` into stage `stage`
+      auto loader = [&](int tile, int stage, int h) {
+        const int kb = kcol + (kk0 + tile) * BK;
+        return [&, kb, tile, stage, h](int l) {
+          const int i = h * LH + l;
+          const int il = i < LOADS_A ? i : i - LOADS_A;
+          int off;
+          // IL: rows r0 + 32 il of the tile, clamped to the last valid row
+          // (the swizzle key is the same for every il: 32 rows keep (row >> 1) & 7)
+          if constexpr (IL) off = min(r0 + 32 * il, i < LOADS_A ? mlim : nlim) * K + kb;
+          else off = goff[i] + tile * BK;
+          const bf16_t* src = (i < LOADS_A ? At : Wtt) + off;
+          uint4* dst = &lds[stage][(i < LOADS_A ? 0 : CHUNKS_A) + (il * NW + wid) * 64];
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)(dst), 16, 0, 0);
+        };
+      };
+      auto no_load = [](int) {};
+      if (n > 0) {
+        wait_vmcnt<0>();   // tile 0 has landed
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          auto rd = reader(af0, bf0, lds[0], 0);
+#pragma unroll
+          for (int r = 0; r < TI + TJ; ++r) rd(r);
+          if (IL || n > 1) {
+            auto ld = loader(min(1, n - 1), 1, 0);
+#pragma unroll
+            for (int l = 0; l < LH; ++l) ld(l);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < n; ++q) {
+          const uint4* cur = lds[q & 1];
+          const uint4* nxt = lds[(q + 1) & 1];
+          if constexpr (IL)
+            mma_step_pipe<TI, TJ, LH>(af0, bf0, acc, reader(af1, bf1, cur, 1),
+                                      loader(min(q + 1, n - 1), (q + 1) & 1, 1));
+          else
+            mma_step_pipe<TI, TJ, 0>(af0, bf0, acc, reader(af1, bf1, cur, 1), no_load);
+          mma_step_pipe<TI, TJ, 0>(af1, bf1, acc, reader(af0, bf0, cur, 2), no_load);
+          mma_step_pipe<TI, TJ, 0>(af0, bf0, acc, reader(af1, bf1, cur, 3), no_load);
+          __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile q+1 and reads of stage q&1 are done
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          if (IL || q + 2 < n)
+            mma_step_pipe<TI, TJ, LH>(af1, bf1, acc, reader(af0, bf0, nxt, 0), loader(min(q + 2, n - 1), q & 1, 0));
+          else
+            mma_step_pipe<TI, TJ, 0>(af1, bf1, acc, reader(af0, bf0, nxt, 0), no_load);
+        }
+      }
+      wait_vmcnt<0>();   // the trailing loads land before the LDS is used again
+    } else if constexpr (IL) {
       static_assert(STAGES == 2, "interleaved loads: two stages");
       for (int q = 0; q < n; ++q) {
         wait_vmcnt<0>();   // tile q has landed
@@ -1375,6 +1537,7 @@ __global__ __launch_bounds__(256) void gemm_parts_epilogue_kernel(GemmArgs g) {
   const long long total = static_cast<long long>(g.M) * groups;
   const size_t plane = static_cast<size_t>(g.M) * g.Nout;
   const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
+  const QkvDst qd = qkv_dst(g);
   for (long long q = blockIdx.x * 256LL + threadIdx.x; q < total; q += static_cast<long long>(gridDim.x) * 256) {
     const int m = static_cast<int>(q / groups);
     const int c = static_cast<int>(q - static_cast<long long>(m) * groups) * 4;
@@ -1429,8 +1592,8 @@ __global__ __launch_bounds__(256) void gemm_parts_epilogue_kernel(GemmArgs g) {
           const int tok = g.idx ? g.idx[static_cast<size_t>(ri.b) * g.n_tokens + ri.r] : ri.r;
           r = (tok >= 0 && tok < g.n_tokens) ? ri.b * g.n_tokens + tok : -1;
         }
-        bf16_t* dst = static_cast<bf16_t*>(which == 0 ? g.q_out : (which == 1 ? g.k_cache : g.v_cache));
-        if (r >= 0) *reinterpret_cast<uint2*>(dst + static_cast<size_t>(r) * d + cc) = w;
+        gbf16_t* dst = qkv_pick(qd, which);
+        if (r >= 0) *reinterpret_cast<gu32x2_t*>(dst + static_cast<size_t>(r) * d + cc) = __builtin_bit_cast(u32x2_v, w);
       } else {
         *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.g_out) + static_cast<size_t>(m) * g.Nout + c) = w;
       }
@@ -1599,6 +1762,11 @@ static_assert(SkWide::kIl && SkWide::kP == 256, "one 4-wave workgroup per CU wit
 // not run; 2: also in its place.
 #ifndef WAMC_GEMM_WIDE_PLANES
 #define WAMC_GEMM_WIDE_PLANES 1
+#endif
+// QKV and MLP-up projections with at least this many 256x256 tiles (over the
+// rows known to be valid) also take them; 0: only from two full rounds on
+#ifndef WAMC_WIDE_MIN_TILES
+#define WAMC_WIDE_MIN_TILES 0
 #endif
 
 GemmScratch gemm_scratch(int B, int rows_cap, int d, int F) {
@@ -1776,7 +1944,9 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   const long long t256 = static_cast<long long>(g.M / g.rows_cap) * ((rows_known + 255) / 256) *
                          ((g.Nout + 255) / 256);
   const bool big = kGemmBig && g.d_model >= 256 && g.sk_partial_bytes >= SkBig::kTileBytes && t256 >= 2 * SkBig::kP;
-  const bool wide4 = big && WAMC_GEMM_WIDE4;
+  const bool wide_few = WAMC_WIDE_MIN_TILES > 0 && g.d_model >= 256 && g.sk_partial_bytes >= SkWide::kTileBytes &&
+                        t256 >= WAMC_WIDE_MIN_TILES && (epi == EPI_QKV || epi == EPI_GELU);
+  const bool wide4 = (big || wide_few) && WAMC_GEMM_WIDE4;
   // pieces per 256x256 tile of a long-K projection (1: no such split)
   int wps = 1;
   const long long t256_cap = static_cast<long long>(g.M / g.rows_cap) * ((g.rows_cap + 255) / 256) *
