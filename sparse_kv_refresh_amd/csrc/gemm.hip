@@ -1763,6 +1763,11 @@ static_assert(SkWide::kIl && SkWide::kP == 256, "one 4-wave workgroup per CU wit
 #ifndef WAMC_GEMM_WIDE_PLANES
 #define WAMC_GEMM_WIDE_PLANES 1
 #endif
+// Short-K residual projections whose plane reduction also does the LayerNorm
+// that follows (the out-projection and adaLN-2) take the same split
+#ifndef WAMC_WIDE_PLANES_LN
+#define WAMC_WIDE_PLANES_LN 0
+#endif
 // QKV and MLP-up projections with at least this many 256x256 tiles (over the
 // rows known to be valid) also take them; 0: only from two full rounds on
 #ifndef WAMC_WIDE_MIN_TILES
@@ -1951,7 +1956,9 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   int wps = 1;
   const long long t256_cap = static_cast<long long>(g.M / g.rows_cap) * ((g.rows_cap + 255) / 256) *
                              ((g.Nout + 255) / 256);
-  if (WAMC_GEMM_WIDE_PLANES && use_sk && pp.S <= 1 && !big && g.d_model >= 256 && g.K / 64 >= kSkLongK &&
+  // (a long K, or a residual projection whose reduction also runs the LayerNorm that follows)
+  const bool planes_pay = g.K / 64 >= kSkLongK || (WAMC_WIDE_PLANES_LN && parts_ln_fuses(epi, g));
+  if (WAMC_GEMM_WIDE_PLANES && use_sk && pp.S <= 1 && !big && g.d_model >= 256 && planes_pay &&
       (!use_ks2 || WAMC_GEMM_WIDE_PLANES >= 2) && t256_cap > 0) {
     const long long plane = static_cast<long long>(g.M) * g.Nout * 4;
     long long S = SkWide::kP / t256_cap;
