@@ -102,6 +102,8 @@ typedef unsigned u32x4_v __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) u32x4_v gu32x4_t;
 typedef __attribute__((address_space(1))) u32x2_v gu32x2_t;
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) f32x4_v gf32x4_t;
 struct QkvDst {
   gbf16_t *q, *k, *v;
 };
@@ -1330,19 +1332,32 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
       // lane (half, col) of block (i, j) holds row wm*WTM + 32i + col, columns
       // wn*WTN + 32j + 8gg + 4half + (0..3); valid rows and columns only
       float* plane = g.sk_partial + static_cast<size_t>(sp) * g.M * g.Nout;
+      // The row and column checks are all taken before the first store and
+      // kept in two registers: the kernel runs at its register limit, and a
+      // bound reloaded from the spill area between the row blocks waited
+      // (vmcnt) for every store issued before it.
+      const int m0r = tl.m0 + wm * WTM + col, c0 = tl.n0 + wn * WTN + 4 * half;
+      static_assert(TI + 4 * TJ <= 32, "row and column checks fit one register");
+      unsigned ok = 0;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) ok |= (m0r + 32 * i < tl.mend ? 1u : 0u) << i;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) ok |= (c0 + 32 * j + 8 * gg < g.Nout ? 1u : 0u) << (TI + j * 4 + gg);
+      // (a global pointer: through the asm statement a generic one would turn the stores into flat ones)
+      gf32x4_t* prow = (gf32x4_t*)(plane + static_cast<size_t>(m0r) * g.Nout + c0);
+      asm volatile("" : "+v"(ok), "+v"(prow));
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const int m = tl.m0 + wm * WTM + 32 * i + col;
-        if (m >= tl.mend) continue;
+        if (!((ok >> i) & 1u)) continue;
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            const int c = tl.n0 + wn * WTN + 32 * j + 8 * gg + 4 * half;
-            if (c < g.Nout)
-              *reinterpret_cast<float4*>(plane + static_cast<size_t>(m) * g.Nout + c) =
-                  make_float4(acc[i][j][4 * gg], acc[i][j][4 * gg + 1], acc[i][j][4 * gg + 2], acc[i][j][4 * gg + 3]);
-          }
+          for (int gg = 0; gg < 4; ++gg)
+            if ((ok >> (TI + j * 4 + gg)) & 1u)
+              prow[(static_cast<size_t>(32 * i) * g.Nout + 32 * j + 8 * gg) / 4] =
+                  f32x4_v{acc[i][j][4 * gg], acc[i][j][4 * gg + 1], acc[i][j][4 * gg + 2], acc[i][j][4 * gg + 3]};
       }
     } else {
       // Partial tiles live in scratch slot u (piece u of the tail).  They are
