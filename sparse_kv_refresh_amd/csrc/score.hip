@@ -26,8 +26,9 @@
 // sustain at HBM speed.  Pass 1 uses S^T = K Q^T so each lane owns one query
 // and reduces its keys in registers; pass 2 uses S = Q K^T so each lane owns
 // one key and reduces its queries in registers.  K fragments are loaded
-// straight from HBM into registers (each lane walks a contiguous 128-byte
-// half row); the action queries of one (layer, head) sit in LDS.
+// straight from HBM into registers (32 bytes of each key row per load
+// instruction, the row's two lane halves side by side); the action queries
+// of one (layer, head) sit in LDS.
 #include "common.h"
 #include "launch.h"
 
@@ -53,12 +54,19 @@ constexpr int kQaStride = kScoreDh + 8;   // LDS row stride (bf16), breaks bank 
 constexpr int kMaxQB = 4;                 // A <= 128
 
 // Fragment slot convention (shared by both MFMA operands, so any fixed
-// bijection is valid): lane half h, k-step s, slot j <-> dh = h*64 + s*8 + j.
+// bijection is valid): lane half h, k-step s, slot j <-> dh = FRAG_DH(h, s) + j.
+#ifndef WAMC_SCORE_PAIRED
+#define WAMC_SCORE_PAIRED 1
+#endif
+// 1: dh = s*16 + h*8, so the two lanes of a key read 32 contiguous bytes per
+// load instruction (32 cache lines per instruction); 0: dh = h*64 + s*8,
+// each lane walking its own 128-byte half row (64 lines per instruction)
+__device__ __forceinline__ int frag_dh(int h, int s) { return WAMC_SCORE_PAIRED ? s * 16 + h * 8 : h * 64 + s * 8; }
 __device__ __forceinline__ void load_k_frags(const bf16_t* __restrict__ krow, bool valid, int h,
                                              uint4 (&f)[8]) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    f[s] = valid ? *reinterpret_cast<const uint4*>(krow + h * 64 + s * 8) : make_uint4(0, 0, 0, 0);
+    f[s] = valid ? *reinterpret_cast<const uint4*>(krow + frag_dh(h, s)) : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -156,12 +164,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_pass1_bf16(
     for (int q = 0; q < kMaxQB; ++q) {
       if (q >= QB) break;
       f32x16_t acc = {};
-      const bf16_t* qrow = sq + (q * 32 + col) * kQaStride + half * 64;
+      const bf16_t* qrow = sq + (q * 32 + col) * kQaStride;
       // the block's query fragments in one batch of LDS reads ahead of the
       // MFMAs (read one by one, each MFMA waited for its own read)
       uint4 qf[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const uint4*>(qrow + s * 8);
+      for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const uint4*>(qrow + frag_dh(half, s));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 8; ++s)
@@ -237,10 +245,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_pass2_bf16(
     for (int q = 0; q < kMaxQB; ++q) {
       if (q >= QB) break;
       f32x16_t acc = {};
-      const bf16_t* qrow = sq + (q * 32 + col) * kQaStride + half * 64;
+      const bf16_t* qrow = sq + (q * 32 + col) * kQaStride;
       uint4 qf[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const uint4*>(qrow + s * 8);
+      for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const uint4*>(qrow + frag_dh(half, s));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 8; ++s)
