@@ -1010,6 +1010,19 @@ __host__ __device__ inline int sk_split(int r, int nk, int P, int room) {
   return S;
 }
 
+// Pieces per 256x256 tile of the plane split when the host leaves the count
+// to the device (g.parts = -Smax): as many as keep the pieces within one
+// workgroup per CU for the tiles of the k_eff rows, at most Smax.  The
+// pieces kernel and the reduction both derive it from the same k_eff.
+__device__ __forceinline__ int planes_split(const GemmArgs& g) {
+  if (g.parts > 0) return g.parts;
+  const int B = g.M / g.rows_cap;
+  int tm = 0;
+  for (int b = 0; b < B; ++b) tm += (rows_of(g.k_eff, b, g.rows_cap) + 255) / 256;
+  const int tiles = tm * ((g.Nout + 255) / 256);
+  return tiles > 0 ? max(1, min(-g.parts, 256 / tiles)) : 1;
+}
+
 struct SkTile {
   int m0, mend, n0;   // first row, end of the episode's valid rows, first column
 };
@@ -1103,7 +1116,7 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   // planes (wide tiles only): every tile is cut into g.parts K-pieces that
   // store raw f32 accumulators to plane [piece][M][Nout]; a second kernel sums
   // the planes in piece order and applies the epilogue
-  const bool planes = IL && g.parts > 1;
+  const bool planes = IL && (g.parts > 1 || g.parts < 0);
   const int ndp = planes ? 0 : (tiles / P) * P;   // tiles done one per workgroup
   const int r = tiles - ndp;                       // tail tiles, split along K
   const int nk = g.K / BK;
@@ -1115,7 +1128,7 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   const int G = static_cast<int>(gridDim.x);
   // (the wide tiles' grid of one workgroup per CU leaves room to split a few
   // dozen short-K tiles, whose partial tiles cost more than the split saves)
-  const int S = planes ? g.parts : IL && nk < kSkLongK ? 1 : sk_split(r, nk, P, min(max(G - ndp, 0), slots));
+  const int S = planes ? planes_split(g) : IL && nk < kSkLongK ? 1 : sk_split(r, nk, P, min(max(G - ndp, 0), slots));
   const int W = ndp + r * S;
 
   // one LDS object only: a second __shared__ variable makes the compiler wait
@@ -1547,7 +1560,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_parts_kernel(Gemm
 // thread (Nout % 4 == 0, so a group lies in one of Q | K | V).
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_parts_epilogue_kernel(GemmArgs g) {
-  const int S = g.parts;
+  const int S = planes_split(g);
   const int groups = g.Nout / 4;
   const long long total = static_cast<long long>(g.M) * groups;
   const size_t plane = static_cast<size_t>(g.M) * g.Nout;
@@ -1627,7 +1640,7 @@ __global__ __launch_bounds__(256) void gemm_parts_resid_ln_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int m = blockIdx.x * 4 + wid;
   if (m >= g.M || !row_info(g, m).valid) return;
-  const int d = g.Nout, S = g.parts;
+  const int d = g.Nout, S = planes_split(g);
   const size_t plane = static_cast<size_t>(g.M) * d;
   const float* src = g.sk_partial + static_cast<size_t>(m) * d;
   float v[NC][4];
@@ -1976,11 +1989,13 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
   if (WAMC_GEMM_WIDE_PLANES && use_sk && pp.S <= 1 && !big && g.d_model >= 256 && planes_pay &&
       (!use_ks2 || WAMC_GEMM_WIDE_PLANES >= 2) && t256_cap > 0) {
     const long long plane = static_cast<long long>(g.M) * g.Nout * 4;
-    long long S = SkWide::kP / t256_cap;
-    S = std::min<long long>(S, (g.K / 64) / kPartsMinIters);
-    S = std::min<long long>(S, kPartsMaxSplit);
-    S = std::min<long long>(S, static_cast<long long>(g.sk_partial_bytes) / plane);
-    if (S >= 2) wps = static_cast<int>(S);
+    long long smax = std::min<long long>((g.K / 64) / kPartsMinIters, kPartsMaxSplit);
+    smax = std::min<long long>(smax, static_cast<long long>(g.sk_partial_bytes) / plane);
+    // taken where the tiles at rows_cap rows split at least two ways; the
+    // count itself comes from k_eff on the device (planes_split), so a launch
+    // sized for every token still splits its k_eff rows' tiles as far as they
+    // go (the union rule, k_eff between its larger budget and N)
+    if (std::min<long long>(SkWide::kP / t256_cap, smax) >= 2) wps = static_cast<int>(smax);
   }
   TimedLaunch t(timer, gemm_name(g, epi), s, pp.S > 1 || wps > 1);   // the split-K paths launch two kernels
   // second kernel of the split-K paths: planes summed in piece order, epilogue
@@ -2009,8 +2024,9 @@ hipError_t launch_gemm(bool bf16, GemmEpi epi, const GemmArgs& g, hipStream_t s,
     reduce_parts(gp);
   } else if (wps > 1) {
     GemmArgs gp = g;
-    gp.parts = wps;
-    const unsigned grid = static_cast<unsigned>((t256_cap * wps + 7) / 8 * 8);
+    gp.parts = -wps;   // at most wps pieces a tile, the count from k_eff
+    // tiles x pieces <= max(one workgroup per CU, the tiles at rows_cap rows)
+    const unsigned grid = static_cast<unsigned>((std::max<long long>(SkWide::kP, t256_cap) + 7) / 8 * 8);
     WAMC_EPI_DISPATCH(epi, (launch(gemm_bf16_sk_kernel<E, 256, 256, 64, 2, 2, 2>, grid, 256, 0, s, gp)));
     reduce_parts(gp);
   } else if (!use_ks2 && use_sk && wide4) {

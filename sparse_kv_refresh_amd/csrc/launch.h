@@ -179,7 +179,8 @@ struct GemmArgs {
   float* sk_partial;        // f32 partial tiles of split output tiles
   size_t sk_partial_bytes;  // its size (bounds the number of pieces)
   int* sk_counters;         // per-tile arrival counters, zero between launches
-  int parts;                // pieces per tile of the split-K path with a separate reduction (set by launch_gemm)
+  int parts;                // pieces per tile of the split-K path with a separate reduction (set by launch_gemm;
+                            // -S: at most S, the count derived from k_eff on the device)
   // EPI_RESID_* (optional): the LayerNorm that follows, h = act(LN(out)(1 + scale) + shift) (no
   // modulation when shift is null), done in the same pass where the schedule holds whole rows
   void* ln_out;             // [M, d] act; null: no LayerNorm here

@@ -3,6 +3,7 @@
     python -m sparse_kv_refresh_amd.rocprof_summary stats  <run_results.db> [--steps K --warmup W]
     python -m sparse_kv_refresh_amd.rocprof_summary traffic <fetch.db> <write.db> --kernel NAME
         [--config c2_layer] [--skip-first N] [--out FILE]
+    python -m sparse_kv_refresh_amd.rocprof_summary sq <run_results.db>
 
 `stats` prints the per-kernel launch count, total and average duration from a
 `--kernel-trace` run.  Given the run's W warm-up and K timed steps, a kernel
@@ -93,6 +94,28 @@ def copy_factor(vals: dict, counter: str) -> float:
     return COPY_BYTES / (big * 1024.0)
 
 
+SQ_COUNTERS = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+               "SQ_ACTIVE_INST_LDS")
+
+
+def sq_summary(db: str):
+    """Per kernel name, from one `--pmc SQ_WAVES SQ_WAVE_CYCLES ...` run:
+    launches, waves per launch and the shares of all resident wave-cycles
+    spent waiting on anything, waiting on a dependency, and issuing VALU and
+    LDS instructions (each counter summed over the launches, so the shares
+    weight launches by their wave-cycles)."""
+    vals = {cn: counters(db, cn) for cn in SQ_COUNTERS}
+    out = []
+    for kn, cyc in vals["SQ_WAVE_CYCLES"].items():
+        tot = sum(cyc)
+        if tot <= 0:
+            continue
+        share = {cn: sum(vals[cn].get(kn, [0.0])) / tot for cn in SQ_COUNTERS[2:]}
+        waves = vals["SQ_WAVES"].get(kn, [0.0])
+        out.append((kn, len(cyc), sum(waves) / max(len(waves), 1), share, tot))
+    return sorted(out, key=lambda r: -r[4])
+
+
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
 
 
@@ -161,6 +184,8 @@ def main(argv=None):
                    help="for kernels launched more than once per step: which launch of each step")
     b.add_argument("--per-step", type=int, default=1, help="launches of this kernel per step")
     b.add_argument("--out")
+    q = sub.add_parser("sq")
+    q.add_argument("db")
     c = sub.add_parser("mfma")
     c.add_argument("db")
     c.add_argument("--config", default="c3_stack")
@@ -179,6 +204,13 @@ def main(argv=None):
             with open(args.out, "w") as fh:
                 fh.write(text + "\n")
         print(text)
+        return
+
+    if args.cmd == "sq":
+        print(f"{'kernel':90s} {'launches':>8s} {'waves':>7s} {'wait':>6s} {'dep':>6s} {'valu':>6s} {'lds':>6s}")
+        for kn, n, waves, sh, _ in sq_summary(args.db):
+            print(f"{kn[:90]:90s} {n:8d} {waves:7.0f} {100 * sh['SQ_WAIT_ANY']:5.0f}% {100 * sh['SQ_WAIT_INST_ANY']:5.0f}%"
+                  f" {100 * sh['SQ_ACTIVE_INST_VALU']:5.0f}% {100 * sh['SQ_ACTIVE_INST_LDS']:5.1f}%")
         return
 
     if args.cmd == "stats":
